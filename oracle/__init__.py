@@ -1,0 +1,222 @@
+"""Plain CPU oracle of the weight-only INT4 (group 32) MoE layer.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this package. The
+product path (the HIP library and its Python binding) never reaches it and
+fails loudly when its native library is missing.
+
+What the layer computes comes from "The Throughput Lever: Quantifying the MoE
+GEMM and Mapping the Road to B300":
+  * section "Phase 3: The INT4 Marlin MoE Throughput Lever": the MoE layer is
+    a grouped GEMM over the experts, run on a dense token batch;
+  * section "Building the Benchmark": expert weights are INT4 with group size
+    32 (GPTQ-style: one scale per 32 consecutive input channels);
+  * section "The Result: Two Regimes": each token is routed to 8 of 384
+    experts (top-8 routing) and the layer streams the weights of the experts
+    that are touched.
+The benchmark workload fixes the routing as softmax over the experts, top-k,
+and renormalisation of the k kept weights, and the expert MLP as FC1
+(gate/up) -> SiLU(gate) * up -> FC2, with the k expert outputs summed with
+the routing weights. Where the pages leave a step open, the plainest reading
+is taken; each reading is named in the function that uses it.
+
+Everything floating-point here is float64. The dequantised weight q*s is exact
+in float64 (a 4-bit integer times an 11-bit fp16 significand).
+
+Pins (what checks this oracle against something other than itself) live in
+``tests/test_oracle_*.py``: hand-packed nibbles, brute-force routing,
+argsort-based alignment, closed forms, a dense masked formulation, a textbook
+SwiGLU MLP for k = 1, and invariances. No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+from typing import Callable, Dict, Tuple
+
+import numpy as np
+
+GROUP = 32
+
+
+# --------------------------------------------------------------------------
+# O1, O2: INT4 unpack and group-32 dequantisation
+# --------------------------------------------------------------------------
+def unpack_int4(qweight: np.ndarray) -> np.ndarray:
+    """Signed 4-bit values q in [-8, 7] from the canonical packed bytes.
+
+    Reading of "Building the Benchmark" (GPTQ-format INT4): byte i of a row
+    holds input channel 2i in its low nibble and 2i+1 in its high nibble,
+    and a nibble u stands for q = u - 8 (zero point 8, symmetric range).
+    Input uint8 [..., K/2]; output int16 [..., K].
+    """
+    qb = np.asarray(qweight, dtype=np.uint8)
+    lo = (qb & 0x0F).astype(np.int16) - 8
+    hi = (qb >> 4).astype(np.int16) - 8
+    q = np.empty(qb.shape[:-1] + (2 * qb.shape[-1],), dtype=np.int16)
+    q[..., 0::2] = lo
+    q[..., 1::2] = hi
+    return q
+
+
+def dequantize(qweight: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
+    """W[n, c] = q[n, c] * s[n, c // 32] in float64 (group size 32 along K).
+
+    "Building the Benchmark": INT4 weights with group size 32. Reading: one
+    fp16 scale per (row, group of 32 channels), symmetric, no zero point
+    beyond the offset of 8 in the nibble code.
+    """
+    q = unpack_int4(qweight).astype(np.float64)
+    s = np.asarray(scales_f16, dtype=np.float16).astype(np.float64)
+    if q.shape[-1] != s.shape[-1] * GROUP:
+        raise ValueError(f"K={q.shape[-1]} does not match {s.shape[-1]} groups of {GROUP}")
+    return q * np.repeat(s, GROUP, axis=-1)
+
+
+# --------------------------------------------------------------------------
+# O3: top-k routing
+# --------------------------------------------------------------------------
+def route(logits: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k experts per token and their renormalised softmax weights.
+
+    "The Result: Two Regimes": each token activates 8 of the 384 experts via
+    top-8 routing. The workload defines the weights as softmax over all
+    experts, keep the k largest, renormalise them to sum 1.
+
+    Readings:
+      * selection is made on the float32 logits (softmax is monotone, so the
+        set is the same in exact arithmetic);
+      * ties go to the lower expert index, and -0.0 ties with +0.0;
+      * slot j holds the (j+1)-th largest logit;
+      * the full-softmax denominator cancels in the renormalisation, so
+        w_j = exp(L_j - L_max) / sum_i exp(L_i - L_max) over the k kept
+        logits, computed in float64.
+    Returns topk_ids int32 [M, k] and topk_weights float64 [M, k].
+    """
+    L = np.asarray(logits, dtype=np.float32)
+    M, E = L.shape
+    if not 1 <= k <= E:
+        raise ValueError("k must be in [1, E]")
+    ids = np.empty((M, k), dtype=np.int32)
+    w = np.empty((M, k), dtype=np.float64)
+    for t in range(M):
+        row = [float(v) + 0.0 for v in L[t]]  # -0.0 + 0.0 == +0.0
+        order = sorted(range(E), key=lambda e: (-row[e], e))
+        chosen = order[:k]
+        ids[t] = chosen
+        top = np.array([row[e] for e in chosen], dtype=np.float64)
+        ex = np.exp(top - top[0])
+        w[t] = ex / ex.sum()
+    return ids, w
+
+
+# --------------------------------------------------------------------------
+# O4: per-expert token grouping (histogram, padded offsets, stable order)
+# --------------------------------------------------------------------------
+def align(topk_ids: np.ndarray, E: int, block_m: int):
+    """Group the M*k assignments by expert, each group padded to block_m.
+
+    The grouped GEMM of "Phase 3: The INT4 Marlin MoE Throughput Lever" runs
+    each expert over the tokens routed to it; the workload asks for a
+    per-expert histogram, a prefix sum, a permutation and padding of each
+    expert's list to the tile size.
+
+    Readings: assignment f = t*k + j; an expert's list is in ascending f
+    (a stable counting sort); padding entries hold the sentinel M*k; experts
+    with no token get no block.
+    Returns dict with counts [E], expert_offsets [E+1], num_tokens_post_pad,
+    sorted_token_ids [NPP], block_expert_ids [NPP/block_m].
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    n_assign = ids.size
+    counts = np.zeros(E, dtype=np.int64)
+    for e in ids:
+        counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        padded = -(-counts[e] // block_m) * block_m
+        offsets[e + 1] = offsets[e] + padded
+    npp = int(offsets[E])
+    sorted_ids = np.full(npp, n_assign, dtype=np.int64)
+    fill = offsets[:E].copy()
+    for f in range(n_assign):
+        e = ids[f]
+        sorted_ids[fill[e]] = f
+        fill[e] += 1
+    blocks = np.empty(npp // block_m, dtype=np.int64)
+    for e in range(E):
+        blocks[offsets[e] // block_m: offsets[e + 1] // block_m] = e
+    return {
+        "counts": counts.astype(np.int32),
+        "expert_offsets": offsets.astype(np.int32),
+        "num_tokens_post_pad": npp,
+        "sorted_token_ids": sorted_ids.astype(np.int32),
+        "block_expert_ids": blocks.astype(np.int32),
+    }
+
+
+# --------------------------------------------------------------------------
+# O5 - O7: expert MLPs and the weighted combine
+# --------------------------------------------------------------------------
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_mlp(x: np.ndarray, W13: np.ndarray, W2: np.ndarray) -> np.ndarray:
+    """One expert on one token: FC1 (gate rows then up rows), SiLU(gate)*up, FC2.
+
+    Reading: W13 has 2I rows, [0, I) the gate projection and [I, 2I) the up
+    projection.
+    """
+    I = W13.shape[0] // 2
+    h = W13 @ x
+    act = silu(h[:I]) * h[I:]
+    return W2 @ act
+
+
+ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]]
+
+
+class DequantCache:
+    """Dequantised experts on demand, keeping at most ``max_items`` of them."""
+
+    def __init__(self, get_expert: ExpertFn, max_items: int = 64):
+        self.get_expert = get_expert
+        self.max_items = max_items
+        self.items: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
+
+    def __call__(self, e: int):
+        if e not in self.items:
+            if len(self.items) >= self.max_items:
+                self.items.pop(next(iter(self.items)))
+            w13, s13, w2, s2 = self.get_expert(e)
+            self.items[e] = (dequantize(w13, s13), dequantize(w2, s2))
+        return self.items[e]
+
+
+def moe_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
+                experts: Callable[[int], Tuple[np.ndarray, np.ndarray]],
+                tokens_subset=None) -> np.ndarray:
+    """out[t] = sum_j w[t, j] * MLP_{ids[t, j]}(x_t), summed in slot order.
+
+    x: float [M, H] (the bf16 activations widened exactly); experts(e) returns
+    the dequantised (W13 [2I, H], W2 [H, I]) of expert e. ``tokens_subset``
+    limits the work to some token rows (the others are returned as NaN).
+    Returns float64 [M, H].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    M, H = x.shape
+    out = np.full((M, H), np.nan)
+    rows = range(M) if tokens_subset is None else tokens_subset
+    for t in rows:
+        acc = np.zeros(H, dtype=np.float64)
+        for j in range(topk_ids.shape[1]):
+            W13, W2 = experts(int(topk_ids[t, j]))
+            acc += topk_weights[t, j] * expert_mlp(x[t], W13, W2)
+        out[t] = acc
+    return out
+
+
+def layer(x: np.ndarray, logits: np.ndarray, k: int, experts, tokens_subset=None):
+    """Routing followed by the expert MLPs and the combine."""
+    ids, w = route(logits, k)
+    return moe_forward(x, ids, w, experts, tokens_subset), ids, w
