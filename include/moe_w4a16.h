@@ -1,0 +1,203 @@
+/*
+ * moe_w4a16.h - C ABI of the MI355X (gfx950) weight-only INT4 MoE layer.
+ *
+ * The layer is the one "The Throughput Lever: Quantifying the MoE GEMM and
+ * Mapping the Road to B300" identifies as the throughput lever of its MoE
+ * serving stack (section "Phase 3: The INT4 Marlin MoE Throughput Lever"):
+ * an INT4, group-size-32 (section "Building the Benchmark"), weight-only
+ * Mixture-of-Experts grouped GEMM run over a dense token batch of
+ * M = streams x q_len tokens (section "What It Means for the Engine"), each
+ * token routed to its top-k experts (section "The Result: Two Regimes").
+ *
+ * One layer call is two entry points on one stream:
+ *   moe_route_align   top-k routing + per-expert grouping of the M*k
+ *                     (token, slot) assignments, padded to the tile size;
+ *   moe_w4a16_forward FC1 (gate/up) with SiLU(gate)*up, FC2, and the
+ *                     routing-weighted sum of each token's k expert outputs.
+ * Weights are converted once by moe_w4a16_repack from the canonical GPTQ-style
+ * format into the device layout the kernels stream.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked "host". The caller allocates
+ *     and frees every buffer; the library allocates nothing, keeps no pointer
+ *     after returning and has no mutable global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work: no host synchronisation, no device-to-host
+ *     copy, so a layer call can be captured in a HIP graph. Buffers must stay
+ *     alive until the stream has executed the work.
+ *   - Arguments are validated on the host before anything is launched; on an
+ *     error nothing is launched and no output is touched. Launch failures
+ *     return MOE_ERR_HIP. A device fault surfaces at the caller's next
+ *     synchronisation. No C++ exception crosses this interface.
+ *   - M = 0 is valid: the call returns MOE_OK and launches nothing.
+ *   - bf16 and fp16 values travel as uint16_t bit patterns.
+ *
+ * Canonical weight format (input of moe_w4a16_repack, a reading of the
+ * "GPTQ-format" INT4 weights of "Building the Benchmark"):
+ *   qweight uint8 [E, N, K/2]: byte i of a row holds input channel 2i in its
+ *           low nibble and 2i+1 in its high nibble; nibble u encodes q = u - 8.
+ *   scales  fp16  [E, N, K/32]: W[e, n, c] = q[e, n, c] * scales[e, n, c/32].
+ *   W13 (kind 0): N = 2*I, K = H; rows [0, I) gate, rows [I, 2I) up.
+ *   W2  (kind 1): N = H,   K = I.
+ *
+ * Limits (MOE_ERR_UNSUPPORTED otherwise): 1 <= E <= 1024, 1 <= top_k <= min(E, 16),
+ * H and I multiples of 128, block_m in {16, 32, 64}, M*top_k*max(H, I) < 2^31.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* null pointer, negative size, misaligned pointer */
+    MOE_ERR_UNSUPPORTED = -2, /* a size outside the limits above */
+    MOE_ERR_CAPACITY = -3,    /* cap smaller than moe_route_align_capacity() */
+    MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_w4a16_workspace_bytes() */
+    MOE_ERR_HIP = -5          /* a HIP launch failed */
+};
+
+/* Version of this interface (bumped on any signature or layout change). */
+int32_t moe_w4a16_abi_version(void);
+
+/* Static, human-readable text for a status code (host). */
+const char* moe_w4a16_status_string(int status);
+
+/*
+ * moe_route_align_capacity (host): entries of sorted_token_ids a call with
+ * these sizes may write, rounded up to a multiple of block_m:
+ *   roundup(M*k + min(E, M*k)*(block_m - 1), block_m).
+ * Every expert's list is padded to a multiple of block_m, so the padded total
+ * never exceeds this. Returns -1 on invalid sizes.
+ */
+int64_t moe_route_align_capacity(int32_t M, int32_t E, int32_t top_k, int32_t block_m);
+
+/*
+ * moe_route_align: top-k routing and per-expert grouping of one token batch.
+ *
+ * Routing ("The Result: Two Regimes": each token activates its top-k
+ * experts; softmax over the experts, keep the k largest, renormalise):
+ *   logits        fp32 [M, E] row-major, finite.
+ *   topk_ids      out int32 [M, top_k]: the k experts with the largest logits,
+ *                 largest first; equal logits go to the lower expert index,
+ *                 -0.0 equals +0.0.
+ *   topk_weights  out fp32 [M, top_k]: exp(L_j - L_0) / sum_i exp(L_i - L_0)
+ *                 over the kept logits (equal to softmax-then-renormalise).
+ * Grouping (the grouped GEMM of "Phase 3: The INT4 Marlin MoE Throughput
+ * Lever" runs each expert over the tokens routed to it). Assignment
+ * f = t*top_k + j:
+ *   expert_offsets     out int32 [E+1]: exclusive prefix sum of the per-expert
+ *                      counts, each rounded up to a multiple of block_m.
+ *   num_tokens_post_pad out int32 [1]: expert_offsets[E] (NPP).
+ *   sorted_token_ids   out int32 [cap]: entries [off[e], off[e+1]) list the
+ *                      assignments of expert e in ascending f, then the
+ *                      sentinel M*top_k up to the end of the range. Entries at
+ *                      positions >= NPP are unspecified.
+ *   block_expert_ids   out int32 [cap/block_m]: expert of each block_m-row
+ *                      block; entries >= NPP/block_m are unspecified.
+ * cap must be >= moe_route_align_capacity(M, E, top_k, block_m) and a multiple
+ * of block_m. The integer outputs are deterministic (identical on every call).
+ */
+int moe_route_align(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t block_m,
+                    int32_t* topk_ids, float* topk_weights,
+                    int32_t* sorted_token_ids, int32_t* block_expert_ids,
+                    int32_t* expert_offsets, int32_t* num_tokens_post_pad,
+                    int64_t cap, void* stream);
+
+/*
+ * moe_w4a16_packed_bytes (host): size of the repacked weights of E experts
+ * of an [N, K] INT4 matrix with the given group size: E*N*K*9/16 (nibbles plus
+ * fp16 scales). Returns -1 unless group == 32, N % 32 == 0 and K % 128 == 0.
+ */
+int64_t moe_w4a16_packed_bytes(int32_t E, int32_t N, int32_t K, int32_t group);
+
+/*
+ * moe_w4a16_repack: canonical INT4 weights -> the device layout the forward
+ * streams. This is the analogue of the one-time weight repack of "Building
+ * the Benchmark" (there into the Marlin layout; here a gfx950 layout of
+ * 16-row x 128-channel tiles, each 1 KiB of nibbles followed by its 128 B of
+ * scales, ordered so one wave reads one tile with one 16-byte load per lane,
+ * and for W13 with gate tile r followed by up tile r).
+ *   qweight  uint8 [E, N, K/2], scales_f16 uint16 [E, N, K/32] (canonical).
+ *   kind     0 = W13 (N = 2I, K = H), 1 = W2 (N = H, K = I).
+ *   packed   out, moe_w4a16_packed_bytes(E, N, K, group) bytes, 16-byte aligned.
+ * The map is a bijection: moe_w4a16_unpack inverts it exactly.
+ */
+int moe_w4a16_repack(const uint8_t* qweight, const uint16_t* scales_f16,
+                     int32_t E, int32_t N, int32_t K, int32_t group, int32_t kind,
+                     void* packed, void* stream);
+
+/* moe_w4a16_unpack: exact inverse of moe_w4a16_repack (used by tests). */
+int moe_w4a16_unpack(const void* packed, int32_t E, int32_t N, int32_t K, int32_t group, int32_t kind,
+                     uint8_t* qweight, uint16_t* scales_f16, void* stream);
+
+/*
+ * moe_w4a16_workspace_bytes (host): scratch the forward needs for M tokens:
+ * an fp32 [M, H] accumulator, per-(token, 32-column tile) arrival counters and
+ * the bf16 [M*top_k, I] FC1 activations. Returns -1 on invalid sizes.
+ */
+int64_t moe_w4a16_workspace_bytes(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k);
+
+/*
+ * moe_w4a16_preferred_block_m (host): the block_m the forward runs best with
+ * for this batch (a function of the expected tokens per expert, M*top_k/E).
+ */
+int32_t moe_w4a16_preferred_block_m(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k);
+
+/*
+ * moe_w4a16_forward: the expert MLPs and the weighted combine for one batch.
+ * Equivalent to moe_w4a16_fc1 followed by moe_w4a16_fc2 on the same stream.
+ *   x_bf16      bf16 [M, H] activations, 16-byte aligned.
+ *   topk_weights, sorted_token_ids, block_expert_ids, expert_offsets,
+ *   num_tokens_post_pad: the outputs of moe_route_align for the same M, E,
+ *               top_k, block_m and cap (read on the device only).
+ *   w13_packed  moe_w4a16_repack output of W13 (kind 0), w2_packed of W2 (kind 1).
+ *   workspace   >= moe_w4a16_workspace_bytes(M, E, H, I, top_k) bytes,
+ *               16-byte aligned; contents on entry do not matter.
+ *   out_bf16    out bf16 [M, H]: out[t] = sum_j topk_weights[t, j] *
+ *               FC2_e(SiLU(gate_e(x_t)) * up_e(x_t)), e = topk_ids[t, j],
+ *               accumulated in fp32 and rounded once to bf16. The FC1
+ *               activation is stored as bf16 between the two GEMMs.
+ * Float results may differ in the last bits between calls (the k
+ * contributions are added with fp32 atomics in arrival order).
+ */
+int moe_w4a16_forward(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
+                      int32_t top_k, int32_t block_m, const float* topk_weights,
+                      const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
+                      const int32_t* expert_offsets, const int32_t* num_tokens_post_pad, int64_t cap,
+                      const void* w13_packed, const void* w2_packed,
+                      void* workspace, int64_t workspace_bytes, uint16_t* out_bf16, void* stream);
+
+/*
+ * moe_w4a16_fc1: first stage of moe_w4a16_forward. For every assignment f in
+ * sorted_token_ids (expert e, token t = f / top_k) it computes
+ * h = W13_e x_t, stores act_f = bf16(SiLU(h[0:I]) * h[I:2I]) in the
+ * workspace, and clears the accumulator and counters stage 2 uses.
+ */
+int moe_w4a16_fc1(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
+                  int32_t top_k, int32_t block_m,
+                  const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
+                  const int32_t* num_tokens_post_pad, int64_t cap,
+                  const void* w13_packed, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * moe_w4a16_fc2: second stage. y_f = W2_e act_f; out[t] += topk_weights[f] * y_f
+ * in fp32; each [token, 32-column] tile is rounded to bf16 into out_bf16 by
+ * whichever workgroup adds its last (top_k-th) contribution. Must follow
+ * moe_w4a16_fc1 with the same workspace on the same stream.
+ */
+int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
+                  const float* topk_weights, const int32_t* sorted_token_ids,
+                  const int32_t* block_expert_ids, const int32_t* num_tokens_post_pad, int64_t cap,
+                  const void* w2_packed, void* workspace, int64_t workspace_bytes,
+                  uint16_t* out_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

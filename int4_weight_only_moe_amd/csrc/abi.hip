@@ -1,0 +1,224 @@
+// Exported C entry points: host-side validation, sizes, and kernel launches.
+// Every check runs before the first HIP call, so an invalid call launches
+// nothing and touches no output.
+#include "../../include/moe_w4a16.h"
+#include "internal.h"
+
+namespace {
+
+using moe::kChunkK;
+using moe::kGroup;
+using moe::kPairRows;
+
+constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kMaxExperts = 1024;
+constexpr int32_t kMaxTopK = 16;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool block_m_ok(int32_t b) { return b == 16 || b == 32 || b == 64; }
+
+// Size checks shared by the entry points. Returns MOE_OK or an error code.
+int check_layer(int32_t M, int32_t E, int32_t H, int32_t I, int32_t k) {
+  if (M < 0 || E <= 0 || H <= 0 || I <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts || k > kMaxTopK || k > E) return MOE_ERR_UNSUPPORTED;
+  if (H % kChunkK != 0 || I % kChunkK != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t mk = (int64_t)M * k;
+  const int64_t widest = H > I ? H : I;
+  if (mk * widest >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t capacity(int32_t M, int32_t E, int32_t k, int32_t block_m) {
+  const int64_t mk = (int64_t)M * k;
+  const int64_t touched = mk < E ? mk : E;
+  const int64_t raw = mk + touched * (block_m - 1);
+  return (raw + block_m - 1) / block_m * block_m;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_w4a16_abi_version(void) { return kAbiVersion; }
+
+const char* moe_w4a16_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, or negative size)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size (see the limits in moe_w4a16.h)";
+    case MOE_ERR_CAPACITY: return "cap is smaller than moe_route_align_capacity() or not a multiple of block_m";
+    case MOE_ERR_WORKSPACE: return "workspace is smaller than moe_w4a16_workspace_bytes()";
+    case MOE_ERR_HIP: return "a HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t moe_route_align_capacity(int32_t M, int32_t E, int32_t top_k, int32_t block_m) {
+  if (M < 0 || E <= 0 || E > kMaxExperts || top_k <= 0 || top_k > E || top_k > kMaxTopK ||
+      !block_m_ok(block_m))
+    return -1;
+  return capacity(M, E, top_k, block_m);
+}
+
+int moe_route_align(const float* logits, int32_t M, int32_t E, int32_t top_k, int32_t block_m,
+                    int32_t* topk_ids, float* topk_weights, int32_t* sorted_token_ids,
+                    int32_t* block_expert_ids, int32_t* expert_offsets, int32_t* num_tokens_post_pad,
+                    int64_t cap, void* stream) {
+  if (M < 0 || E <= 0 || top_k <= 0) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts || top_k > E || top_k > kMaxTopK || !block_m_ok(block_m)) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)M * top_k >= (int64_t(1) << 30)) return MOE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weights || !sorted_token_ids || !block_expert_ids ||
+      !expert_offsets || !num_tokens_post_pad)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned4(logits) || !aligned4(topk_ids) || !aligned4(topk_weights) || !aligned4(sorted_token_ids) ||
+      !aligned4(block_expert_ids) || !aligned4(expert_offsets) || !aligned4(num_tokens_post_pad))
+    return MOE_ERR_INVALID_ARG;
+  if (cap < capacity(M, E, top_k, block_m) || cap % block_m != 0) return MOE_ERR_CAPACITY;
+  return hip_status(moe::launch_route_align(logits, M, E, top_k, block_m, topk_ids, topk_weights,
+                                            sorted_token_ids, block_expert_ids, expert_offsets,
+                                            num_tokens_post_pad, cap, (hipStream_t)stream));
+}
+
+int64_t moe_w4a16_packed_bytes(int32_t E, int32_t N, int32_t K, int32_t group) {
+  if (E <= 0 || N <= 0 || K <= 0 || group != kGroup || N % kPairRows != 0 || K % kChunkK != 0) return -1;
+  return (int64_t)E * moe::packed_bytes_per_expert(N, K);
+}
+
+static int check_repack(const void* a, const void* b, const void* c, int32_t E, int32_t N, int32_t K,
+                        int32_t group, int32_t kind) {
+  if (E <= 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+  if (kind != 0 && kind != 1) return MOE_ERR_INVALID_ARG;
+  if (group != kGroup || N % kPairRows != 0 || K % kChunkK != 0) return MOE_ERR_UNSUPPORTED;
+  if (kind == 0 && (N / 2) % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!a || !b || !c) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int moe_w4a16_repack(const uint8_t* qweight, const uint16_t* scales_f16, int32_t E, int32_t N, int32_t K,
+                     int32_t group, int32_t kind, void* packed, void* stream) {
+  const int st = check_repack(qweight, scales_f16, packed, E, N, K, group, kind);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_repack(qweight, scales_f16, E, N, K, kind, (uint8_t*)packed,
+                                       (hipStream_t)stream));
+}
+
+int moe_w4a16_unpack(const void* packed, int32_t E, int32_t N, int32_t K, int32_t group, int32_t kind,
+                     uint8_t* qweight, uint16_t* scales_f16, void* stream) {
+  const int st = check_repack(packed, qweight, scales_f16, E, N, K, group, kind);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_unpack((const uint8_t*)packed, E, N, K, kind, qweight, scales_f16,
+                                       (hipStream_t)stream));
+}
+
+int64_t moe_w4a16_workspace_bytes(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
+  if (check_layer(M, E, H, I, top_k) != MOE_OK) return -1;
+  return moe::workspace_layout(M, H, I, top_k).total;
+}
+
+int32_t moe_w4a16_preferred_block_m(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
+  if (check_layer(M, E, H, I, top_k) != MOE_OK) return -1;
+  // Expected tokens per touched expert decides how many 16-row sub-tiles a
+  // block should carry: one block per expert whenever that stays <= 64 rows.
+  const double per_expert = (double)M * top_k / E;
+  if (per_expert <= 8.0) return 16;
+  if (per_expert <= 20.0) return 32;
+  return 64;
+}
+
+static int check_fc(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m, int64_t cap,
+                    int64_t workspace_bytes) {
+  const int st = check_layer(M, E, H, I, top_k);
+  if (st != MOE_OK) return st;
+  if (!block_m_ok(block_m)) return MOE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  if (cap < capacity(M, E, top_k, block_m) || cap % block_m != 0) return MOE_ERR_CAPACITY;
+  if (workspace_bytes < moe::workspace_layout(M, H, I, top_k).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+static moe::FcArgs fc_args(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
+                           int64_t cap, const int32_t* sorted_ids, const int32_t* block_expert,
+                           const int32_t* npp, void* workspace) {
+  moe::FcArgs a{};
+  const moe::WorkspaceLayout L = moe::workspace_layout(M, H, I, top_k);
+  uint8_t* ws = (uint8_t*)workspace;
+  a.sorted_ids = sorted_ids;
+  a.block_expert = block_expert;
+  a.npp = npp;
+  a.acc = (float*)(ws + L.acc_off);
+  a.counters = (uint32_t*)(ws + L.cnt_off);
+  a.act_out = (uint16_t*)(ws + L.act_off);
+  a.M = M; a.E = E; a.H = H; a.I = I; a.k = top_k; a.block_m = block_m;
+  a.cap = cap;
+  a.zero_words16 = (L.cnt_off + (int64_t)M * (H / kPairRows) * 4) / 16;
+  return a;
+}
+
+int moe_w4a16_fc1(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k,
+                  int32_t block_m, const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
+                  const int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed, void* workspace,
+                  int64_t workspace_bytes, void* stream) {
+  int st = check_fc(M, E, H, I, top_k, block_m, cap, workspace_bytes);
+  if (st != MOE_OK || M == 0) return st;
+  if (!x_bf16 || !sorted_token_ids || !block_expert_ids || !num_tokens_post_pad || !w13_packed || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_bf16) || !aligned16(w13_packed) || !aligned16(workspace) || !aligned4(sorted_token_ids) ||
+      !aligned4(block_expert_ids) || !aligned4(num_tokens_post_pad))
+    return MOE_ERR_INVALID_ARG;
+  moe::FcArgs a = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
+                          num_tokens_post_pad, workspace);
+  a.act_in = x_bf16;
+  a.wpacked = (const uint8_t*)w13_packed;
+  return hip_status(moe::launch_fc1(a, (hipStream_t)stream));
+}
+
+int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
+                  const float* topk_weights, const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
+                  const int32_t* num_tokens_post_pad, int64_t cap, const void* w2_packed, void* workspace,
+                  int64_t workspace_bytes, uint16_t* out_bf16, void* stream) {
+  int st = check_fc(M, E, H, I, top_k, block_m, cap, workspace_bytes);
+  if (st != MOE_OK || M == 0) return st;
+  if (!topk_weights || !sorted_token_ids || !block_expert_ids || !num_tokens_post_pad || !w2_packed ||
+      !workspace || !out_bf16)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w2_packed) || !aligned16(workspace) || !aligned16(out_bf16) || !aligned4(topk_weights) ||
+      !aligned4(sorted_token_ids) || !aligned4(block_expert_ids) || !aligned4(num_tokens_post_pad))
+    return MOE_ERR_INVALID_ARG;
+  moe::FcArgs a = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
+                          num_tokens_post_pad, workspace);
+  a.act_in = a.act_out;  // FC2 reads the FC1 activations
+  a.act_out = nullptr;
+  a.wpacked = (const uint8_t*)w2_packed;
+  a.topk_weights = topk_weights;
+  a.out = out_bf16;
+  return hip_status(moe::launch_fc2(a, (hipStream_t)stream));
+}
+
+int moe_w4a16_forward(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k,
+                      int32_t block_m, const float* topk_weights, const int32_t* sorted_token_ids,
+                      const int32_t* block_expert_ids, const int32_t* expert_offsets,
+                      const int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed,
+                      const void* w2_packed, void* workspace, int64_t workspace_bytes, uint16_t* out_bf16,
+                      void* stream) {
+  int st = check_fc(M, E, H, I, top_k, block_m, cap, workspace_bytes);
+  if (st != MOE_OK || M == 0) return st;
+  if (!x_bf16 || !topk_weights || !sorted_token_ids || !block_expert_ids || !expert_offsets ||
+      !num_tokens_post_pad || !w13_packed || !w2_packed || !workspace || !out_bf16)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_bf16) || !aligned16(w13_packed) || !aligned16(w2_packed) || !aligned16(workspace) ||
+      !aligned16(out_bf16) || !aligned4(topk_weights) || !aligned4(sorted_token_ids) ||
+      !aligned4(block_expert_ids) || !aligned4(expert_offsets) || !aligned4(num_tokens_post_pad))
+    return MOE_ERR_INVALID_ARG;
+  st = moe_w4a16_fc1(x_bf16, M, E, H, I, top_k, block_m, sorted_token_ids, block_expert_ids,
+                     num_tokens_post_pad, cap, w13_packed, workspace, workspace_bytes, stream);
+  if (st != MOE_OK) return st;
+  return moe_w4a16_fc2(M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
+                       num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
+}
+
+}  // extern "C"

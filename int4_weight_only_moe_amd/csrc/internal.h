@@ -1,0 +1,75 @@
+// Internal declarations shared by the host-side entry points (abi.hip) and
+// the kernel translation units. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Device layout of the repacked INT4 weights.
+//   A "tile" is 16 rows x 128 input channels: 1024 bytes of nibbles followed
+//   by 128 bytes of fp16 scales (16 rows x 4 groups of 32).
+//   A "pair" is two tiles read together by one wave: for W13 the gate rows
+//   [16r, 16r+16) and the up rows I + [16r, 16r+16); for W2 the rows
+//   [32r, 32r+16) and [32r+16, 32r+32).
+//   Per expert: pairs in row order, each pair's K-chunks in K order, each
+//   K-chunk holds the two tiles back to back.
+constexpr int kGroup = 32;
+constexpr int kTileRows = 16;
+constexpr int kChunkK = 128;                 // input channels per tile
+constexpr int kTileNibbleBytes = 1024;       // 16 x 128 / 2
+constexpr int kTileScaleBytes = 128;         // 16 x 4 x 2
+constexpr int kTileBytes = kTileNibbleBytes + kTileScaleBytes;
+constexpr int kPairRows = 32;
+constexpr int kPairChunkBytes = 2 * kTileBytes;
+
+__host__ __device__ inline int64_t packed_bytes_per_expert(int64_t N, int64_t K) {
+  return (N / kPairRows) * (K / kChunkK) * kPairChunkBytes;
+}
+
+// Workspace layout of the forward: [acc fp32 M x H][counters u32 M x H/32][act bf16 M*k x I]
+struct WorkspaceLayout {
+  int64_t acc_off, cnt_off, act_off, total;
+};
+inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+inline WorkspaceLayout workspace_layout(int64_t M, int64_t H, int64_t I, int64_t k) {
+  WorkspaceLayout w;
+  w.acc_off = 0;
+  w.cnt_off = align256(M * H * 4);
+  w.act_off = w.cnt_off + align256(M * (H / kPairRows) * 4);
+  w.total = w.act_off + align256(M * k * I * 2);
+  return w;
+}
+
+// Kernel launchers (each returns the hipError_t of its launches).
+hipError_t launch_route_align(const float* logits, int M, int E, int k, int block_m,
+                              int32_t* topk_ids, float* topk_weights, int32_t* sorted_ids,
+                              int32_t* block_expert, int32_t* offsets, int32_t* npp,
+                              int64_t cap, hipStream_t stream);
+
+hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int E, int N, int K, int kind,
+                         uint8_t* packed, hipStream_t stream);
+hipError_t launch_unpack(const uint8_t* packed, int E, int N, int K, int kind, uint8_t* q,
+                         uint16_t* s, hipStream_t stream);
+
+struct FcArgs {
+  const uint16_t* act_in;      // FC1: x [M, H]; FC2: act [M*k, I]
+  const uint8_t* wpacked;      // repacked weights
+  const int32_t* sorted_ids;   // [cap]
+  const int32_t* block_expert; // [cap / block_m]
+  const int32_t* npp;          // [1]
+  const float* topk_weights;   // FC2 only, [M*k]
+  uint16_t* act_out;           // FC1 only: act [M*k, I]
+  float* acc;                  // fp32 [M, H]
+  uint32_t* counters;          // [M, H/32]
+  uint16_t* out;               // FC2 only: bf16 [M, H]
+  int M, E, H, I, k, block_m;
+  int64_t cap;
+  int64_t zero_words16;         // FC1: 16-byte words to clear at acc (accumulator + counters)
+};
+
+hipError_t launch_fc1(const FcArgs& a, hipStream_t stream);
+hipError_t launch_fc2(const FcArgs& a, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,266 @@
+// Top-k routing and per-expert grouping of the M*k (token, slot) assignments.
+//
+// Routing follows "The Throughput Lever: Quantifying the MoE GEMM and
+// Mapping the Road to B300", section "The Result: Two Regimes" (each token
+// activates its top-k experts): the k largest logits, ties to the lower
+// expert index, weights = softmax over the kept logits.
+// Grouping feeds the grouped GEMM of section "Phase 3: The INT4 Marlin MoE
+// Throughput Lever": a per-expert histogram, a prefix sum of the counts padded
+// to the tile size, a stable permutation of the assignments and the padding.
+//
+// Two launch shapes produce identical integers:
+//   M <= kFusedMaxTokens: one workgroup does the top-k (one wave per token)
+//                         and then the grouping;
+//   otherwise:            a top-k kernel with one wave per token over many
+//                         workgroups, then a one-workgroup grouping kernel.
+#include "internal.h"
+#include "device_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / 64;
+constexpr int kMaxExperts = 1024;
+constexpr int kFusedMaxTokens = 16;
+constexpr int kTopkWavesPerBlock = 4;
+
+// Order-preserving map of a finite fp32 value to uint32 (larger value ->
+// larger key); -0.0 is first turned into +0.0 so that the two tie. Key 0 is
+// never produced for finite inputs and marks "absent / already taken".
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+  uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    uint32_t olo = (uint32_t)__shfl_xor((int)lo, off, 64);
+    uint32_t ohi = (uint32_t)__shfl_xor((int)hi, off, 64);
+    uint64_t o = ((uint64_t)ohi << 32) | olo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One wave routes token t. Lane l holds logits l, l+64, ... (VPL of them).
+// Candidates compare as (key << 32) | ~e, so equal logits prefer the lower e.
+template <int VPL>
+__device__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
+                           int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[VPL];
+  const float* row = logits + (int64_t)t * E;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    int e = v * 64 + lane;
+    key[v] = (e < E) ? order_key(row[e]) : 0u;
+  }
+  uint32_t my_key = 0;
+  int my_e = 0;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      uint32_t e = (uint32_t)(v * 64 + lane);
+      uint64_t c = ((uint64_t)key[v] << 32) | (uint32_t)~e;
+      best = (key[v] != 0u && c > best) ? c : best;
+    }
+    best = wave_max_u64(best);
+    const uint32_t win_e = ~(uint32_t)best;
+    const uint32_t win_key = (uint32_t)(best >> 32);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if ((uint32_t)(v * 64 + lane) == win_e) key[v] = 0u;
+    if (lane == r) {
+      my_key = win_key;
+      my_e = (int)win_e;
+    }
+  }
+  const float l0 = key_value((uint32_t)__shfl((int)my_key, 0, 64));
+  const float ex = (lane < k) ? expf(key_value(my_key) - l0) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    topk_ids[(int64_t)t * k + lane] = my_e;
+    topk_w[(int64_t)t * k + lane] = ex / sum;
+  }
+}
+
+template <int VPL>
+__global__ __launch_bounds__(64 * kTopkWavesPerBlock) void topk_kernel(
+    const float* __restrict__ logits, int M, int E, int k, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_w) {
+  const int t = blockIdx.x * kTopkWavesPerBlock + (threadIdx.x >> 6);
+  if (t >= M) return;
+  topk_token<VPL>(logits, t, E, k, topk_ids, topk_w);
+}
+
+// Grouping by one workgroup of kAlignThreads threads.
+//   counts     histogram of the expert ids (LDS atomics: order-free);
+//   offsets    exclusive scan of the counts rounded up to block_m;
+//   placement  assignments are taken in chunks of kAlignThreads in ascending f;
+//              a lane's rank among equal experts of its wave comes from
+//              comparing against every lane of the wave in lane order, and
+//              earlier waves and chunks add their counts, so each expert's
+//              list is in ascending f without any order-dependent atomic.
+struct AlignShared {
+  int cnt[kMaxExperts];
+  int off[kMaxExperts + 1];
+  int run[kMaxExperts];
+  int wave_tot[kAlignWaves];
+  int wcnt[kAlignWaves][kMaxExperts];
+};
+
+__device__ void align_body(AlignShared& sh, const int32_t* __restrict__ ids, int MK, int E,
+                           int block_m, int32_t* __restrict__ sorted_ids,
+                           int32_t* __restrict__ block_expert, int32_t* __restrict__ offsets,
+                           int32_t* __restrict__ npp_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += kAlignThreads) {
+    sh.cnt[e] = 0;
+    sh.run[e] = 0;
+  }
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) sh.wcnt[i / E][i % E] = 0;
+  __syncthreads();
+  for (int f = tid; f < MK; f += kAlignThreads) {
+    int e = ids[f];
+    if (e >= 0 && e < E) atomicAdd(&sh.cnt[e], 1);
+  }
+  __syncthreads();
+
+  // exclusive scan of padded counts (E <= kAlignThreads: one expert per thread)
+  int padded = 0;
+  if (tid < E) padded = (sh.cnt[tid] + block_m - 1) / block_m * block_m;
+  int incl = padded;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) sh.wave_tot[wave] = incl;
+  __syncthreads();
+  int wave_base = 0;
+  for (int w = 0; w < wave; ++w) wave_base += sh.wave_tot[w];
+  const int excl = wave_base + incl - padded;
+  if (tid < E) {
+    sh.off[tid] = excl;
+    offsets[tid] = excl;
+  }
+  if (tid == E - 1) {
+    sh.off[E] = excl + padded;
+    offsets[E] = excl + padded;
+    *npp_out = excl + padded;
+  }
+  __syncthreads();
+
+  // block -> expert map and sentinel padding, one expert per thread
+  if (tid < E) {
+    const int o0 = sh.off[tid], o1 = sh.off[tid + 1], c = sh.cnt[tid];
+    for (int bb = o0 / block_m; bb < o1 / block_m; ++bb) block_expert[bb] = tid;
+    for (int p = o0 + c; p < o1; ++p) sorted_ids[p] = MK;
+  }
+
+  // stable placement
+  for (int base = 0; base < MK; base += kAlignThreads) {
+    const int f = base + tid;
+    int e = (f < MK) ? ids[f] : -1;
+    if (e >= E) e = -1;
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      const int m = (ej == e) ? 1 : 0;
+      tot += m;
+      before += (j < lane) ? m : 0;
+    }
+    if (e >= 0 && before == tot - 1) sh.wcnt[wave][e] = tot;
+    __syncthreads();
+    if (e >= 0) {
+      int pos = sh.off[e] + sh.run[e] + before;
+      for (int w = 0; w < wave; ++w) pos += sh.wcnt[w][e];
+      sorted_ids[pos] = f;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int s = 0;
+      for (int w = 0; w < kAlignWaves; ++w) {
+        s += sh.wcnt[w][tid];
+        sh.wcnt[w][tid] = 0;
+      }
+      sh.run[tid] += s;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int32_t* __restrict__ ids, int MK, int E, int block_m, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ offsets, int32_t* __restrict__ npp) {
+  __shared__ AlignShared sh;
+  align_body(sh, ids, MK, E, block_m, sorted_ids, block_expert, offsets, npp);
+}
+
+// Small batches: waves 0..M-1 route one token each, then the whole
+// workgroup groups the assignments (the ids are read back after a barrier).
+template <int VPL>
+__global__ __launch_bounds__(kAlignThreads) void route_align_fused_kernel(
+    const float* __restrict__ logits, int M, int E, int k, int block_m, int32_t* topk_ids,
+    float* __restrict__ topk_w, int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ npp) {
+  __shared__ AlignShared sh;
+  const int wave = threadIdx.x >> 6;
+  if (wave < M) topk_token<VPL>(logits, wave, E, k, topk_ids, topk_w);
+  __threadfence_block();
+  __syncthreads();
+  align_body(sh, topk_ids, M * k, E, block_m, sorted_ids, block_expert, offsets, npp);
+}
+
+template <int VPL>
+hipError_t launch_vpl(const float* logits, int M, int E, int k, int block_m, int32_t* topk_ids,
+                      float* topk_w, int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets,
+                      int32_t* npp, hipStream_t stream) {
+  if (M <= kFusedMaxTokens) {
+    route_align_fused_kernel<VPL><<<1, kAlignThreads, 0, stream>>>(
+        logits, M, E, k, block_m, topk_ids, topk_w, sorted_ids, block_expert, offsets, npp);
+    return hipGetLastError();
+  }
+  const int blocks = (M + kTopkWavesPerBlock - 1) / kTopkWavesPerBlock;
+  topk_kernel<VPL><<<blocks, 64 * kTopkWavesPerBlock, 0, stream>>>(logits, M, E, k, topk_ids, topk_w);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  align_kernel<<<1, kAlignThreads, 0, stream>>>(topk_ids, M * k, E, block_m, sorted_ids, block_expert,
+                                                offsets, npp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route_align(const float* logits, int M, int E, int k, int block_m,
+                              int32_t* topk_ids, float* topk_weights, int32_t* sorted_ids,
+                              int32_t* block_expert, int32_t* offsets, int32_t* npp, int64_t cap,
+                              hipStream_t stream) {
+  (void)cap;
+  if (E <= 64)
+    return launch_vpl<1>(logits, M, E, k, block_m, topk_ids, topk_weights, sorted_ids, block_expert, offsets, npp, stream);
+  if (E <= 128)
+    return launch_vpl<2>(logits, M, E, k, block_m, topk_ids, topk_weights, sorted_ids, block_expert, offsets, npp, stream);
+  if (E <= 256)
+    return launch_vpl<4>(logits, M, E, k, block_m, topk_ids, topk_weights, sorted_ids, block_expert, offsets, npp, stream);
+  if (E <= 512)
+    return launch_vpl<8>(logits, M, E, k, block_m, topk_ids, topk_weights, sorted_ids, block_expert, offsets, npp, stream);
+  return launch_vpl<16>(logits, M, E, k, block_m, topk_ids, topk_weights, sorted_ids, block_expert, offsets, npp, stream);
+}
+
+}  // namespace moe

@@ -57,18 +57,28 @@ def unpack_int4(qweight: np.ndarray) -> np.ndarray:
     return q
 
 
-def dequantize(qweight: np.ndarray, scales_f16: np.ndarray) -> np.ndarray:
+def dequantize(qweight: np.ndarray, scales_f16: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
     """W[n, c] = q[n, c] * s[n, c // 32] in float64 (group size 32 along K).
 
     "Building the Benchmark": INT4 weights with group size 32. Reading: one
     fp16 scale per (row, group of 32 channels), symmetric, no zero point
-    beyond the offset of 8 in the nibble code.
+    beyond the offset of 8 in the nibble code (q = u - 8, as in unpack_int4).
+    ``out`` (float64 [..., K]) may be passed to reuse memory; the values are
+    written in place: the nibbles, minus 8, times the group's scale.
     """
-    q = unpack_int4(qweight).astype(np.float64)
+    qb = np.asarray(qweight, dtype=np.uint8)
     s = np.asarray(scales_f16, dtype=np.float16).astype(np.float64)
-    if q.shape[-1] != s.shape[-1] * GROUP:
-        raise ValueError(f"K={q.shape[-1]} does not match {s.shape[-1]} groups of {GROUP}")
-    return q * np.repeat(s, GROUP, axis=-1)
+    K = 2 * qb.shape[-1]
+    if K != s.shape[-1] * GROUP:
+        raise ValueError(f"K={K} does not match {s.shape[-1]} groups of {GROUP}")
+    W = np.empty(qb.shape[:-1] + (K,), dtype=np.float64) if out is None else out
+    pairs = W.reshape(qb.shape + (2,))
+    np.bitwise_and(qb, 0x0F, out=pairs[..., 0], casting="unsafe")  # channel 2i: low nibble
+    np.right_shift(qb, 4, out=pairs[..., 1], casting="unsafe")      # channel 2i+1: high nibble
+    W -= 8.0
+    groups = W.reshape(qb.shape[:-1] + (K // GROUP, GROUP))
+    groups *= s[..., None]
+    return W
 
 
 # --------------------------------------------------------------------------
@@ -177,19 +187,31 @@ ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]
 
 
 class DequantCache:
-    """Dequantised experts on demand, keeping at most ``max_items`` of them."""
+    """Dequantised experts on demand.
+
+    Keeps up to ``max_items`` experts; with ``max_items == 0`` it keeps none
+    and rewrites one pair of scratch buffers on every call (the caller uses
+    an expert's matrices before asking for the next one).
+    """
 
     def __init__(self, get_expert: ExpertFn, max_items: int = 64):
         self.get_expert = get_expert
         self.max_items = max_items
         self.items: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
+        self.scratch = None
 
     def __call__(self, e: int):
-        if e not in self.items:
-            if len(self.items) >= self.max_items:
-                self.items.pop(next(iter(self.items)))
-            w13, s13, w2, s2 = self.get_expert(e)
-            self.items[e] = (dequantize(w13, s13), dequantize(w2, s2))
+        if e in self.items:
+            return self.items[e]
+        w13, s13, w2, s2 = self.get_expert(e)
+        if self.max_items == 0:
+            if self.scratch is None or self.scratch[0].shape != (w13.shape[0], 2 * w13.shape[1]):
+                self.scratch = (np.empty((w13.shape[0], 2 * w13.shape[1])),
+                                np.empty((w2.shape[0], 2 * w2.shape[1])))
+            return dequantize(w13, s13, self.scratch[0]), dequantize(w2, s2, self.scratch[1])
+        if len(self.items) >= self.max_items:
+            self.items.pop(next(iter(self.items)))
+        self.items[e] = (dequantize(w13, s13), dequantize(w2, s2))
         return self.items[e]
 
 

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/moe_w4a16.h declares,
+and reject invalid arguments with the documented status before any HIP call
+(so these calls never touch a device). Sizes returned by the helpers are
+checked against their closed forms.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_weight_only_moe_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4a16.h")
+FAKE = 0x10000  # an aligned non-null address; validation fails before any use
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = ctypes.CDLL(moe.library_path())
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    assert moe.moe_w4a16_abi_version() == 1
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert moe.status_string(code) and moe.status_string(code) != "unknown status"
+    assert moe.status_string(42) == "unknown status"
+
+
+@pytest.mark.parametrize("M,E,k,B", [(1, 384, 8, 16), (1024, 384, 8, 32), (1024, 384, 8, 64), (16, 8, 2, 16),
+                                     (0, 8, 2, 16), (3, 4, 4, 64)])
+def test_capacity_formula(M, E, k, B):
+    raw = M * k + min(E, M * k) * (B - 1)
+    assert moe.moe_route_align_capacity(M, E, k, B) == -(-raw // B) * B
+
+
+def test_capacity_rejects():
+    assert moe.moe_route_align_capacity(1, 384, 8, 8) == -1
+    assert moe.moe_route_align_capacity(1, 2000, 8, 16) == -1
+    assert moe.moe_route_align_capacity(1, 4, 5, 16) == -1
+    assert moe.moe_route_align_capacity(-1, 4, 2, 16) == -1
+
+
+def test_packed_bytes():
+    assert moe.moe_w4a16_packed_bytes(384, 4096, 7168) == 384 * 4096 * 7168 * 9 // 16
+    assert moe.moe_w4a16_packed_bytes(384, 7168, 2048) == 384 * 7168 * 2048 * 9 // 16
+    total = moe.moe_w4a16_packed_bytes(384, 4096, 7168) + moe.moe_w4a16_packed_bytes(384, 7168, 2048)
+    assert total == 9_512_681_472  # nibbles + fp16 scales of the 384-expert layer
+    assert moe.moe_w4a16_packed_bytes(1, 48, 128) == -1     # N not a multiple of 32
+    assert moe.moe_w4a16_packed_bytes(1, 32, 96) == -1      # K not a multiple of 128
+    assert moe.moe_w4a16_packed_bytes(1, 32, 128, 64) == -1  # only group 32
+
+
+def test_workspace_bytes():
+    def a256(v):
+        return (v + 255) // 256 * 256
+    M, E, H, I, k = 1024, 384, 7168, 2048, 8
+    want = a256(M * H * 4) + a256(M * (H // 32) * 4) + a256(M * k * I * 2)
+    assert moe.moe_w4a16_workspace_bytes(M, E, H, I, k) == want
+    assert moe.moe_w4a16_workspace_bytes(1, E, 7000, I, k) == -1
+
+
+def test_preferred_block_m():
+    assert moe.moe_w4a16_preferred_block_m(1, 384, 7168, 2048, 8) == 16
+    assert moe.moe_w4a16_preferred_block_m(90, 384, 7168, 2048, 8) == 16
+    assert moe.moe_w4a16_preferred_block_m(512, 384, 7168, 2048, 8) == 32
+    assert moe.moe_w4a16_preferred_block_m(4096, 384, 7168, 2048, 8) == 64
+
+
+def _route(lib, M=4, E=384, k=8, B=16, cap=None, ptr=FAKE, logits=FAKE):
+    if cap is None:
+        cap = moe.moe_route_align_capacity(max(M, 0), E, k, B) if M >= 0 else 0
+    return lib.moe_route_align(logits, M, E, k, B, ptr, ptr, ptr, ptr, ptr, ptr, cap, None)
+
+
+def test_route_align_validation():
+    lib = moe.lib()
+    assert _route(lib, M=0, ptr=None, logits=None) == moe.MOE_OK  # empty batch: no launch
+    assert _route(lib, M=-1) == moe.MOE_ERR_INVALID_ARG
+    assert _route(lib, E=1025) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(lib, k=17, E=64) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(lib, k=9, E=8) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(lib, B=8, cap=1024) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(lib, logits=None) == moe.MOE_ERR_INVALID_ARG
+    assert _route(lib, logits=FAKE + 2) == moe.MOE_ERR_INVALID_ARG
+    cap = moe.moe_route_align_capacity(4, 384, 8, 16)
+    assert _route(lib, cap=cap - 16) == moe.MOE_ERR_CAPACITY
+    assert _route(lib, cap=cap + 1) == moe.MOE_ERR_CAPACITY  # not a multiple of block_m
+
+
+def test_repack_validation():
+    lib = moe.lib()
+    assert lib.moe_w4a16_repack(FAKE, FAKE, 2, 64, 128, 32, 2, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_w4a16_repack(FAKE, FAKE, 2, 48, 128, 32, 1, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_w4a16_repack(FAKE, FAKE, 2, 64, 96, 32, 1, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_w4a16_repack(FAKE, FAKE, 2, 64, 128, 16, 1, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_w4a16_repack(None, FAKE, 2, 64, 128, 32, 1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_w4a16_repack(FAKE + 8, FAKE, 2, 64, 128, 32, 1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_w4a16_unpack(FAKE, 2, 64, 128, 32, 0, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def _fwd(lib, M=4, E=384, H=7168, I=2048, k=8, B=16, cap=None, ws=None, x=FAKE, out=FAKE):
+    if cap is None:
+        cap = moe.moe_route_align_capacity(max(M, 0), E, k, B)
+    if ws is None:
+        ws = moe.moe_w4a16_workspace_bytes(max(M, 0), E, H, I, k)
+    p = FAKE
+    return lib.moe_w4a16_forward(x, M, E, H, I, k, B, p, p, p, p, p, cap, p, p, p, ws, out, None)
+
+
+def test_forward_validation():
+    lib = moe.lib()
+    assert lib.moe_w4a16_forward(None, 0, 384, 7168, 2048, 8, 16, None, None, None, None, None, 0, None, None,
+                                 None, 0, None, None) == moe.MOE_OK
+    assert _fwd(lib, H=7000) == moe.MOE_ERR_UNSUPPORTED
+    assert _fwd(lib, I=2000) == moe.MOE_ERR_UNSUPPORTED
+    assert _fwd(lib, B=128) == moe.MOE_ERR_UNSUPPORTED
+    assert _fwd(lib, k=0) == moe.MOE_ERR_INVALID_ARG
+    cap = moe.moe_route_align_capacity(4, 384, 8, 16)
+    assert _fwd(lib, cap=cap - 16) == moe.MOE_ERR_CAPACITY
+    ws = moe.moe_w4a16_workspace_bytes(4, 384, 7168, 2048, 8)
+    assert _fwd(lib, ws=ws - 1) == moe.MOE_ERR_WORKSPACE
+    assert _fwd(lib, x=None) == moe.MOE_ERR_INVALID_ARG
+    assert _fwd(lib, out=FAKE + 4) == moe.MOE_ERR_INVALID_ARG
+    assert _fwd(lib, M=1 << 20) == moe.MOE_ERR_UNSUPPORTED  # M*k*max(H, I) >= 2^31
+
+
+def test_fc_stage_validation():
+    lib = moe.lib()
+    cap = moe.moe_route_align_capacity(4, 384, 8, 16)
+    ws = moe.moe_w4a16_workspace_bytes(4, 384, 7168, 2048, 8)
+    p = FAKE
+    assert lib.moe_w4a16_fc1(p, 4, 384, 7168, 2048, 8, 16, p, p, p, cap, p, p, ws - 16, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_w4a16_fc2(4, 384, 7168, 2048, 8, 16, p, p, p, p, cap, p, p, ws, None, None) == moe.MOE_ERR_INVALID_ARG

@@ -1,0 +1,165 @@
+"""The full layer (moe_route_align + moe_w4a16_forward) on the GPU against the
+oracle: every element at sizes the oracle finishes in seconds (several tiles,
+ragged tails), sampled token rows at the 384-expert sizes, closed forms, and
+edge cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_moe_amd as moe
+import oracle
+import workloads as wl
+from gpu_common import (DeviceLayer, assert_output_close, assert_route_matches, device_layer, k26_layer,
+                        oracle_experts, route_host, run_layer, to_dev, x_device)
+
+pytestmark = pytest.mark.gpu
+
+MID_SHAPES = [
+    # (shape, M, weight seed, token seed): several tiles in N and K, ragged M
+    (wl.TINY, 16, 0, 0),
+    (wl.LayerShape(E=16, H=512, I=256, k=4), 37, 1, 2),
+    (wl.LayerShape(E=64, H=1024, I=384, k=6), 100, 3, 4),
+    (wl.LayerShape(E=32, H=384, I=640, k=1), 70, 5, 6),
+    (wl.LayerShape(E=4, H=256, I=128, k=4), 200, 7, 8),   # every expert gets every token: many blocks
+]
+
+
+@pytest.mark.parametrize("case", range(len(MID_SHAPES)))
+@pytest.mark.parametrize("block_m", [16, 32, 64])
+def test_full_parity_mid_shapes(case, block_m):
+    shape, M, wseed, tseed = MID_SHAPES[case]
+    print(f"forward {shape} M={M} block_m={block_m}", flush=True)
+    layer = device_layer(shape, wseed)
+    t = wl.tokens(shape, M, tseed)
+    rb, out = run_layer(layer, t.logits, t.x_bits, block_m)
+    ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, block_m)
+    x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)
+    ref = oracle.moe_forward(x, ids, w, oracle_experts(shape, wseed))
+    assert np.all(np.isfinite(out))
+    assert_output_close(out, ref, f"{shape} M={M} B={block_m}")
+
+
+def const_layer(shape, byte=0x99, scale_bits=0x2000):
+    E, H, I = shape.E, shape.H, shape.I
+    q13 = torch.full((E, 2 * I, H // 2), byte, dtype=torch.uint8, device="cuda")
+    s13 = torch.full((E, 2 * I, H // 32), scale_bits, dtype=torch.int16, device="cuda").view(torch.float16)
+    q2 = torch.full((E, H, I // 2), byte, dtype=torch.uint8, device="cuda")
+    s2 = torch.full((E, H, I // 32), scale_bits, dtype=torch.int16, device="cuda").view(torch.float16)
+    layer = DeviceLayer.__new__(DeviceLayer)
+    layer.shape = shape
+    layer.w13 = moe.repack(q13, s13, moe.KIND_W13)
+    layer.w2 = moe.repack(q2, s2, moe.KIND_W2)
+    torch.cuda.synchronize()
+    return layer
+
+
+@pytest.mark.parametrize("shape,M,expect", [
+    (wl.TINY, 16, 3.515625),   # act = bf16(silu(2) * 2) = 3.515625, y = act * I/128 = act
+    (wl.K26, 3, 50176.0),      # gate = up = 56, act = 3136, y = 16 * 3136, all exact
+])
+def test_closed_form_constant_weights(shape, M, expect):
+    """q = +1, s = 2^-7, x = 1: out = (I/128) * bf16(silu(H/128) * H/128), exactly."""
+    layer = const_layer(shape)
+    rng = np.random.default_rng(11)
+    logits = rng.standard_normal((M, shape.E)).astype(np.float32)
+    x_bits = wl.bf16_bits_from_f32(np.ones((M, shape.H), np.float32))
+    for block_m in (16, 64):
+        _, out = run_layer(layer, logits, x_bits, block_m)
+        assert np.all(out == expect), (block_m, np.unique(out)[:8])
+    h = shape.H / 128
+    act = h / (1 + math.exp(-h)) * h
+    assert abs(act * shape.I / 128 - expect) <= 2 ** -7 * expect  # the bf16 rounding of act
+
+
+def test_zero_input_gives_zero_output():
+    shape = wl.LayerShape(E=16, H=512, I=256, k=4)
+    layer = device_layer(shape, 1)
+    rng = np.random.default_rng(2)
+    logits = rng.standard_normal((40, shape.E)).astype(np.float32)
+    x_bits = np.zeros((40, shape.H), np.uint16)
+    _, out = run_layer(layer, logits, x_bits, 16)
+    assert np.all(out == 0.0)
+
+
+def test_empty_batch_is_a_no_op():
+    shape = wl.TINY
+    layer = device_layer(shape, 0)
+    rb = moe.alloc_route_buffers(0, shape.E, shape.k, 16)
+    out = torch.full((0, shape.H), 1.0, dtype=torch.bfloat16, device="cuda")
+    x = torch.empty((0, shape.H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    moe.moe_w4a16_forward(x, shape.E, shape.I, shape.k, 16, rb.topk_weights, rb.sorted_token_ids,
+                          rb.block_expert_ids, rb.expert_offsets, rb.num_tokens_post_pad, layer.w13, layer.w2,
+                          ws, out, cap=rb.cap)
+    torch.cuda.synchronize()
+
+
+def test_output_guard_bands_and_reuse():
+    """Output rows outside [0, M) untouched; a second, smaller call reuses the workspace."""
+    shape = wl.LayerShape(E=16, H=512, I=256, k=4)
+    layer = device_layer(shape, 1)
+    big = moe.moe_w4a16_workspace_bytes(60, shape.E, shape.H, shape.I, shape.k)
+    ws = torch.full((big,), 0xAB, dtype=torch.uint8, device="cuda")
+    experts = oracle_experts(shape, 1)
+    for M in (60, 23):
+        t = wl.tokens(shape, M, 100 + M)
+        rb = moe.alloc_route_buffers(M, shape.E, shape.k, 16)
+        moe.route_align(to_dev(t.logits), rb)
+        G = 3
+        guarded = torch.full((M + 2 * G, shape.H), -7.0, dtype=torch.bfloat16, device="cuda")
+        moe.forward(x_device(t.x_bits), rb, shape.I, layer.w13, layer.w2, workspace=ws, out=guarded[G:G + M])
+        torch.cuda.synchronize()
+        g = guarded.float().cpu().numpy()
+        assert np.all(g[:G] == -7.0) and np.all(g[-G:] == -7.0)
+        ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, 16)
+        x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)
+        assert_output_close(g[G:G + M], oracle.moe_forward(x, ids, w, experts), f"M={M}")
+
+
+# ---------------------------------------------------------------- 384-expert layer
+K26_SAMPLES = {
+    "k26_m1": [0],
+    "k26_m9": [0, 4, 8],
+    "k26_m90": [0, 57, 89],
+    "k26_m256": [0, 255],
+    "k26_m1024": [0, 700, 1023],
+    "k26_m1024_skew": [0, 1023],
+}
+
+
+@pytest.mark.parametrize("name", list(K26_SAMPLES))
+def test_k26_sampled_parity(name):
+    w = wl.WORKLOADS[name]
+    s = w.shape
+    print(f"forward {name}: building/using the 384-expert layer", flush=True)
+    layer = k26_layer()
+    t = wl.workload_tokens(w)
+    block_m = moe.moe_w4a16_preferred_block_m(w.M, s.E, s.H, s.I, s.k)
+    rb, out = run_layer(layer, t.logits, t.x_bits, block_m)
+    print(f"forward {name}: block_m={block_m}, checking routing", flush=True)
+    ids, wts = assert_route_matches(route_host(rb), t.logits, s.E, s.k, block_m)
+    assert np.all(np.isfinite(out))
+    rows = list(K26_SAMPLES[name])
+    if name.endswith("skew"):  # also a token routed to the hottest expert
+        hot = np.bincount(ids.reshape(-1), minlength=s.E).argmax()
+        rows.append(int(np.nonzero((ids == hot).any(axis=1))[0][5]))
+    x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)
+    ref = oracle.moe_forward(x, ids, wts, oracle_experts(s, 2026, keep=0), tokens_subset=rows)
+    rel, mx = assert_output_close(out[rows], ref[rows], name)
+    print(f"forward {name}: rows {rows} rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("block_m", [16, 32, 64])
+def test_k26_m90_every_block_m(block_m):
+    w = wl.WORKLOADS["k26_m90"]
+    s = w.shape
+    layer = k26_layer()
+    t = wl.workload_tokens(w)
+    rb, out = run_layer(layer, t.logits, t.x_bits, block_m)
+    ids, wts = assert_route_matches(route_host(rb), t.logits, s.E, s.k, block_m)
+    x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)
+    rows = [13]
+    ref = oracle.moe_forward(x, ids, wts, oracle_experts(s, 2026, keep=0), tokens_subset=rows)
+    assert_output_close(out[rows], ref[rows], f"k26_m90 B={block_m}")
