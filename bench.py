@@ -1,0 +1,321 @@
+"""Benchmark of the INT4 (group 32) weight-only MoE layer on one MI355X.
+
+One step = one layer call over one batch: moe_route_align, then the two
+stages of moe_w4a16_forward (FC1, FC2). The headline workload is the
+384-expert layer (hidden 7168, intermediate 2048, top-8) at M = 1 token
+(one decoding stream), the shape of "The Throughput Lever: Quantifying the MoE
+GEMM and Mapping the Road to B300", section "The Result: Two Regimes", table
+row M = 1. A sweep over M = 9, 90, 256, 512, 1024 and the skewed M = 1024
+batch is reported in the same JSON line.
+
+Weights are synthetic (random INT4 codes, fp16 scales in [0.005, 0.02]) and
+resident in HBM before timing starts. To keep the 256 MB last-level cache from
+serving a step's weights out of the previous step, the timed loop cycles
+through R copies of the layer's weights at different addresses (a model with R
+MoE layers); each step reads copy i % R.
+
+Timing: W untimed warm-up steps, then K steps bracketed by
+torch.cuda.synchronize(), queued behind a GPU spin so that they run back to
+back as under a HIP graph; HIP events on the launch stream bracket the K
+steps and every FC1 launch (for the roofline figure). The same K steps
+replayed from one captured HIP graph are reported as context. The CPU oracle is timed on a bounded sample of
+the same workload (cpu_baseline).
+
+    python bench.py [--steps K] [--warmup W] [--replicas R] [--no-sweep] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
+HEADLINE = "k26_m1"
+SWEEP = ["k26_m9", "k26_m90", "k26_m256", "k26_m512", "k26_m1024", "k26_m1024_skew"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_k26_m1_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--replicas", type=int, default=8)
+    p.add_argument("--workload", default=HEADLINE)
+    p.add_argument("--sweep-steps", type=int, default=30)
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def fc_source_sha() -> str:
+    with open(os.path.join(ROOT, "int4_weight_only_moe_amd", "csrc", "fc.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def layer_bytes(D, M, s):
+    """Algorithmic bytes of one layer call: touched experts' nibbles + scales,
+    x in and out (bf16), logits (fp32), ids and weights."""
+    per_expert = (2 * s.I * s.H + s.H * s.I) * 9 // 16
+    return D * per_expert + 4 * M * s.H + 4 * M * s.E + 8 * M * s.k
+
+
+def fc1_bytes(D, M, s):
+    """Algorithmic bytes of one FC1 launch: touched experts' W13 nibbles + scales,
+    the x rows, and the bf16 activations it writes."""
+    return D * (2 * s.I * s.H * 9 // 16) + 2 * M * s.H + 2 * M * s.k * s.I
+
+
+def flops(M, s):
+    return 2 * M * s.k * (2 * s.I * s.H + s.H * s.I)
+
+
+class Bench:
+    def __init__(self, replicas: int):
+        import torch
+        import int4_weight_only_moe_amd as moe
+        import workloads as wl
+
+        self.torch, self.moe, self.wl = torch, moe, wl
+        self.s = wl.K26
+        t0 = time.time()
+        w13, s13, w2, s2 = wl.layer_weights(self.s, 2026)
+        self.host = (w13, s13, w2, s2)
+        dev = "cuda"
+        q13 = torch.from_numpy(w13).to(dev)
+        sc13 = torch.from_numpy(s13).to(dev)
+        p13 = moe.repack(q13, sc13, moe.KIND_W13)
+        del q13, sc13
+        q2 = torch.from_numpy(w2).to(dev)
+        sc2 = torch.from_numpy(s2).to(dev)
+        p2 = moe.repack(q2, sc2, moe.KIND_W2)
+        del q2, sc2
+        torch.cuda.synchronize()
+        t1 = time.time()
+        # repack time on its own (one more repack of W13 + W2 from device copies)
+        self.repack_ms = self._time_repack(w13, s13, w2, s2)
+        self.layers = [(p13, p2)] + [(p13.clone(), p2.clone()) for _ in range(replicas - 1)]
+        torch.cuda.synchronize()
+        print(f"# weights: generated + repacked in {t1 - t0:.1f} s, {replicas} copies "
+              f"({replicas * (p13.numel() + p2.numel()) / 1e9:.1f} GB)", file=sys.stderr, flush=True)
+
+    def _time_repack(self, w13, s13, w2, s2):
+        torch, moe = self.torch, self.moe
+        q13, sc13 = torch.from_numpy(w13).cuda(), torch.from_numpy(s13).cuda()
+        q2, sc2 = torch.from_numpy(w2).cuda(), torch.from_numpy(s2).cuda()
+        o13 = torch.empty(moe.moe_w4a16_packed_bytes(self.s.E, 2 * self.s.I, self.s.H), dtype=torch.uint8, device="cuda")
+        o2 = torch.empty(moe.moe_w4a16_packed_bytes(self.s.E, self.s.H, self.s.I), dtype=torch.uint8, device="cuda")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        moe.moe_w4a16_repack(q13, sc13, moe.KIND_W13, o13)
+        moe.moe_w4a16_repack(q2, sc2, moe.KIND_W2, o2)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        del q13, sc13, q2, sc2, o13, o2
+        return ms
+
+    def prepare(self, name):
+        torch, moe, wl = self.torch, self.moe, self.wl
+        w = wl.WORKLOADS[name]
+        s = w.shape
+        t = wl.workload_tokens(w)
+        B = moe.moe_w4a16_preferred_block_m(w.M, s.E, s.H, s.I, s.k)
+        rb = moe.alloc_route_buffers(w.M, s.E, s.k, B)
+        logits = torch.from_numpy(t.logits).cuda()
+        x = torch.from_numpy(t.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        ws = torch.empty(moe.moe_w4a16_workspace_bytes(w.M, s.E, s.H, s.I, s.k), dtype=torch.uint8, device="cuda")
+        out = torch.empty((w.M, s.H), dtype=torch.bfloat16, device="cuda")
+        D = int(len(np.unique(self._oracle_free_ids(t.logits, s.k))))
+        return dict(w=w, t=t, B=B, rb=rb, logits=logits, x=x, ws=ws, out=out, D=D)
+
+    @staticmethod
+    def _oracle_free_ids(logits, k):
+        # touched experts for the byte count: the k largest logits per row
+        return np.argsort(-logits, axis=1, kind="stable")[:, :k]
+
+    def step(self, c, layer, ev=None):
+        moe, s = self.moe, self.s
+        rb = c["rb"]
+        moe.route_align(c["logits"], rb)
+        if ev is not None:
+            ev[0].record()
+        moe.moe_w4a16_fc1(c["x"], s.E, s.I, s.k, rb.block_m, rb.sorted_token_ids, rb.block_expert_ids,
+                          rb.num_tokens_post_pad, layer[0], c["ws"], cap=rb.cap)
+        if ev is not None:
+            ev[1].record()
+        moe.moe_w4a16_fc2(c["w"].M, s.E, s.H, s.I, s.k, rb.block_m, rb.topk_weights, rb.sorted_token_ids,
+                          rb.block_expert_ids, rb.num_tokens_post_pad, layer[1], c["ws"], c["out"], cap=rb.cap)
+
+    def run(self, name, steps, warmup, replicas):
+        """W eager warm-up steps, then K timed steps launched back to back.
+
+        The Python host needs longer to launch a step than the GPU needs to run
+        it at small M, so the timed steps are queued behind a GPU spin of known
+        length: by the time the GPU reaches the start event, every step is
+        already in the queue and runs without host gaps (as under a HIP graph).
+        Events on the launch stream bracket the K steps and each FC1 launch.
+        """
+        torch = self.torch
+        c = self.prepare(name)
+        R = min(replicas, len(self.layers))
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        for i in range(warmup):
+            self.step(c, self.layers[i % R])
+        host_per_step = (time.perf_counter() - h0) / max(warmup, 1)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        spin_s = min(2.0, 2.0 * host_per_step * steps + 2e-3)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        torch.cuda._sleep(int(spin_s * 2.4e9))
+        start.record()
+        for i in range(steps):
+            self.step(c, self.layers[i % R], evs[i])
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = start.elapsed_time(stop)
+        fc1_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        return c, total_ms / steps, fc1_us, wall
+
+    def run_graph(self, name, steps, replicas):
+        """The same K steps captured in one HIP graph and replayed (context)."""
+        torch = self.torch
+        c = self.prepare(name)
+        R = min(replicas, len(self.layers))
+        self.step(c, self.layers[0])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                self.step(c, self.layers[i % R])
+        g.replay()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        del g
+        return start.elapsed_time(stop) / steps
+
+    def record(self, name, steps, warmup, replicas):
+        c, ms, fc1_us, wall = self.run(name, steps, warmup, replicas)
+        w, s, D = c["w"], self.s, c["D"]
+        us = ms * 1e3
+        return dict(
+            workload=name, M=w.M, block_m=c["B"], experts_touched=D, us_per_call=round(us, 2),
+            us_per_token=round(us / w.M, 3), hbm_TBps=round(layer_bytes(D, w.M, s) / (us * 1e-6) / 1e12, 3),
+            mfma_pct=round(100 * flops(w.M, s) / (us * 1e-6) / (MFMA_BF16_PEAK_TFS * 1e12), 2),
+            roofline_frac=round(max(layer_bytes(D, w.M, s) / (HBM_PEAK_GBS * 1e9),
+                                    flops(w.M, s) / (MFMA_BF16_PEAK_TFS * 1e12)) / (us * 1e-6), 4),
+            fc1_us=round(fc1_us, 2), fc1_GBps=round(fc1_bytes(D, w.M, s) / (fc1_us * 1e-6) / 1e9, 1),
+            replicas=min(replicas, len(self.layers)), wall_s=round(wall, 3)), c
+
+    def cpu_baseline(self, c, budget_s=12.0):
+        """The oracle (as it stands) on the headline batch, repeated for about budget_s seconds."""
+        import oracle
+        import workloads as wl
+        w13, s13, w2, s2 = self.host
+        cache = oracle.DequantCache(lambda e: (w13[e], s13[e], w2[e], s2[e]), max_items=0)
+        t = c["t"]
+        x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)
+        tokens, n = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.layer(x, t.logits, self.s.k, cache)
+            tokens += t.logits.shape[0]
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        el = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        except Exception:
+            blas = 1
+        return {"value": round(el / tokens * 1e6, 1), "unit": "us/token", "cores": int(blas), "kind": "oracle",
+                "sample": f"{n} full oracle calls (route, dequantise 8 experts in float64, expert MLPs, combine) "
+                          f"on the {c['w'].M}-token batch, {el:.1f} s; dequantisation single-threaded numpy, "
+                          f"matmuls on {blas} BLAS threads; host has {len(os.sched_getaffinity(0))} cores"}
+
+
+def traffic_for(launch_bytes_alg):
+    """HBM bytes per FC1 launch from committed rocprofv3 counter runs, if they
+    were taken on the current FC1 source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        d = json.load(f)
+    if d.get("fc_source_sha") != fc_source_sha():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported in this build "
+              "(the layer's multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    b = Bench(a.replicas)
+    head, c = b.record(a.workload, a.steps, a.warmup, a.replicas)
+    s, D, M = b.s, c["D"], c["w"].M
+    fc1_alg = fc1_bytes(D, M, s)
+    fc1_s = head["fc1_us"] * 1e-6
+    sweep = []
+    if not a.no_sweep:
+        for name in SWEEP:
+            r, _ = b.record(name, a.sweep_steps, 5, a.replicas)
+            sweep.append(r)
+            print(f"# {json.dumps(r)}", file=sys.stderr, flush=True)
+        warm, _ = b.record(a.workload, a.sweep_steps, 5, 1)
+        warm["note"] = "one weight copy: consecutive steps may hit the last-level cache (context only)"
+        sweep.append(warm)
+    cpu = None if a.no_cpu_baseline else b.cpu_baseline(c)
+    line = {
+        "metric": "MoE layer us/token (+ achieved HBM TB/s, MFMA %) on the 384-expert INT4 g32 layer",
+        "value": head["us_per_token"],
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(head["us_per_call"] / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random INT4 weights and router logits, bf16 N(0,1) activations)",
+        "config": {"workload": f"{a.workload}: E=384, H=7168, I=2048, top-8, INT4 g32, M={M} tokens",
+                   "global_batch": M, "block_m": head["block_m"], "experts_touched": D,
+                   "weight_copies_cycled": head["replicas"],
+                   "launch": "eager, queued ahead of the GPU"},
+        "graph_us_per_call": round(b.run_graph(a.workload, a.steps, a.replicas) * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(fc1_alg / fc1_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(fc1_alg / fc1_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for(fc1_alg), "kernel": "fc_kernel<16, FC1>",
+                     "kernel_avg_us": head["fc1_us"], "algorithmic_bytes": fc1_alg},
+        "layer": {k: head[k] for k in ("us_per_call", "hbm_TBps", "mfma_pct", "roofline_frac")},
+        "repack_ms": round(b.repack_ms, 2),
+        "sweep": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -137,8 +137,8 @@ int moe_w4a16_unpack(const void* packed, int32_t E, int32_t N, int32_t K, int32_
 
 /*
  * moe_w4a16_workspace_bytes (host): scratch the forward needs for M tokens:
- * an fp32 [M, H] accumulator, per-(token, 32-column tile) arrival counters and
- * the bf16 [M*top_k, I] FC1 activations. Returns -1 on invalid sizes.
+ * an fp32 [M, H] accumulator and the bf16 [M*top_k, I] FC1 activations, each
+ * padded to 256 bytes. Returns -1 on invalid sizes.
  */
 int64_t moe_w4a16_workspace_bytes(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k);
 
@@ -176,7 +176,7 @@ int moe_w4a16_forward(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, i
  * moe_w4a16_fc1: first stage of moe_w4a16_forward. For every assignment f in
  * sorted_token_ids (expert e, token t = f / top_k) it computes
  * h = W13_e x_t, stores act_f = bf16(SiLU(h[0:I]) * h[I:2I]) in the
- * workspace, and clears the accumulator and counters stage 2 uses.
+ * workspace, and clears the fp32 accumulator stage 2 uses.
  */
 int moe_w4a16_fc1(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
                   int32_t top_k, int32_t block_m,
@@ -185,9 +185,8 @@ int moe_w4a16_fc1(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32
                   const void* w13_packed, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
- * moe_w4a16_fc2: second stage. y_f = W2_e act_f; out[t] += topk_weights[f] * y_f
- * in fp32; each [token, 32-column] tile is rounded to bf16 into out_bf16 by
- * whichever workgroup adds its last (top_k-th) contribution. Must follow
+ * moe_w4a16_fc2: second stage. y_f = W2_e act_f; acc[t] += topk_weights[f] * y_f
+ * in fp32 (atomics), then out_bf16 = bf16(acc) in one rounding. Must follow
  * moe_w4a16_fc1 with the same workspace on the same stream.
  */
 int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,

@@ -151,11 +151,10 @@ static moe::FcArgs fc_args(int32_t M, int32_t E, int32_t H, int32_t I, int32_t t
   a.block_expert = block_expert;
   a.npp = npp;
   a.acc = (float*)(ws + L.acc_off);
-  a.counters = (uint32_t*)(ws + L.cnt_off);
   a.act_out = (uint16_t*)(ws + L.act_off);
   a.M = M; a.E = E; a.H = H; a.I = I; a.k = top_k; a.block_m = block_m;
   a.cap = cap;
-  a.zero_words16 = (L.cnt_off + (int64_t)M * (H / kPairRows) * 4) / 16;
+  a.zero_words16 = (int64_t)M * H * 4 / 16;
   return a;
 }
 

@@ -28,16 +28,15 @@ __host__ __device__ inline int64_t packed_bytes_per_expert(int64_t N, int64_t K)
   return (N / kPairRows) * (K / kChunkK) * kPairChunkBytes;
 }
 
-// Workspace layout of the forward: [acc fp32 M x H][counters u32 M x H/32][act bf16 M*k x I]
+// Workspace layout of the forward: [acc fp32 M x H][act bf16 M*k x I]
 struct WorkspaceLayout {
-  int64_t acc_off, cnt_off, act_off, total;
+  int64_t acc_off, act_off, total;
 };
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 inline WorkspaceLayout workspace_layout(int64_t M, int64_t H, int64_t I, int64_t k) {
   WorkspaceLayout w;
   w.acc_off = 0;
-  w.cnt_off = align256(M * H * 4);
-  w.act_off = w.cnt_off + align256(M * (H / kPairRows) * 4);
+  w.act_off = align256(M * H * 4);
   w.total = w.act_off + align256(M * k * I * 2);
   return w;
 }
@@ -62,11 +61,10 @@ struct FcArgs {
   const float* topk_weights;   // FC2 only, [M*k]
   uint16_t* act_out;           // FC1 only: act [M*k, I]
   float* acc;                  // fp32 [M, H]
-  uint32_t* counters;          // [M, H/32]
   uint16_t* out;               // FC2 only: bf16 [M, H]
   int M, E, H, I, k, block_m;
   int64_t cap;
-  int64_t zero_words16;         // FC1: 16-byte words to clear at acc (accumulator + counters)
+  int64_t zero_words16;         // FC1: 16-byte words of acc to clear
 };
 
 hipError_t launch_fc1(const FcArgs& a, hipStream_t stream);

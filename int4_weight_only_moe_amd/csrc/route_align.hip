@@ -37,21 +37,58 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    uint32_t olo = (uint32_t)__shfl_xor((int)lo, off, 64);
-    uint32_t ohi = (uint32_t)__shfl_xor((int)hi, off, 64);
-    uint64_t o = ((uint64_t)ohi << 32) | olo;
-    v = o > v ? o : v;
+// Cross-lane exchanges without LDS: DPP inside rows of 16 lanes, then the
+// gfx950 row swaps (permlane16/32_swap) across rows. After each step every
+// lane holds the combination of itself and its partner, so after all six
+// every lane holds the value of the whole wave.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, kCtrl, 0xf, 0xf, false);
+}
+constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// (hi, lo) lexicographic max
+__device__ __forceinline__ void max_pair(uint32_t& hi, uint32_t& lo, uint32_t ohi, uint32_t olo) {
+  const bool take = (ohi > hi) || (ohi == hi && olo > lo);
+  hi = take ? ohi : hi;
+  lo = take ? olo : lo;
+}
+
+__device__ __forceinline__ void wave_max_pair(uint32_t& hi, uint32_t& lo) {
+  max_pair(hi, lo, dpp<kQuadSwap1>(hi), dpp<kQuadSwap1>(lo));
+  max_pair(hi, lo, dpp<kQuadSwap2>(hi), dpp<kQuadSwap2>(lo));
+  max_pair(hi, lo, dpp<kRowHalfMirror>(hi), dpp<kRowHalfMirror>(lo));
+  max_pair(hi, lo, dpp<kRowMirror>(hi), dpp<kRowMirror>(lo));
+  {  // rows 0<->1, 2<->3: one of the two results is this lane's own value
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    hi = h[0]; lo = l[0];
+    max_pair(hi, lo, h[1], l[1]);
   }
-  return v;
+  {  // halves 0-31 <-> 32-63
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    hi = h[0]; lo = l[0];
+    max_pair(hi, lo, h[1], l[1]);
+  }
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  v += __uint_as_float(dpp<kQuadSwap1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kQuadSwap2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kRowHalfMirror>(__float_as_uint(v)));
+  v += __uint_as_float(dpp<kRowMirror>(__float_as_uint(v)));
+  {
+    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  }
+  {
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  }
   return v;
 }
 
@@ -59,7 +96,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Candidates compare as (key << 32) | ~e, so equal logits prefer the lower e.
 template <int VPL>
 __device__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
-                           int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+                           int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                           int32_t* ids_copy = nullptr) {
   const int lane = threadIdx.x & 63;
   uint32_t key[VPL];
   const float* row = logits + (int64_t)t * E;
@@ -71,30 +109,32 @@ __device__ void topk_token(const float* __restrict__ logits, int t, int E, int k
   uint32_t my_key = 0;
   int my_e = 0;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
+    // this lane's best candidate: largest key, then smallest expert (~e larger)
+    uint32_t bhi = 0, blo = 0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      uint32_t e = (uint32_t)(v * 64 + lane);
-      uint64_t c = ((uint64_t)key[v] << 32) | (uint32_t)~e;
-      best = (key[v] != 0u && c > best) ? c : best;
+      const uint32_t ne = ~(uint32_t)(v * 64 + lane);
+      const bool take = key[v] != 0u && (key[v] > bhi || (key[v] == bhi && ne > blo));
+      bhi = take ? key[v] : bhi;
+      blo = take ? ne : blo;
     }
-    best = wave_max_u64(best);
-    const uint32_t win_e = ~(uint32_t)best;
-    const uint32_t win_key = (uint32_t)(best >> 32);
+    wave_max_pair(bhi, blo);
+    const uint32_t win_e = ~blo;
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
       if ((uint32_t)(v * 64 + lane) == win_e) key[v] = 0u;
     if (lane == r) {
-      my_key = win_key;
+      my_key = bhi;
       my_e = (int)win_e;
     }
   }
-  const float l0 = key_value((uint32_t)__shfl((int)my_key, 0, 64));
+  const float l0 = key_value(__builtin_amdgcn_readfirstlane(my_key));
   const float ex = (lane < k) ? expf(key_value(my_key) - l0) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
     topk_ids[(int64_t)t * k + lane] = my_e;
     topk_w[(int64_t)t * k + lane] = ex / sum;
+    if (ids_copy) ids_copy[t * k + lane] = my_e;
   }
 }
 
@@ -128,11 +168,14 @@ __device__ void align_body(AlignShared& sh, const int32_t* __restrict__ ids, int
                            int32_t* __restrict__ block_expert, int32_t* __restrict__ offsets,
                            int32_t* __restrict__ npp_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += kAlignThreads) {
-    sh.cnt[e] = 0;
-    sh.run[e] = 0;
+  if (tid < E) {
+    sh.cnt[tid] = 0;
+    sh.run[tid] = 0;
+    if (MK > 64) {
+#pragma unroll
+      for (int w = 0; w < kAlignWaves; ++w) sh.wcnt[w][tid] = 0;
+    }
   }
-  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) sh.wcnt[i / E][i % E] = 0;
   __syncthreads();
   for (int f = tid; f < MK; f += kAlignThreads) {
     int e = ids[f];
@@ -173,6 +216,20 @@ __device__ void align_body(AlignShared& sh, const int32_t* __restrict__ ids, int
   }
 
   // stable placement
+  if (MK <= 64) {
+    // one wave's worth: rank among equal experts of the earlier lanes only
+    if (wave == 0) {
+      const int e = (lane < MK) ? ids[lane] : -1;
+      int before = 0;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        before += (j < lane && ej == e) ? 1 : 0;
+      }
+      if (e >= 0 && e < E) sorted_ids[sh.off[e] + before] = lane;
+    }
+    return;
+  }
   for (int base = 0; base < MK; base += kAlignThreads) {
     const int f = base + tid;
     int e = (f < MK) ? ids[f] : -1;
@@ -192,6 +249,7 @@ __device__ void align_body(AlignShared& sh, const int32_t* __restrict__ ids, int
       for (int w = 0; w < wave; ++w) pos += sh.wcnt[w][e];
       sorted_ids[pos] = f;
     }
+    if (base + kAlignThreads >= MK) break;  // last chunk: nothing to carry
     __syncthreads();
     if (tid < E) {
       int s = 0;
@@ -220,11 +278,11 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_fused_kernel(
     float* __restrict__ topk_w, int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ offsets, int32_t* __restrict__ npp) {
   __shared__ AlignShared sh;
+  __shared__ int32_t ids_lds[kFusedMaxTokens * 16];
   const int wave = threadIdx.x >> 6;
-  if (wave < M) topk_token<VPL>(logits, wave, E, k, topk_ids, topk_w);
-  __threadfence_block();
+  if (wave < M) topk_token<VPL>(logits, wave, E, k, topk_ids, topk_w, ids_lds);
   __syncthreads();
-  align_body(sh, topk_ids, M * k, E, block_m, sorted_ids, block_expert, offsets, npp);
+  align_body(sh, ids_lds, M * k, E, block_m, sorted_ids, block_expert, offsets, npp);
 }
 
 template <int VPL>
