@@ -1,7 +1,8 @@
 """Benchmark of the INT4 (group 32) weight-only MoE layer on one MI355X.
 
-One step = one layer call over one batch: moe_route_align, then the two
-stages of moe_w4a16_forward (FC1, FC2). The headline workload is the
+One step = one layer call over one batch through moe_w4a16_layer: routing,
+FC1 (gate/up, SiLU*mul) and FC2 with the weighted combine (two kernels for
+M <= 4, four above). The headline workload is the
 384-expert layer (hidden 7168, intermediate 2048, top-8) at M = 1 token
 (one decoding stream), the shape of "The Throughput Lever: Quantifying the MoE
 GEMM and Mapping the Road to B300", section "The Result: Two Regimes", table
@@ -79,6 +80,36 @@ def flops(M, s):
     return 2 * M * s.k * (2 * s.I * s.H + s.H * s.I)
 
 
+class HipEvent:
+    """A raw hipEvent_t (the library records it on the launch stream)."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = hip
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreate(ctypes.byref(self.ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.handle = self.ev.value
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        t = self._ct.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(self._ct.byref(t), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return t.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.ev:
+            HipEvent._hip.hipEventDestroy(self.ev)
+
+
 class Bench:
     def __init__(self, replicas: int):
         import torch
@@ -144,17 +175,11 @@ class Bench:
         return np.argsort(-logits, axis=1, kind="stable")[:, :k]
 
     def step(self, c, layer, ev=None):
-        moe, s = self.moe, self.s
-        rb = c["rb"]
-        moe.route_align(c["logits"], rb)
-        if ev is not None:
-            ev[0].record()
-        moe.moe_w4a16_fc1(c["x"], s.E, s.I, s.k, rb.block_m, rb.sorted_token_ids, rb.block_expert_ids,
-                          rb.num_tokens_post_pad, layer[0], c["ws"], cap=rb.cap)
-        if ev is not None:
-            ev[1].record()
-        moe.moe_w4a16_fc2(c["w"].M, s.E, s.H, s.I, s.k, rb.block_m, rb.topk_weights, rb.sorted_token_ids,
-                          rb.block_expert_ids, rb.num_tokens_post_pad, layer[1], c["ws"], c["out"], cap=rb.cap)
+        """One layer call: moe_w4a16_layer (routing + FC1 + FC2); ev = optional
+        pair of HIP events recorded around its FC1 stage."""
+        s = self.s
+        self.moe.layer(c["logits"], c["x"], c["rb"], s.I, layer[0], layer[1], workspace=c["ws"], out=c["out"],
+                       stage_events=None if ev is None else (ev[0].handle, ev[1].handle))
 
     def run(self, name, steps, warmup, replicas):
         """W eager warm-up steps, then K timed steps launched back to back.
@@ -174,7 +199,7 @@ class Bench:
             self.step(c, self.layers[i % R])
         host_per_step = (time.perf_counter() - h0) / max(warmup, 1)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         spin_s = min(2.0, 2.0 * host_per_step * steps + 2e-3)
         torch.cuda.synchronize()
@@ -187,7 +212,7 @@ class Bench:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         total_ms = start.elapsed_time(stop)
-        fc1_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        fc1_us = float(np.mean([a.elapsed_ms(b) for a, b in evs])) * 1e3
         return c, total_ms / steps, fc1_us, wall
 
     def run_graph(self, name, steps, replicas):
@@ -307,7 +332,7 @@ def main():
         "graph_us_per_call": round(b.run_graph(a.workload, a.steps, a.replicas) * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(fc1_alg / fc1_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(fc1_alg / fc1_s / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for(fc1_alg), "kernel": "fc_kernel<16, FC1>",
+                     "traffic": traffic_for(fc1_alg), "kernel": "FC1 stage (fc1_decode_kernel for M <= 4, else fc_kernel FC1)",
                      "kernel_avg_us": head["fc1_us"], "algorithmic_bytes": fc1_alg},
         "layer": {k: head[k] for k in ("us_per_call", "hbm_TBps", "mfma_pct", "roofline_frac")},
         "repack_ms": round(b.repack_ms, 2),

@@ -195,6 +195,31 @@ int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int
                   const void* w2_packed, void* workspace, int64_t workspace_bytes,
                   uint16_t* out_bf16, void* stream);
 
+/*
+ * moe_w4a16_layer: one whole layer call, moe_route_align followed by
+ * moe_w4a16_forward, with the same arguments, outputs and results (integer
+ * outputs identical, out_bf16 within the same tolerance).
+ *
+ * "The Throughput Lever: Quantifying the MoE GEMM and Mapping the Road to
+ * B300", section "The B300 Analysis: When the Bottleneck Flips": at decode
+ * sizes fixed per-step costs such as kernel launches dominate once the GEMM
+ * runs at HBM speed. For M <= 4 and M*top_k <= 64 this call therefore runs
+ * two kernels instead of four: the routing is recomputed inside every FC1
+ * workgroup (workgroup 0 also writes the routing/grouping outputs), and FC2
+ * is output-stationary (each output tile sums its token's top_k expert
+ * results in slot order in one workgroup: no atomics, and the bf16 output is
+ * then identical on every call). Larger batches take the four-kernel path.
+ *   stage_events  NULL, or two hipEvent_t: [0] is recorded on the stream just
+ *                 before the FC1 stage (for M <= 4 the routing is part of it),
+ *                 [1] just after it; for timing the stages.
+ */
+int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
+                    int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights,
+                    int32_t* sorted_token_ids, int32_t* block_expert_ids, int32_t* expert_offsets,
+                    int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed, const void* w2_packed,
+                    void* workspace, int64_t workspace_bytes, uint16_t* out_bf16, void* stream,
+                    void* const* stage_events);
+
 #ifdef __cplusplus
 }
 #endif

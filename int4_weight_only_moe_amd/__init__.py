@@ -17,7 +17,7 @@ import torch
 from ._binding import (  # noqa: F401
     GROUP, KIND_W13, KIND_W2, MOE_ERR_CAPACITY, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE, MOE_OK, MoeError, lib, library_path, moe_route_align, moe_route_align_capacity,
-    moe_w4a16_abi_version, moe_w4a16_fc1, moe_w4a16_fc2, moe_w4a16_forward, moe_w4a16_packed_bytes,
+    moe_w4a16_abi_version, moe_w4a16_fc1, moe_w4a16_fc2, moe_w4a16_forward, moe_w4a16_layer, moe_w4a16_packed_bytes,
     moe_w4a16_preferred_block_m, moe_w4a16_repack, moe_w4a16_unpack, moe_w4a16_workspace_bytes, status_string,
 )
 
@@ -78,4 +78,20 @@ def forward(x: torch.Tensor, rb: RouteBuffers, I: int, w13_packed: torch.Tensor,
     moe_w4a16_forward(x, rb.E, I, rb.top_k, rb.block_m, rb.topk_weights, rb.sorted_token_ids,
                       rb.block_expert_ids, rb.expert_offsets, rb.num_tokens_post_pad, w13_packed, w2_packed,
                       workspace, out, cap=rb.cap, stream=stream)
+    return out
+
+
+def layer(logits: torch.Tensor, x: torch.Tensor, rb: RouteBuffers, I: int, w13_packed: torch.Tensor,
+          w2_packed: torch.Tensor, workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+          stream=None, stage_events=None) -> torch.Tensor:
+    """Routing + expert MLPs in one call (two kernels for M <= 4, four above)."""
+    M, H = x.shape
+    if workspace is None:
+        workspace = torch.empty(max(moe_w4a16_workspace_bytes(M, rb.E, H, I, rb.top_k), 16),
+                                dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    moe_w4a16_layer(logits, x, I, rb.top_k, rb.block_m, rb.topk_ids, rb.topk_weights, rb.sorted_token_ids,
+                    rb.block_expert_ids, rb.expert_offsets, rb.num_tokens_post_pad, w13_packed, w2_packed,
+                    workspace, out, cap=rb.cap, stream=stream, stage_events=stage_events)
     return out

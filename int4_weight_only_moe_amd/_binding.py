@@ -47,6 +47,8 @@ _SIGNATURES = {
                                      _i64, _vp]),
     "moe_w4a16_fc2": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                                      _i64, _vp, _vp]),
+    "moe_w4a16_layer": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
 }
 
 
@@ -213,3 +215,32 @@ def moe_w4a16_fc2(M: int, E: int, H: int, I: int, top_k: int, block_m: int, topk
         _ptr(w2_packed, torch.uint8, "w2_packed"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), _ptr(out, torch.bfloat16, "out"), _stream(stream))
     _check("moe_w4a16_fc2", st)
+
+
+def moe_w4a16_layer(logits: torch.Tensor, x: torch.Tensor, I: int, top_k: int, block_m: int,
+                    topk_ids: torch.Tensor, topk_weights: torch.Tensor, sorted_token_ids: torch.Tensor,
+                    block_expert_ids: torch.Tensor, expert_offsets: torch.Tensor,
+                    num_tokens_post_pad: torch.Tensor, w13_packed: torch.Tensor, w2_packed: torch.Tensor,
+                    workspace: torch.Tensor, out: torch.Tensor, cap: int | None = None, stream=None,
+                    stage_events=None) -> None:
+    """stage_events: None or a pair of raw hipEvent_t handles (ints)."""
+    M, E = logits.shape
+    H = x.shape[1]
+    if x.shape[0] != M:
+        raise ValueError("logits and x must have the same number of rows")
+    if cap is None:
+        cap = sorted_token_ids.numel()
+    ev = None
+    if stage_events is not None:
+        ev = (ctypes.c_void_p * 2)(int(stage_events[0]), int(stage_events[1]))
+    st = lib().moe_w4a16_layer(
+        _ptr(logits, torch.float32, "logits"), _ptr(x, torch.bfloat16, "x"), M, E, H, I, top_k, block_m,
+        _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_weights, torch.float32, "topk_weights"),
+        _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
+        _ptr(block_expert_ids, torch.int32, "block_expert_ids"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"),
+        _ptr(num_tokens_post_pad, torch.int32, "num_tokens_post_pad"), cap,
+        _ptr(w13_packed, torch.uint8, "w13_packed"), _ptr(w2_packed, torch.uint8, "w2_packed"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _ptr(out, torch.bfloat16, "out"),
+        _stream(stream), ev)
+    _check("moe_w4a16_layer", st)

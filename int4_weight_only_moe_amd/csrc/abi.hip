@@ -12,7 +12,7 @@ using moe::kPairRows;
 
 constexpr int32_t kAbiVersion = 1;
 constexpr int32_t kMaxExperts = 1024;
-constexpr int32_t kMaxTopK = 16;
+using moe::kMaxTopK;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -216,6 +216,57 @@ int moe_w4a16_forward(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, i
   st = moe_w4a16_fc1(x_bf16, M, E, H, I, top_k, block_m, sorted_token_ids, block_expert_ids,
                      num_tokens_post_pad, cap, w13_packed, workspace, workspace_bytes, stream);
   if (st != MOE_OK) return st;
+  return moe_w4a16_fc2(M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
+                       num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
+}
+
+int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
+                    int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights,
+                    int32_t* sorted_token_ids, int32_t* block_expert_ids, int32_t* expert_offsets,
+                    int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed, const void* w2_packed,
+                    void* workspace, int64_t workspace_bytes, uint16_t* out_bf16, void* stream,
+                    void* const* stage_events) {
+  int st = check_fc(M, E, H, I, top_k, block_m, cap, workspace_bytes);
+  if (st != MOE_OK || M == 0) return st;
+  if (!logits || !x_bf16 || !topk_ids || !topk_weights || !sorted_token_ids || !block_expert_ids ||
+      !expert_offsets || !num_tokens_post_pad || !w13_packed || !w2_packed || !workspace || !out_bf16)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned4(logits) || !aligned16(x_bf16) || !aligned4(topk_ids) || !aligned4(topk_weights) ||
+      !aligned4(sorted_token_ids) || !aligned4(block_expert_ids) || !aligned4(expert_offsets) ||
+      !aligned4(num_tokens_post_pad) || !aligned16(w13_packed) || !aligned16(w2_packed) ||
+      !aligned16(workspace) || !aligned16(out_bf16))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t ev0 = stage_events ? (hipEvent_t)stage_events[0] : nullptr;
+  hipEvent_t ev1 = stage_events ? (hipEvent_t)stage_events[1] : nullptr;
+  if ((int64_t)M <= moe::kDecodeMaxTokens && (int64_t)M * top_k <= moe::kDecodeMaxAssign) {
+    moe::DecodeArgs d{};
+    d.fc = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
+                   workspace);
+    d.fc.act_in = x_bf16;
+    d.fc.wpacked = (const uint8_t*)w13_packed;
+    d.fc.topk_weights = topk_weights;
+    d.fc.out = out_bf16;
+    d.logits = logits;
+    d.w2 = (const uint8_t*)w2_packed;
+    d.topk_ids = topk_ids;
+    d.topk_weights = topk_weights;
+    d.sorted_ids = sorted_token_ids;
+    d.block_expert = block_expert_ids;
+    d.expert_offsets = expert_offsets;
+    d.npp_out = num_tokens_post_pad;
+    d.block_m = block_m;
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(moe::launch_decode(d, s, ev1));
+  }
+  st = moe_route_align(logits, M, E, top_k, block_m, topk_ids, topk_weights, sorted_token_ids, block_expert_ids,
+                       expert_offsets, num_tokens_post_pad, cap, stream);
+  if (st != MOE_OK) return st;
+  if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return MOE_ERR_HIP;
+  st = moe_w4a16_fc1(x_bf16, M, E, H, I, top_k, block_m, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
+                     cap, w13_packed, workspace, workspace_bytes, stream);
+  if (st != MOE_OK) return st;
+  if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return MOE_ERR_HIP;
   return moe_w4a16_fc2(M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
                        num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
 }

@@ -1,0 +1,263 @@
+// Decode path of the layer for tiny batches (M <= 4 tokens, M*k <= 64):
+// two kernels instead of four.
+//
+// "The Throughput Lever: Quantifying the MoE GEMM and Mapping the Road to
+// B300", section "The B300 Analysis: When the Bottleneck Flips": once the
+// MoE GEMM runs at HBM speed, fixed per-step overheads (launches among them)
+// dominate a decode step, and at M = 1 only ~8 of 384 experts are touched
+// (section "The Result: Two Regimes"). On gfx950 every kernel boundary costs
+// a few microseconds of dispatch and cache maintenance, so for M <= 4:
+//
+//   fc1_decode_kernel  each workgroup first routes the whole batch itself
+//                      (one wave per token, top-k kept in LDS), derives the
+//                      distinct experts in ascending order and the rows of
+//                      the block it owns, then runs the FC1 tile body of the
+//                      grouped GEMM; workgroup 0 also writes the routing and
+//                      grouping outputs in the same format moe_route_align
+//                      produces.
+//   fc2_decode_kernel  output-stationary FC2: one workgroup per (token,
+//                      16-column tile of the output), one wave per routing
+//                      slot j streaming the W2 tile of expert ids[t, j]; the k
+//                      slot results meet in LDS and are summed in slot order
+//                      with their routing weights, then rounded once to bf16.
+//                      No atomics, no accumulator to clear, no finalize
+//                      kernel, and the float result is deterministic.
+// Each expert is read once per token that routes to it; with M <= 4 tokens
+// and top-8 of 384 experts, repeats are rare, so the weight traffic stays the
+// touched experts' bytes.
+#include "internal.h"
+#include "device_common.h"
+#include "fc_common.h"
+#include "route_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kDecKSplit = 4;   // FC1 waves per workgroup (split K)
+constexpr int kDecP1 = 3;       // FC1 chunks in flight per wave
+
+struct SmallRoute {
+  int32_t ids[kDecodeMaxAssign];
+  float w[kDecodeMaxAssign];
+  int32_t list[kDecodeMaxAssign];                    // distinct experts, ascending
+  int32_t cnt[kDecodeMaxAssign];                     // assignments per distinct expert
+  int32_t rowf[kDecodeMaxAssign][kDecodeMaxTokens];  // their f, ascending
+};
+
+template <int VPL, int NCH>
+__global__ __launch_bounds__(64 * kDecKSplit) __attribute__((amdgpu_waves_per_eu(4)))
+void fc1_decode_kernel(DecodeArgs d) {
+  __shared__ SmallRoute sh;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int M = d.fc.M, E = d.fc.E, k = d.fc.k;
+  const int MK = M * k;
+  const int npairs = d.fc.I / 16;
+  const int blk = blockIdx.x / npairs;
+  const int pair = blockIdx.x % npairs;
+
+  if (wave < M) topk_token<VPL>(d.logits, wave, E, k, sh.ids, sh.w);
+  __syncthreads();
+
+  // Distinct experts in ascending order and each assignment's rank among the
+  // assignments of its expert (f ascending), from lane f's expert id.
+  const int e = (lane < MK) ? sh.ids[lane] : -1;
+  int before = 0, tot = 0;
+  for (int j = 0; j < MK; ++j) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    tot += (ej == e) ? 1 : 0;
+    before += (j < lane && ej == e) ? 1 : 0;
+  }
+  const bool first = e >= 0 && before == 0;
+  int rank = 0;  // distinct experts smaller than e
+  for (int j = 0; j < MK; ++j) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    const int bj = __builtin_amdgcn_readlane(before, j);
+    rank += (bj == 0 && ej < e) ? 1 : 0;
+  }
+  const int nd = __builtin_popcountll(__ballot(first));
+
+  if (blockIdx.x == 0) {  // routing + grouping outputs, block_m-padded like moe_route_align
+    const int B = d.block_m;
+    if (wave == 0 && e >= 0) {
+      sh.rowf[rank][before] = lane;
+      if (first) {
+        sh.list[rank] = e;
+        sh.cnt[rank] = tot;
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < MK; i += blockDim.x) {
+      d.topk_ids[i] = sh.ids[i];
+      d.topk_weights[i] = sh.w[i];
+    }
+    for (int x = threadIdx.x; x <= E; x += blockDim.x) {
+      int below = 0;
+      for (int q = 0; q < nd; ++q) below += (sh.list[q] < x) ? 1 : 0;
+      d.expert_offsets[x] = B * below;  // every touched expert holds <= M <= B rows: one block
+    }
+    if (threadIdx.x == 0) *d.npp_out = B * nd;
+    for (int pos = threadIdx.x; pos < nd * B; pos += blockDim.x) {
+      const int q = pos / B, r = pos % B;
+      d.sorted_ids[pos] = (r < sh.cnt[q]) ? sh.rowf[q][r] : MK;
+    }
+    for (int q = threadIdx.x; q < nd; q += blockDim.x) d.block_expert[q] = sh.list[q];
+  }
+
+  if (blk >= nd) return;
+  // expert of this block, and this lane's row (lane % 16) of it
+  const unsigned long long mb = __ballot(first && rank == blk);
+  const int eb = __builtin_amdgcn_readlane(e, __builtin_ctzll(mb));
+  int frow[1] = {MK};
+  for (int r = 0; r < M; ++r) {
+    const unsigned long long m = __ballot(e == eb && before == r);
+    if ((lane & 15) == r && m) frow[0] = __builtin_ctzll(m);
+  }
+  fc_block<1, kDecKSplit, kDecP1, NCH, true>(d.fc, eb, pair, frow, wave, lane);
+}
+
+// One 16-row tile of a pair, for one activation row: per group, one MFMA for
+// -136*sum(x), one for the tile, scaled into the sum.
+__device__ __forceinline__ void mma_chunk_tile(uint4 q, uint2 sc, const uint4 (&xa)[4], const bf16x8_t neg136,
+                                               f32x4_t& acc) {
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+  const uint32_t sw[2] = {sc.x, sc.y};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x8_t b = dequant_u4_plus128(qq[j]);
+    const float g = f16_bits_to_f32((sw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+    const bf16x8_t xv = as_bf16x8(xa[j]);
+    const f32x4_t off = mfma16x16x32(xv, neg136, zero4);
+    const f32x4_t t = mfma16x16x32(xv, b, off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(t[i], g, acc[i]);
+  }
+}
+
+// ROWV: 16-byte vectors of the activation row each lane stages, when the
+// launcher knows it (I = 64 * 8 * ROWV); 0 = any I (staged by a loop).
+template <int ROWV, int KW>  // KW: waves per workgroup the launch bounds allow (>= top_k)
+__global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(4)))
+void fc2_decode_kernel(DecodeArgs d) {
+  // Each wave's activation row (I bf16) is staged in LDS once; per chunk the
+  // A operand comes from LDS, so registers hold only the weight stream.
+  extern __shared__ uint4 xrows[];  // [k][I / 8]
+  __shared__ float part[KW][16];
+  const int lane = threadIdx.x & 63;
+  const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // routing slot
+  const FcArgs& a = d.fc;
+  const int H = a.H, I = a.I, k = a.k;
+  const int ntiles = H / 16;
+  const int t = blockIdx.x / ntiles;
+  const int tile = blockIdx.x % ntiles;
+  const int pair = tile >> 1, h = tile & 1;
+  const int f = t * k + j;
+  const int ef = __builtin_amdgcn_readfirstlane(d.topk_ids[f]);
+  const bool ok = ef >= 0 && ef < a.E;  // always, for ids from the routing kernels
+  const int e = ok ? ef : 0;
+  const float wf = ok ? d.topk_weights[f] : 0.f;
+
+  const int n = I / kChunkK;
+  const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(H, I) +
+                         (int64_t)pair * n * kPairChunkBytes + h * kTileBytes;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)n * kPairChunkBytes);
+  const uint32_t oq = 16u * lane, os = kTileNibbleBytes + 8u * (lane & 15);
+  const int row16 = I / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(a.act_in) + (int64_t)f * row16;
+  uint4* dst = xrows + j * row16;
+
+  constexpr int P2 = KW > 8 ? 4 : 6;
+  uint4 qb[P2];
+  uint2 sb[P2];
+  auto load = [&](int slot, int c) {
+    const uint32_t base = (uint32_t)c * kPairChunkBytes;  // past the K range: zeros
+    qb[slot] = bload16(wr, base + oq);
+    sb[slot] = bload8(wr, base + os);
+  };
+  // Issue order: the activation row, then the first P2 weight chunks, so that
+  // staging the row waits only for its own loads.
+  if constexpr (ROWV > 0) {
+    uint4 xs[ROWV];
+#pragma unroll
+    for (int r = 0; r < ROWV; ++r) xs[r] = ok ? src[lane + 64 * r] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < P2; ++s) load(s, s);
+#pragma unroll
+    for (int r = 0; r < ROWV; ++r) dst[lane + 64 * r] = xs[r];
+  } else {
+    for (int i = lane; i < row16; i += 64) dst[i] = ok ? src[i] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < P2; ++s) load(s, s);
+  }
+  __syncthreads();
+  // lane l reads K values 8*(l/16).. of each group; every A row is the token's
+  // row (rows 1..15 of D are not used), so no lane needs a zero fill
+  const uint4* xl = dst + (lane >> 4);
+
+  const bf16x8_t neg136 = as_bf16x8(make_uint4(kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair));
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // A loop, not straight-line code: unrolled, the scheduler hoists every
+  // chunk's LDS reads and spills; looped, the memory waits stay exact because
+  // the only loads in flight are the weight ring's.
+  for (int c = 0; c < n; c += P2) {
+#pragma unroll
+    for (int s = 0; s < P2; ++s) {
+      if (c + s < n) {
+        uint4 xa[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) xa[g] = xl[(c + s) * (kChunkK / 8) + 4 * g];
+        mma_chunk_tile(qb[s], sb[s], xa, neg136, acc);
+      }
+      load(s, c + s + P2);
+    }
+  }
+  // D row 0 (the token) sits in lanes 0..15, element 0
+  if (lane < 16) part[j][lane] = wf * acc[0];
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float s = 0.f;
+    for (int q = 0; q < k; ++q) s += part[q][threadIdx.x];
+    a.out[(int64_t)t * H + 32 * pair + 16 * h + threadIdx.x] = (uint16_t)f32_to_bf16_bits(s);
+  }
+}
+
+template <int VPL>
+hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t between_stages) {
+  const int M = d.fc.M, E = d.fc.E, k = d.fc.k;
+  const int nblk = M * k < E ? M * k : E;
+  const unsigned grid1 = (unsigned)(nblk * (d.fc.I / 16));
+  if (d.fc.H == 56 * kChunkK && 56 % kDecKSplit == 0)
+    fc1_decode_kernel<VPL, 56 / kDecKSplit><<<grid1, 64 * kDecKSplit, 0, stream>>>(d);
+  else
+    fc1_decode_kernel<VPL, 0><<<grid1, 64 * kDecKSplit, 0, stream>>>(d);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (between_stages && (err = hipEventRecord(between_stages, stream)) != hipSuccess) return err;
+  DecodeArgs d2 = d;
+  d2.fc.act_in = d.fc.act_out;
+  d2.fc.wpacked = d.w2;
+  const unsigned grid2 = (unsigned)(M * (d.fc.H / 16));
+  const bool i2048 = d.fc.I == 2048;  // the 384-expert layer: 4 row vectors per lane
+  const size_t lds = (size_t)k * d.fc.I * 2;  // the k activation rows
+  if (k <= 8) {
+    if (i2048) fc2_decode_kernel<4, 8><<<grid2, 64 * k, lds, stream>>>(d2);
+    else fc2_decode_kernel<0, 8><<<grid2, 64 * k, lds, stream>>>(d2);
+  } else {
+    fc2_decode_kernel<0, kMaxTopK><<<grid2, 64 * k, lds, stream>>>(d2);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t between_stages) {
+  const int E = d.fc.E;
+  if (E <= 64) return launch_decode_vpl<1>(d, stream, between_stages);
+  if (E <= 128) return launch_decode_vpl<2>(d, stream, between_stages);
+  if (E <= 256) return launch_decode_vpl<4>(d, stream, between_stages);
+  if (E <= 512) return launch_decode_vpl<8>(d, stream, between_stages);
+  return launch_decode_vpl<16>(d, stream, between_stages);
+}
+
+}  // namespace moe

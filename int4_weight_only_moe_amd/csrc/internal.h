@@ -70,4 +70,23 @@ struct FcArgs {
 hipError_t launch_fc1(const FcArgs& a, hipStream_t stream);
 hipError_t launch_fc2(const FcArgs& a, hipStream_t stream);
 
+// Decode path (tiny batches): routing fused into FC1, output-stationary FC2.
+constexpr int kMaxTopK = 16;
+constexpr int kDecodeMaxTokens = 4;
+constexpr int kDecodeMaxAssign = 64;  // M * k
+struct DecodeArgs {
+  FcArgs fc;               // FC1 view: act_in = x, wpacked = W13, act_out = act, out = output
+  const float* logits;     // [M, E]
+  const uint8_t* w2;       // repacked W2
+  int32_t* topk_ids;       // [M*k]
+  float* topk_weights;     // [M*k]
+  int32_t* sorted_ids;     // [cap], block_m-padded as by moe_route_align
+  int32_t* block_expert;   // [cap / block_m]
+  int32_t* expert_offsets; // [E + 1]
+  int32_t* npp_out;        // [1]
+  int block_m;
+};
+// between_stages (may be null) is recorded on the stream after the FC1 stage.
+hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t between_stages);
+
 }  // namespace moe

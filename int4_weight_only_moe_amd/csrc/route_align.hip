@@ -15,6 +15,7 @@
 //                         workgroups, then a one-workgroup grouping kernel.
 #include "internal.h"
 #include "device_common.h"
+#include "route_common.h"
 
 namespace moe {
 namespace {
@@ -24,119 +25,6 @@ constexpr int kAlignWaves = kAlignThreads / 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kFusedMaxTokens = 16;
 constexpr int kTopkWavesPerBlock = 4;
-
-// Order-preserving map of a finite fp32 value to uint32 (larger value ->
-// larger key); -0.0 is first turned into +0.0 so that the two tie. Key 0 is
-// never produced for finite inputs and marks "absent / already taken".
-__device__ __forceinline__ uint32_t order_key(float v) {
-  uint32_t u = __float_as_uint(v + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t key) {
-  uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
-  return __uint_as_float(u);
-}
-
-// Cross-lane exchanges without LDS: DPP inside rows of 16 lanes, then the
-// gfx950 row swaps (permlane16/32_swap) across rows. After each step every
-// lane holds the combination of itself and its partner, so after all six
-// every lane holds the value of the whole wave.
-template <int kCtrl>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return __builtin_amdgcn_update_dpp(0u, v, kCtrl, 0xf, 0xf, false);
-}
-constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
-
-// (hi, lo) lexicographic max
-__device__ __forceinline__ void max_pair(uint32_t& hi, uint32_t& lo, uint32_t ohi, uint32_t olo) {
-  const bool take = (ohi > hi) || (ohi == hi && olo > lo);
-  hi = take ? ohi : hi;
-  lo = take ? olo : lo;
-}
-
-__device__ __forceinline__ void wave_max_pair(uint32_t& hi, uint32_t& lo) {
-  max_pair(hi, lo, dpp<kQuadSwap1>(hi), dpp<kQuadSwap1>(lo));
-  max_pair(hi, lo, dpp<kQuadSwap2>(hi), dpp<kQuadSwap2>(lo));
-  max_pair(hi, lo, dpp<kRowHalfMirror>(hi), dpp<kRowHalfMirror>(lo));
-  max_pair(hi, lo, dpp<kRowMirror>(hi), dpp<kRowMirror>(lo));
-  {  // rows 0<->1, 2<->3: one of the two results is this lane's own value
-    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    hi = h[0]; lo = l[0];
-    max_pair(hi, lo, h[1], l[1]);
-  }
-  {  // halves 0-31 <-> 32-63
-    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    hi = h[0]; lo = l[0];
-    max_pair(hi, lo, h[1], l[1]);
-  }
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-  v += __uint_as_float(dpp<kQuadSwap1>(__float_as_uint(v)));
-  v += __uint_as_float(dpp<kQuadSwap2>(__float_as_uint(v)));
-  v += __uint_as_float(dpp<kRowHalfMirror>(__float_as_uint(v)));
-  v += __uint_as_float(dpp<kRowMirror>(__float_as_uint(v)));
-  {
-    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-  }
-  {
-    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-  }
-  return v;
-}
-
-// One wave routes token t. Lane l holds logits l, l+64, ... (VPL of them).
-// Candidates compare as (key << 32) | ~e, so equal logits prefer the lower e.
-template <int VPL>
-__device__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
-                           int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-                           int32_t* ids_copy = nullptr) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[VPL];
-  const float* row = logits + (int64_t)t * E;
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    int e = v * 64 + lane;
-    key[v] = (e < E) ? order_key(row[e]) : 0u;
-  }
-  uint32_t my_key = 0;
-  int my_e = 0;
-  for (int r = 0; r < k; ++r) {
-    // this lane's best candidate: largest key, then smallest expert (~e larger)
-    uint32_t bhi = 0, blo = 0;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const uint32_t ne = ~(uint32_t)(v * 64 + lane);
-      const bool take = key[v] != 0u && (key[v] > bhi || (key[v] == bhi && ne > blo));
-      bhi = take ? key[v] : bhi;
-      blo = take ? ne : blo;
-    }
-    wave_max_pair(bhi, blo);
-    const uint32_t win_e = ~blo;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if ((uint32_t)(v * 64 + lane) == win_e) key[v] = 0u;
-    if (lane == r) {
-      my_key = bhi;
-      my_e = (int)win_e;
-    }
-  }
-  const float l0 = key_value(__builtin_amdgcn_readfirstlane(my_key));
-  const float ex = (lane < k) ? expf(key_value(my_key) - l0) : 0.0f;
-  const float sum = wave_sum(ex);
-  if (lane < k) {
-    topk_ids[(int64_t)t * k + lane] = my_e;
-    topk_w[(int64_t)t * k + lane] = ex / sum;
-    if (ids_copy) ids_copy[t * k + lane] = my_e;
-  }
-}
 
 template <int VPL>
 __global__ __launch_bounds__(64 * kTopkWavesPerBlock) void topk_kernel(

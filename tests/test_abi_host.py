@@ -144,3 +144,22 @@ def test_fc_stage_validation():
     p = FAKE
     assert lib.moe_w4a16_fc1(p, 4, 384, 7168, 2048, 8, 16, p, p, p, cap, p, p, ws - 16, None) == moe.MOE_ERR_WORKSPACE
     assert lib.moe_w4a16_fc2(4, 384, 7168, 2048, 8, 16, p, p, p, p, cap, p, p, ws, None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_layer_validation():
+    lib = moe.lib()
+    p = FAKE
+    cap = moe.moe_route_align_capacity(4, 384, 8, 16)
+    ws = moe.moe_w4a16_workspace_bytes(4, 384, 7168, 2048, 8)
+
+    def call(M=4, E=384, H=7168, I=2048, k=8, B=16, cap=cap, ws=ws, logits=p, x=p, ev=None):
+        return lib.moe_w4a16_layer(logits, x, M, E, H, I, k, B, p, p, p, p, p, p, cap, p, p, p, ws, p, None, ev)
+
+    assert lib.moe_w4a16_layer(None, None, 0, 384, 7168, 2048, 8, 16, None, None, None, None, None, None, 0,
+                               None, None, None, 0, None, None, None) == moe.MOE_OK
+    assert call(H=7000) == moe.MOE_ERR_UNSUPPORTED
+    assert call(cap=cap - 16) == moe.MOE_ERR_CAPACITY
+    assert call(ws=ws - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(logits=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(x=p + 2) == moe.MOE_ERR_INVALID_ARG
+    assert call(E=1025) == moe.MOE_ERR_UNSUPPORTED

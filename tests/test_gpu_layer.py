@@ -1,0 +1,106 @@
+"""moe_w4a16_layer: the one-call layer. For M <= 4 it runs the two-kernel
+decode path (routing inside FC1, output-stationary FC2); above, the four-kernel
+path. Integers must equal moe_route_align's, the output must meet the oracle
+bar, and the decode path's output must be identical on every call."""
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_moe_amd as moe
+import oracle
+import workloads as wl
+from gpu_common import (assert_output_close, assert_route_matches, device_layer, k26_layer, oracle_experts,
+                        route_host, to_dev, x_device)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "tiny": (wl.TINY, 0),
+    "mid": (wl.LayerShape(E=64, H=1024, I=384, k=6), 3),
+    "k16": (wl.LayerShape(E=32, H=256, I=128, k=16), 4),   # M*k up to 64
+    "k1": (wl.LayerShape(E=32, H=384, I=640, k=1), 5),
+}
+
+
+def run_layer_call(layer, logits, x_bits, block_m, reps=1):
+    s = layer.shape
+    M = logits.shape[0]
+    rb = moe.alloc_route_buffers(M, s.E, s.k, block_m)
+    lg, x = to_dev(logits), x_device(x_bits)
+    outs = []
+    for _ in range(reps):
+        outs.append(moe.layer(lg, x, rb, s.I, layer.w13, layer.w2).float().cpu().numpy())
+    torch.cuda.synchronize()
+    return rb, outs
+
+
+@pytest.mark.parametrize("shape_name", list(SHAPES))
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9])
+@pytest.mark.parametrize("block_m", [16, 64])
+def test_layer_matches_oracle(shape_name, M, block_m):
+    shape, seed = SHAPES[shape_name]
+    if M * shape.k > 64 and M <= 4:
+        pytest.skip("not a decode-path size")
+    print(f"layer {shape_name} M={M} block_m={block_m}", flush=True)
+    layer = device_layer(shape, seed)
+    t = wl.tokens(shape, M, 1000 + M)
+    rb, outs = run_layer_call(layer, t.logits, t.x_bits, block_m, reps=3)
+    ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, block_m)
+    ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,
+                             oracle_experts(shape, seed))
+    assert_output_close(outs[0], ref, f"{shape_name} M={M}")
+    if M <= 4:
+        for o in outs[1:]:
+            assert np.array_equal(o, outs[0]), "decode path must be deterministic"
+
+
+def test_layer_k26_decode_sizes():
+    layer = k26_layer()
+    s = layer.shape
+    for M in (1, 2, 4):
+        t = wl.tokens(s, M, 4242 + M)
+        rb, outs = run_layer_call(layer, t.logits, t.x_bits, 16, reps=2)
+        ids, w = assert_route_matches(route_host(rb), t.logits, s.E, s.k, 16)
+        assert np.array_equal(outs[0], outs[1])
+        rows = [0, M - 1]
+        ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,
+                                 oracle_experts(s, 2026, keep=0), tokens_subset=rows)
+        rel, mx = assert_output_close(outs[0][rows], ref[rows], f"k26 M={M}")
+        print(f"layer k26 M={M}: rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
+
+
+def test_layer_k26_m1_closed_form():
+    """Constant weights (q = +1, s = 2^-7) and x = 1: exactly 50176 through the decode path."""
+    from test_gpu_forward import const_layer
+    layer = const_layer(wl.K26)
+    rng = np.random.default_rng(12)
+    logits = rng.standard_normal((1, 384)).astype(np.float32)
+    x_bits = wl.bf16_bits_from_f32(np.ones((1, 7168), np.float32))
+    _, outs = run_layer_call(layer, logits, x_bits, 16)
+    assert np.all(outs[0] == 50176.0)
+
+
+def test_layer_graph_replays():
+    shape, seed = SHAPES["mid"]
+    layer = device_layer(shape, seed)
+    M = 2
+    t = wl.tokens(shape, M, 5)
+    lg, x = to_dev(t.logits), x_device(t.x_bits)
+    rb = moe.alloc_route_buffers(M, shape.E, shape.k, 16)
+    ws = torch.empty(moe.moe_w4a16_workspace_bytes(M, shape.E, shape.H, shape.I, shape.k), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((M, shape.H), dtype=torch.bfloat16, device="cuda")
+    moe.layer(lg, x, rb, shape.I, layer.w13, layer.w2, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.layer(lg, x, rb, shape.I, layer.w13, layer.w2, workspace=ws, out=out)
+    y = torch.randn(512, 512, device="cuda")
+    for _ in range(4):
+        out.fill_(0)
+        rb.topk_ids.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        (y @ y).sum().item()
