@@ -75,6 +75,169 @@ void fc_kernel(FcArgs a) {
   fc_block<S, KSPLIT, P, NCH, kFc1>(a, e, pair, frow, wave, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Wide variant for blocks of 32 or 64 rows (batches with tens of tokens per
+// expert). Streaming each activation row once per tile pair, as fc_kernel
+// does, multiplies the activation traffic by the number of pairs (128 for
+// FC1 of the 384-expert layer); here one workgroup covers kWideNP pairs
+// (one wave each, full K) and stages the block's activation chunk in LDS once
+// for all of them. The -136*sum(x) correction of each (row, group) is summed
+// while staging and enters the MFMA as its accumulator input, so no MFMA is
+// spent on it. Workgroup ids are remapped so that each XCD (workgroups are
+// dealt to the 8 XCDs round-robin) walks a contiguous range of blocks: a
+// block's activations and an expert's weights then stay in one XCD's L2.
+//
+// Per chunk step c (one barrier per step):
+//   issue the activation loads of chunk c+P and the weight loads of c+P
+//   (both rings P deep in registers, so a wait for one never drains the other),
+//   run chunk c from LDS slot c%2, then store chunk c+1 into slot (c+1)%2.
+constexpr int kWideNP = 16;                 // waves = tile pairs per workgroup
+constexpr int kWideP = 2;                   // chunks in flight per wave (even: LDS slot parity is static)
+constexpr int kRowVecs = kChunkK / 8;       // 16-byte vectors of a row's chunk slice
+constexpr int kRowPad = kRowVecs + 1;       // +16 B per row: conflict-free A reads
+
+__device__ __forceinline__ int xcd_remap(int p, int G) {
+  const int g8 = G / 8, rem = G % 8, x = p % 8, i = p / 8;
+  return x * g8 + (x < rem ? x : rem) + i;
+}
+
+template <int S, bool kFc1>
+__global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
+  constexpr int BM = 16 * S;
+  constexpr int kThreads = 64 * kWideNP;
+  constexpr int kItems = BM * kRowVecs;  // multiple of 64: whole waves stage or idle
+  constexpr int P = kWideP;
+  __shared__ uint4 xt[2][BM][kRowPad];
+  __shared__ f32x4_t xs4[2][4][BM / 4];  // -136 * group sums: [slot][group][4-row quad]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = kFc1 ? a.H : a.I;
+  const int N = kFc1 ? 2 * a.I : a.H;
+  const int npairs = N / kPairRows;
+  const int MK = a.M * a.k;
+
+  if constexpr (kFc1) {  // clear FC2's accumulator
+    uint4* z = reinterpret_cast<uint4*>(a.acc);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < a.zero_words16; i += stride)
+      z[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int npg = npairs / kWideNP;
+  const int blk = L / npg;
+  const int pair = (L % npg) * kWideNP + wave;
+  const int32_t* rows = a.sorted_ids + (int64_t)blk * BM;
+  int frow[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) frow[s] = rows[16 * s + (lane & 15)];
+  const bool stager = tid < kItems;
+  const int srow = tid / kRowVecs, svec = tid % kRowVecs;
+  const int sf = stager ? rows[srow] : MK;
+  const int npp = __builtin_amdgcn_readfirstlane(*a.npp);
+  const int e = __builtin_amdgcn_readfirstlane(a.block_expert[blk]);
+  if (blk * BM >= npp) return;
+  if (e < 0 || e >= a.E) return;
+
+  bool sact[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) sact[s] = __builtin_amdgcn_readfirstlane(frow[s]) < MK;
+
+  const int n = K / kChunkK;
+  const int rows_total = kFc1 ? a.M : MK;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.act_in, (uint32_t)rows_total * (uint32_t)K * 2u);
+  const bool svalid = stager && sf >= 0 && sf < MK;
+  const uint32_t soff = svalid ? ((uint32_t)(kFc1 ? sf / a.k : sf) * (uint32_t)K + 8u * svec) * 2u : kOutOfRange;
+
+  const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(N, K) + (int64_t)pair * n * kPairChunkBytes;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)n * kPairChunkBytes);
+  const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
+  const uint32_t os0 = kTileNibbleBytes + 8u * (lane & 15), os1 = kTileBytes + kTileNibbleBytes + 8u * (lane & 15);
+  auto load_w = [&](int c) {
+    const uint32_t base = (uint32_t)c * kPairChunkBytes;  // past the K range: zeros
+    WChunk w;
+    w.q0 = bload16(wr, base + oq0);
+    w.q1 = bload16(wr, base + oq1);
+    w.s0 = bload8(wr, base + os0);
+    w.s1 = bload8(wr, base + os1);
+    return w;
+  };
+  auto load_x = [&](int c) { return bload16(xr, (c < n) ? soff + (uint32_t)c * (kChunkK * 2) : kOutOfRange); };
+  // store one staged vector and its share of the group sum (4 vectors = 1 group)
+  auto store_x = [&](uint4 v, int slot) {
+    if (!stager) return;
+    xt[slot][srow][svec] = v;
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sum += __uint_as_float(w4[i] << 16) + __uint_as_float(w4[i] & 0xFFFF0000u);
+    sum += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(sum), 0xB1, 0xf, 0xf, false));
+    sum += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(sum), 0x4E, 0xf, 0xf, false));
+    if ((svec & 3) == 0) reinterpret_cast<float*>(&xs4[slot][svec >> 2][0])[srow] = -136.0f * sum;
+  };
+
+  f32x4_t acc0[S], acc1[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    acc0[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc1[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  WChunk wb[P];
+  uint4 xg[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    xg[j] = load_x(j);
+    wb[j] = load_w(j);
+  }
+  store_x(xg[0], 0);
+  __syncthreads();
+
+  const int mrow = lane & 15, kv = lane >> 4;
+  for (int c = 0; c < n; c += P) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int cc = c + j;
+      if (cc < n) {
+        const int slot = j & 1;  // == cc & 1 since c is a multiple of the even P
+        xg[j] = load_x(cc + P);
+        const WChunk w = wb[j];
+        const uint32_t q0[4] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w};
+        const uint32_t q1[4] = {w.q1.x, w.q1.y, w.q1.z, w.q1.w};
+        const uint32_t s0w[2] = {w.s0.x, w.s0.y};
+        const uint32_t s1w[2] = {w.s1.x, w.s1.y};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const bf16x8_t b0 = dequant_u4_plus128(q0[g]);
+          const bf16x8_t b1 = dequant_u4_plus128(q1[g]);
+          const float g0 = f16_bits_to_f32((s0w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
+          const float g1 = f16_bits_to_f32((s1w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            if (s > 0 && !sact[s]) continue;
+            const bf16x8_t xv = as_bf16x8(xt[slot][16 * s + mrow][4 * g + kv]);
+            const f32x4_t off = xs4[slot][g][4 * s + kv];
+            const f32x4_t t0 = mfma16x16x32(xv, b0, off);
+            const f32x4_t t1 = mfma16x16x32(xv, b1, off);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc0[s][i] = __builtin_fmaf(t0[i], g0, acc0[s][i]);
+              acc1[s][i] = __builtin_fmaf(t1[i], g1, acc1[s][i]);
+            }
+          }
+          // keep the LDS reads of later groups from being hoisted (register pressure)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        wb[j] = load_w(cc + P);
+        if (cc + 1 < n) store_x(xg[(j + 1) % P], (j + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+  fc_epilogue<S, kFc1>(a, pair, frow, sact, acc0, acc1, lane);
+}
+
 // out = bf16(acc), 8 values per thread.
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ acc, uint16_t* __restrict__ out,
                                                        int64_t n8) {
@@ -113,10 +276,18 @@ hipError_t launch_fc(const FcArgs& a, hipStream_t stream) {
   const int64_t nblk = a.cap / a.block_m;
   const int64_t grid = nblk * (N / kPairRows);
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const bool wide = (N / kPairRows) % kWideNP == 0;  // pairs split evenly over the wide workgroups
+  const unsigned wgrid = (unsigned)(nblk * (N / kPairRows / kWideNP));
   switch (a.block_m) {
     case 16: launch<1, 4, 3, kFc1>(a, (unsigned)grid, stream); break;
-    case 32: launch<2, 4, 2, kFc1>(a, (unsigned)grid, stream); break;
-    case 64: launch<4, 4, 2, kFc1>(a, (unsigned)grid, stream); break;
+    case 32:
+      if (wide) fc_wide_kernel<2, kFc1><<<wgrid, 64 * kWideNP, 0, stream>>>(a);
+      else launch<2, 4, 2, kFc1>(a, (unsigned)grid, stream);
+      break;
+    case 64:
+      if (wide) fc_wide_kernel<4, kFc1><<<wgrid, 64 * kWideNP, 0, stream>>>(a);
+      else launch<4, 4, 2, kFc1>(a, (unsigned)grid, stream);
+      break;
     default: return hipErrorInvalidValue;
   }
   hipError_t err = hipGetLastError();

@@ -65,6 +65,50 @@ __device__ __forceinline__ void mma_chunk(const WChunk& w, const uint4 (&xa)[S][
   }
 }
 
+// Epilogue of a workgroup's tile pair for the rows frow of its block:
+// FC1 stores act_f = bf16(SiLU(gate) * up); FC2 adds w_f * y_f into the fp32
+// accumulator with atomics. Lane l holds D rows 4*(l/16)+i, column l % 16.
+template <int S, bool kFc1>
+__device__ __forceinline__ void fc_epilogue(const FcArgs& a, const int pair, const int (&frow)[S],
+                                            const bool (&sact)[S], const f32x4_t (&acc0)[S],
+                                            const f32x4_t (&acc1)[S], const int lane) {
+  const int MK = a.M * a.k;
+  const int col = lane & 15;
+  if constexpr (kFc1) {
+    const int I = a.I;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (!sact[s]) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = __shfl(frow[s], 4 * (lane >> 4) + i, 64);
+        if (f < 0 || f >= MK) continue;
+        const float g = acc0[s][i], u = acc1[s][i];
+        const float v = g / (1.0f + __expf(-g)) * u;
+        a.act_out[(int64_t)f * I + 16 * pair + col] = (uint16_t)f32_to_bf16_bits(v);
+      }
+    }
+  } else {
+    const int H = a.H;
+    const int c0 = kPairRows * pair;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (!sact[s]) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = __shfl(frow[s], 4 * (lane >> 4) + i, 64);
+        if (f < 0 || f >= MK) continue;
+        const int t = f / a.k;
+        const float w = a.topk_weights[f];
+        float* dst = a.acc + (int64_t)t * H + c0;
+        unsafeAtomicAdd(dst + col, w * acc0[s][i]);
+        unsafeAtomicAdd(dst + 16 + col, w * acc1[s][i]);
+      }
+    }
+  }
+}
+
+
 // The work of one workgroup: block rows frow (per sub-tile, this lane's row
 // lane % 16; entries outside [0, M*k) are padding) of expert e times tile
 // pair `pair`, K split over the KSPLIT waves, then the FC1 or FC2 epilogue.
@@ -181,39 +225,7 @@ __device__ __forceinline__ void fc_block(const FcArgs& a, const int e, const int
     }
   }
 
-  const int col = lane & 15;
-  if constexpr (kFc1) {
-    const int I = a.I;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (!sact[s]) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = __shfl(frow[s], 4 * (lane >> 4) + i, 64);
-        if (f < 0 || f >= MK) continue;
-        const float g = acc0[s][i], u = acc1[s][i];
-        const float v = g / (1.0f + __expf(-g)) * u;
-        a.act_out[(int64_t)f * I + 16 * pair + col] = (uint16_t)f32_to_bf16_bits(v);
-      }
-    }
-  } else {
-    const int H = a.H;
-    const int c0 = kPairRows * pair;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (!sact[s]) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = __shfl(frow[s], 4 * (lane >> 4) + i, 64);
-        if (f < 0 || f >= MK) continue;
-        const int t = f / a.k;
-        const float w = a.topk_weights[f];
-        float* dst = a.acc + (int64_t)t * H + c0;
-        unsafeAtomicAdd(dst + col, w * acc0[s][i]);
-        unsafeAtomicAdd(dst + 16 + col, w * acc1[s][i]);
-      }
-    }
-  }
+  fc_epilogue<S, kFc1>(a, pair, frow, sact, acc0, acc1, lane);
 }
 
 
