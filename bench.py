@@ -55,12 +55,19 @@ def parse():
     p.add_argument("--sweep-steps", type=int, default=30)
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run one plain 1 GiB device-to-device copy (to scale HBM counters)")
     return p.parse_args()
 
 
-def fc_source_sha() -> str:
-    with open(os.path.join(ROOT, "int4_weight_only_moe_amd", "csrc", "fc.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_sha() -> str:
+    """Hash of every kernel source: counters taken on other sources do not apply."""
+    d = os.path.join(ROOT, "int4_weight_only_moe_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def layer_bytes(D, M, s):
@@ -74,6 +81,12 @@ def fc1_bytes(D, M, s):
     """Algorithmic bytes of one FC1 launch: touched experts' W13 nibbles + scales,
     the x rows, and the bf16 activations it writes."""
     return D * (2 * s.I * s.H * 9 // 16) + 2 * M * s.H + 2 * M * s.k * s.I
+
+
+def fc2_bytes(D, M, s):
+    """Algorithmic bytes of one FC2 stage: touched experts' W2 nibbles + scales, the
+    bf16 activations it reads and the bf16 output."""
+    return D * (s.H * s.I * 9 // 16) + 2 * M * s.k * s.I + 2 * M * s.H
 
 
 def flops(M, s):
@@ -284,7 +297,7 @@ def traffic_for(launch_bytes_alg):
         return None
     with open(TRAFFIC_FILE) as f:
         d = json.load(f)
-    if d.get("fc_source_sha") != fc_source_sha():
+    if d.get("kernel_source_sha") != kernel_source_sha():
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -298,6 +311,13 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     b = Bench(a.replicas)
+    if a.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     head, c = b.record(a.workload, a.steps, a.warmup, a.replicas)
     s, D, M = b.s, c["D"], c["w"].M
     fc1_alg = fc1_bytes(D, M, s)
