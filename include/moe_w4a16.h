@@ -209,9 +209,9 @@ int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int
  * is output-stationary (each output tile sums its token's top_k expert
  * results in slot order in one workgroup: no atomics, and the bf16 output is
  * then identical on every call). Larger batches take the four-kernel path.
- *   stage_events  NULL, or two hipEvent_t: [0] is recorded on the stream just
- *                 before the FC1 stage (for M <= 4 the routing is part of it),
- *                 [1] just after it; for timing the stages.
+ *   stage_events  NULL, or two hipEvent_t that receive the start and end
+ *                 timestamps of the FC1-stage kernel itself (for M <= 4 the
+ *                 routing is part of it), for timing that stage.
  */
 int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
                     int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights,

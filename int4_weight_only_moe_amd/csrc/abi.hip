@@ -256,17 +256,19 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
     d.expert_offsets = expert_offsets;
     d.npp_out = num_tokens_post_pad;
     d.block_m = block_m;
-    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return MOE_ERR_HIP;
-    return hip_status(moe::launch_decode(d, s, ev1));
+    return hip_status(moe::launch_decode(d, s, ev0, ev1));
   }
   st = moe_route_align(logits, M, E, top_k, block_m, topk_ids, topk_weights, sorted_token_ids, block_expert_ids,
                        expert_offsets, num_tokens_post_pad, cap, stream);
   if (st != MOE_OK) return st;
-  if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return MOE_ERR_HIP;
-  st = moe_w4a16_fc1(x_bf16, M, E, H, I, top_k, block_m, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
-                     cap, w13_packed, workspace, workspace_bytes, stream);
+  {
+    moe::FcArgs a = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
+                            num_tokens_post_pad, workspace);
+    a.act_in = x_bf16;
+    a.wpacked = (const uint8_t*)w13_packed;
+    st = hip_status(moe::launch_fc1(a, s, ev0, ev1));
+  }
   if (st != MOE_OK) return st;
-  if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return MOE_ERR_HIP;
   return moe_w4a16_fc2(M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
                        num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
 }

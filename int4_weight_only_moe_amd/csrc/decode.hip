@@ -9,12 +9,12 @@
 // a few microseconds of dispatch and cache maintenance, so for M <= 4:
 //
 //   fc1_decode_kernel  each workgroup first routes the whole batch itself
-//                      (one wave per token, top-k kept in LDS), derives the
-//                      distinct experts in ascending order and the rows of
-//                      the block it owns, then runs the FC1 tile body of the
-//                      grouped GEMM; workgroup 0 also writes the routing and
-//                      grouping outputs in the same format moe_route_align
-//                      produces.
+//                      (one wave per token, top-k kept in LDS), takes the
+//                      distinct experts in order of first occurrence and the
+//                      rows of the block it owns, then runs the FC1 tile body
+//                      of the grouped GEMM; workgroup 0 also writes the
+//                      routing and grouping outputs (experts ascending) in
+//                      the format moe_route_align produces.
 //   fc2_decode_kernel  output-stationary FC2: one workgroup per (token,
 //                      16-column tile of the output), one wave per routing
 //                      slot j streaming the W2 tile of expert ids[t, j]; the k
@@ -59,25 +59,29 @@ void fc1_decode_kernel(DecodeArgs d) {
   if (wave < M) topk_token<VPL>(d.logits, wave, E, k, sh.ids, sh.w);
   __syncthreads();
 
-  // Distinct experts in ascending order and each assignment's rank among the
-  // assignments of its expert (f ascending), from lane f's expert id.
+  // Assignment f sits in lane f. `before` = earlier assignments of the same
+  // expert (its row within the expert's block), `first` = first occurrence.
+  // A token never repeats an expert, so for M = 1 every lane is a first.
   const int e = (lane < MK) ? sh.ids[lane] : -1;
-  int before = 0, tot = 0;
-  for (int j = 0; j < MK; ++j) {
-    const int ej = __builtin_amdgcn_readlane(e, j);
-    tot += (ej == e) ? 1 : 0;
-    before += (j < lane && ej == e) ? 1 : 0;
+  int before = 0, tot = 1;
+  if (M > 1) {
+    tot = 0;
+    for (int j = 0; j < MK; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      tot += (ej == e) ? 1 : 0;
+      before += (j < lane && ej == e) ? 1 : 0;
+    }
   }
   const bool first = e >= 0 && before == 0;
-  int rank = 0;  // distinct experts smaller than e
-  for (int j = 0; j < MK; ++j) {
-    const int ej = __builtin_amdgcn_readlane(e, j);
-    const int bj = __builtin_amdgcn_readlane(before, j);
-    rank += (bj == 0 && ej < e) ? 1 : 0;
-  }
-  const int nd = __builtin_popcountll(__ballot(first));
+  const unsigned long long firsts = __ballot(first);
+  const int nd = __builtin_popcountll(firsts);
 
   if (blockIdx.x == 0) {  // routing + grouping outputs, block_m-padded like moe_route_align
+    int rank = 0;         // distinct experts smaller than e: the ascending order
+    for (int j = 0; j < MK; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      rank += (((firsts >> j) & 1ull) && ej < e) ? 1 : 0;
+    }
     const int B = d.block_m;
     if (wave == 0 && e >= 0) {
       sh.rowf[rank][before] = lane;
@@ -105,8 +109,10 @@ void fc1_decode_kernel(DecodeArgs d) {
   }
 
   if (blk >= nd) return;
-  // expert of this block, and this lane's row (lane % 16) of it
-  const unsigned long long mb = __ballot(first && rank == blk);
+  // FC1 takes the distinct experts in order of first occurrence: block blk is
+  // the expert of the blk-th first occurrence; this lane's row (lane % 16) of it
+  unsigned long long mb = firsts;
+  for (int i = 0; i < blk; ++i) mb &= mb - 1;
   const int eb = __builtin_amdgcn_readlane(e, __builtin_ctzll(mb));
   int frow[1] = {MK};
   for (int r = 0; r < M; ++r) {
@@ -223,17 +229,16 @@ void fc2_decode_kernel(DecodeArgs d) {
 }
 
 template <int VPL>
-hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t between_stages) {
+hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int M = d.fc.M, E = d.fc.E, k = d.fc.k;
   const int nblk = M * k < E ? M * k : E;
   const unsigned grid1 = (unsigned)(nblk * (d.fc.I / 16));
   if (d.fc.H == 56 * kChunkK && 56 % kDecKSplit == 0)
-    fc1_decode_kernel<VPL, 56 / kDecKSplit><<<grid1, 64 * kDecKSplit, 0, stream>>>(d);
+    launch_kernel(fc1_decode_kernel<VPL, 56 / kDecKSplit>, grid1, 64 * kDecKSplit, 0, stream, e0, e1, d);
   else
-    fc1_decode_kernel<VPL, 0><<<grid1, 64 * kDecKSplit, 0, stream>>>(d);
+    launch_kernel(fc1_decode_kernel<VPL, 0>, grid1, 64 * kDecKSplit, 0, stream, e0, e1, d);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (between_stages && (err = hipEventRecord(between_stages, stream)) != hipSuccess) return err;
   DecodeArgs d2 = d;
   d2.fc.act_in = d.fc.act_out;
   d2.fc.wpacked = d.w2;
@@ -251,13 +256,14 @@ hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t between_stages) {
+hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int E = d.fc.E;
-  if (E <= 64) return launch_decode_vpl<1>(d, stream, between_stages);
-  if (E <= 128) return launch_decode_vpl<2>(d, stream, between_stages);
-  if (E <= 256) return launch_decode_vpl<4>(d, stream, between_stages);
-  if (E <= 512) return launch_decode_vpl<8>(d, stream, between_stages);
-  return launch_decode_vpl<16>(d, stream, between_stages);
+  if (E <= 64) return launch_decode_vpl<1>(d, stream, e0, e1);
+  if (E <= 128) return launch_decode_vpl<2>(d, stream, e0, e1);
+  if (E <= 256) return launch_decode_vpl<4>(d, stream, e0, e1);
+  if (E <= 384) return launch_decode_vpl<6>(d, stream, e0, e1);
+  if (E <= 512) return launch_decode_vpl<8>(d, stream, e0, e1);
+  return launch_decode_vpl<16>(d, stream, e0, e1);
 }
 
 }  // namespace moe

@@ -257,21 +257,21 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
 // layer (hidden 7168 = 56 chunks, intermediate 2048 = 16 chunks) split over
 // KSPLIT waves. Other shapes take the run-time loop.
 template <int S, int KSPLIT, int P, bool kFc1>
-void launch(const FcArgs& a, unsigned grid, hipStream_t stream) {
+void launch(const FcArgs& a, unsigned grid, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int nkc = (kFc1 ? a.H : a.I) / kChunkK;
   constexpr int kNchFc1 = 56 / KSPLIT, kNchFc2 = 16 / KSPLIT;
   constexpr int kNch = kFc1 ? kNchFc1 : kNchFc2;
   if constexpr (S == 1 && kNch >= P) {  // unrolled code only fits registers for one sub-tile
     if (nkc == kNch * KSPLIT) {
-      fc_kernel<S, KSPLIT, P, kNch, kFc1><<<grid, 64 * KSPLIT, 0, stream>>>(a);
+      launch_kernel(fc_kernel<S, KSPLIT, P, kNch, kFc1>, grid, 64 * KSPLIT, 0, stream, e0, e1, a);
       return;
     }
   }
-  fc_kernel<S, KSPLIT, P, 0, kFc1><<<grid, 64 * KSPLIT, 0, stream>>>(a);
+  launch_kernel(fc_kernel<S, KSPLIT, P, 0, kFc1>, grid, 64 * KSPLIT, 0, stream, e0, e1, a);
 }
 
 template <bool kFc1>
-hipError_t launch_fc(const FcArgs& a, hipStream_t stream) {
+hipError_t launch_fc(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int N = kFc1 ? 2 * a.I : a.H;
   const int64_t nblk = a.cap / a.block_m;
   const int64_t grid = nblk * (N / kPairRows);
@@ -279,14 +279,14 @@ hipError_t launch_fc(const FcArgs& a, hipStream_t stream) {
   const bool wide = (N / kPairRows) % kWideNP == 0;  // pairs split evenly over the wide workgroups
   const unsigned wgrid = (unsigned)(nblk * (N / kPairRows / kWideNP));
   switch (a.block_m) {
-    case 16: launch<1, 4, 3, kFc1>(a, (unsigned)grid, stream); break;
+    case 16: launch<1, 4, 3, kFc1>(a, (unsigned)grid, stream, e0, e1); break;
     case 32:
-      if (wide) fc_wide_kernel<2, kFc1><<<wgrid, 64 * kWideNP, 0, stream>>>(a);
-      else launch<2, 4, 2, kFc1>(a, (unsigned)grid, stream);
+      if (wide) launch_kernel(fc_wide_kernel<2, kFc1>, wgrid, 64 * kWideNP, 0, stream, e0, e1, a);
+      else launch<2, 4, 2, kFc1>(a, (unsigned)grid, stream, e0, e1);
       break;
     case 64:
-      if (wide) fc_wide_kernel<4, kFc1><<<wgrid, 64 * kWideNP, 0, stream>>>(a);
-      else launch<4, 4, 2, kFc1>(a, (unsigned)grid, stream);
+      if (wide) launch_kernel(fc_wide_kernel<4, kFc1>, wgrid, 64 * kWideNP, 0, stream, e0, e1, a);
+      else launch<4, 4, 2, kFc1>(a, (unsigned)grid, stream, e0, e1);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -299,7 +299,9 @@ hipError_t launch_fc(const FcArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_fc1(const FcArgs& a, hipStream_t stream) { return launch_fc<true>(a, stream); }
-hipError_t launch_fc2(const FcArgs& a, hipStream_t stream) { return launch_fc<false>(a, stream); }
+hipError_t launch_fc1(const FcArgs& a, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  return launch_fc<true>(a, stream, ev_start, ev_stop);
+}
+hipError_t launch_fc2(const FcArgs& a, hipStream_t stream) { return launch_fc<false>(a, stream, nullptr, nullptr); }
 
 }  // namespace moe

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace moe {
@@ -67,7 +68,10 @@ struct FcArgs {
   int64_t zero_words16;         // FC1: 16-byte words of acc to clear
 };
 
-hipError_t launch_fc1(const FcArgs& a, hipStream_t stream);
+// ev_start / ev_stop (may be null) take the FC1 kernel's own start and end
+// timestamps (hipExtLaunchKernel), for timing the stage without extra packets.
+hipError_t launch_fc1(const FcArgs& a, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                      hipEvent_t ev_stop = nullptr);
 hipError_t launch_fc2(const FcArgs& a, hipStream_t stream);
 
 // Decode path (tiny batches): routing fused into FC1, output-stationary FC2.
@@ -86,7 +90,17 @@ struct DecodeArgs {
   int32_t* npp_out;        // [1]
   int block_m;
 };
-// between_stages (may be null) is recorded on the stream after the FC1 stage.
-hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t between_stages);
+// ev_start / ev_stop (may be null) take the routing+FC1 kernel's own timestamps.
+hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+
+// Launch with optional kernel-timestamp events.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                          hipEvent_t ev_start, hipEvent_t ev_stop, Args... args) {
+  if (ev_start || ev_stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev_start, ev_stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
 
 }  // namespace moe

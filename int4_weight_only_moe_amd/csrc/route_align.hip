@@ -204,6 +204,8 @@ hipError_t launch_route_align(const float* logits, int M, int E, int k, int bloc
     return launch_vpl<2>(logits, M, E, k, block_m, topk_ids, topk_weights, sorted_ids, block_expert, offsets, npp, stream);
   if (E <= 256)
     return launch_vpl<4>(logits, M, E, k, block_m, topk_ids, topk_weights, sorted_ids, block_expert, offsets, npp, stream);
+  if (E <= 384)
+    return launch_vpl<6>(logits, M, E, k, block_m, topk_ids, topk_weights, sorted_ids, block_expert, offsets, npp, stream);
   if (E <= 512)
     return launch_vpl<8>(logits, M, E, k, block_m, topk_ids, topk_weights, sorted_ids, block_expert, offsets, npp, stream);
   return launch_vpl<16>(logits, M, E, k, block_m, topk_ids, topk_weights, sorted_ids, block_expert, offsets, npp, stream);

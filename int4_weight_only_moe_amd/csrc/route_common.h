@@ -78,51 +78,89 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // One wave routes token t. Lane l holds logits l, l+64, ... (VPL of them).
 // Candidates compare as (key << 32) | ~e, so equal logits prefer the lower e.
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+// Wave-wide max / min of a 32-bit value, every lane gets the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax(v, dpp<kQuadSwap1>(v));
+  v = umax(v, dpp<kQuadSwap2>(v));
+  v = umax(v, dpp<kRowHalfMirror>(v));
+  v = umax(v, dpp<kRowMirror>(v));
+  const auto h = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = umax(h[0], h[1]);
+  const auto g = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return umax(g[0], g[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = umin(v, dpp<kQuadSwap1>(v));
+  v = umin(v, dpp<kQuadSwap2>(v));
+  v = umin(v, dpp<kRowHalfMirror>(v));
+  v = umin(v, dpp<kRowMirror>(v));
+  const auto h = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = umin(h[0], h[1]);
+  const auto g = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return umin(g[0], g[1]);
+}
+
 template <int VPL>
 __device__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
                            int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
                            int32_t* ids_copy = nullptr) {
   const int lane = threadIdx.x & 63;
-  // Candidates as (key << 32 | ~e): larger means larger logit, then smaller
-  // expert; 0 means none. Each lane sorts its VPL candidates once; every
-  // round takes the wave maximum of the lane heads and the winning lane (the
-  // candidates are unique) drops its head.
-  uint64_t c[VPL];
+  // Lane l holds experts l, l+64, ...: keys (0 = none) sorted descending with
+  // their expert index, equal keys keeping ascending expert order. Each round
+  // takes the wave maximum of the lane heads (32-bit: a few cross-lane
+  // steps); a ballot finds the lane holding it, ties between lanes go to the
+  // smallest expert index; that lane drops its head.
+  uint32_t key[VPL], ex[VPL];
   const float* row = logits + (int64_t)t * E;
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = v * 64 + lane;
-    c[v] = (e < E) ? (((uint64_t)order_key(row[e]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+    key[v] = (e < E) ? order_key(row[e]) : 0u;
+    ex[v] = (uint32_t)e;
   }
 #pragma unroll
   for (int i = 1; i < VPL; ++i) {
 #pragma unroll
     for (int j = i; j > 0; --j) {
-      const uint64_t hi = c[j] > c[j - 1] ? c[j] : c[j - 1];
-      const uint64_t lo = c[j] > c[j - 1] ? c[j - 1] : c[j];
-      c[j - 1] = hi;
-      c[j] = lo;
+      const bool sw = key[j] > key[j - 1];  // strict: equal keys keep ascending e
+      const uint32_t k0 = sw ? key[j] : key[j - 1], k1 = sw ? key[j - 1] : key[j];
+      const uint32_t e0 = sw ? ex[j] : ex[j - 1], e1 = sw ? ex[j - 1] : ex[j];
+      key[j - 1] = k0; key[j] = k1; ex[j - 1] = e0; ex[j] = e1;
     }
   }
-  uint64_t mine = 0;
+  uint32_t my_key = 0, my_e = 0;
   for (int r = 0; r < k; ++r) {
-    uint32_t bhi = (uint32_t)(c[0] >> 32), blo = (uint32_t)c[0];
-    wave_max_pair(bhi, blo);
-    const uint64_t best = ((uint64_t)bhi << 32) | blo;
-    const bool won = c[0] == best;
+    const uint32_t m = wave_max_u32(key[0]);
+    unsigned long long hold = __ballot(key[0] == m);
+    if (__builtin_popcountll(hold) > 1) {  // equal logits in several lanes
+      const uint32_t emin = wave_min_u32(key[0] == m ? ex[0] : 0xFFFFFFFFu);
+      hold = __ballot(key[0] == m && ex[0] == emin);
+    }
+    const int wl = __builtin_ctzll(hold);
+    const uint32_t we = __builtin_amdgcn_readlane(ex[0], wl);
+    if (lane == wl) {
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) c[v] = won ? (v + 1 < VPL ? c[v + 1] : 0ull) : c[v];
-    if (lane == r) mine = best;
+      for (int v = 0; v + 1 < VPL; ++v) {
+        key[v] = key[v + 1];
+        ex[v] = ex[v + 1];
+      }
+      key[VPL - 1] = 0u;
+    }
+    if (lane == r) {
+      my_key = m;
+      my_e = we;
+    }
   }
-  const uint32_t my_key = (uint32_t)(mine >> 32);
-  const int my_e = (int)~(uint32_t)mine;
   const float l0 = key_value(__builtin_amdgcn_readfirstlane(my_key));
-  const float ex = (lane < k) ? expf(key_value(my_key) - l0) : 0.0f;
-  const float sum = wave_sum(ex);
+  const float exv = (lane < k) ? expf(key_value(my_key) - l0) : 0.0f;
+  const float sum = wave_sum(exv);
   if (lane < k) {
-    topk_ids[(int64_t)t * k + lane] = my_e;
-    topk_w[(int64_t)t * k + lane] = ex / sum;
-    if (ids_copy) ids_copy[t * k + lane] = my_e;
+    topk_ids[(int64_t)t * k + lane] = (int)my_e;
+    topk_w[(int64_t)t * k + lane] = exv / sum;
+    if (ids_copy) ids_copy[t * k + lane] = (int)my_e;
   }
 }
 

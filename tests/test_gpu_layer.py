@@ -104,3 +104,22 @@ def test_layer_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
         (y @ y).sum().item()
+
+
+def test_layer_decode_ties_and_shared_experts():
+    """Equal logits at the top-k boundary and tokens sharing experts, through the decode path."""
+    shape = wl.LayerShape(E=64, H=256, I=128, k=8)
+    layer = device_layer(shape, 21)
+    base = np.full((3, 64), -1.0, np.float32)
+    base[:, [3, 9, 17, 40, 41, 50, 60, 63, 5, 7]] = 2.0          # 10 equal maxima: lowest 8 indices win
+    base[1, 12] = 3.0
+    base[2] = np.linspace(1, 0, 64, dtype=np.float32)               # shares experts 0..7 with nobody
+    base[2, 3] = 5.0                                                # shares expert 3 with tokens 0 and 1
+    x_bits = wl.bf16_bits_from_f32(np.random.default_rng(3).standard_normal((3, 256)).astype(np.float32))
+    for M in (1, 2, 3):
+        rb, outs = run_layer_call(layer, base[:M], x_bits[:M], 16, reps=2)
+        ids, w = assert_route_matches(route_host(rb), base[:M], shape.E, shape.k, 16)
+        ref = oracle.moe_forward(wl.f32_from_bf16_bits(x_bits[:M]).astype(np.float64), ids, w,
+                                 oracle_experts(shape, 21))
+        assert_output_close(outs[0], ref, f"ties M={M}")
+        assert np.array_equal(outs[0], outs[1])
