@@ -239,7 +239,7 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t ev0 = stage_events ? (hipEvent_t)stage_events[0] : nullptr;
   hipEvent_t ev1 = stage_events ? (hipEvent_t)stage_events[1] : nullptr;
-  if ((int64_t)M <= moe::kDecodeMaxTokens && (int64_t)M * top_k <= moe::kDecodeMaxAssign) {
+  if (moe::decode_path_fits(M, H, I, top_k)) {
     moe::DecodeArgs d{};
     d.fc = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
                    workspace);

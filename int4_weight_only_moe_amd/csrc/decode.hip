@@ -34,7 +34,8 @@ namespace moe {
 namespace {
 
 constexpr int kDecKSplit = 4;   // FC1 waves per workgroup (split K)
-constexpr int kDecP1 = 3;       // FC1 chunks in flight per wave
+// FC1 chunks in flight per wave (fewer for 3-4 rows: their sums need the registers)
+constexpr int dec_p1(int rows) { return rows <= 2 ? 4 : 3; }
 
 struct SmallRoute {
   int32_t ids[kDecodeMaxAssign];
@@ -44,21 +45,175 @@ struct SmallRoute {
   int32_t rowf[kDecodeMaxAssign][kDecodeMaxTokens];  // their f, ascending
 };
 
-template <int VPL, int NCH>
+// FC1 of one (expert, tile pair) for the M <= 4 rows of a block. Lane l < 16
+// holds D rows 0..3 (the block's rows) of column l of both tiles; lanes 16..63
+// hold padding rows, so only lanes 0..15 load scales and only the MR real
+// rows are scaled into the sums. The A operand of lane l is the staged x row
+// of its block row (row 0 for padding rows: finite values whose D rows are
+// never used).
+template <int MR, int NCH>
+__device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4* __restrict__ xs, int row16,
+                                                const int e, const int pair, const int frow, const int wave,
+                                                const int lane) {
+  const FcArgs& a = d.fc;
+  const int H = a.H, I = a.I, MK = a.M * a.k;
+  const int nkc = H / kChunkK;
+  const int kc0 = wave * nkc / kDecKSplit;
+  const int n = NCH > 0 ? NCH : (wave + 1) * nkc / kDecKSplit - kc0;
+
+  const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(2 * I, H) +
+                         ((int64_t)pair * nkc + kc0) * kPairChunkBytes;
+  const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
+  // lanes 16..63 read their scales out of range: zeros, no memory access
+  const uint32_t os0 = lane < 16 ? kTileNibbleBytes + 8u * lane : kOutOfRange;
+  const uint32_t os1 = lane < 16 ? kTileBytes + kTileNibbleBytes + 8u * lane : kOutOfRange;
+
+  // x of this lane's row, at this wave's first chunk and this lane's K offset
+  const int xrow = (frow >= 0 && frow < MK) ? frow / a.k : 0;
+  const uint4* xl = xs + xrow * row16 + kc0 * (kChunkK / 8) + (lane >> 4);
+
+  // One buffer descriptor per chunk (scalar arithmetic), so the per-lane
+  // offsets stay four constant registers; a chunk at or past n has no
+  // bytes in range and reads zeros.
+  auto load_w = [&](int c) {
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(wbase + (int64_t)c * kPairChunkBytes, c < n ? (uint32_t)kPairChunkBytes : 0u);
+    WChunk w;
+    w.q0 = bload16(wr, oq0);
+    w.q1 = bload16(wr, oq1);
+    w.s0 = bload8(wr, os0);
+    w.s1 = bload8(wr, os1);
+    return w;
+  };
+
+  constexpr int P = dec_p1(MR);
+  const bf16x8_t neg136 = as_bf16x8(make_uint4(kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair));
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  float acc0[MR], acc1[MR];
+#pragma unroll
+  for (int i = 0; i < MR; ++i) acc0[i] = acc1[i] = 0.f;
+
+  auto chunk = [&](const WChunk& w, int c) {
+    const uint32_t q0[4] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w};
+    const uint32_t q1[4] = {w.q1.x, w.q1.y, w.q1.z, w.q1.w};
+    const uint32_t s0w[2] = {w.s0.x, w.s0.y};
+    const uint32_t s1w[2] = {w.s1.x, w.s1.y};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8_t xv = as_bf16x8(xl[c * (kChunkK / 8) + 4 * j]);
+      const bf16x8_t b0 = dequant_u4_plus128(q0[j]);
+      const bf16x8_t b1 = dequant_u4_plus128(q1[j]);
+      const float g0 = f16_bits_to_f32((s0w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      const float g1 = f16_bits_to_f32((s1w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      const f32x4_t off = mfma16x16x32(xv, neg136, zero4);
+      const f32x4_t t0 = mfma16x16x32(xv, b0, off);
+      const f32x4_t t1 = mfma16x16x32(xv, b1, off);
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        acc0[i] = __builtin_fmaf(t0[i], g0, acc0[i]);
+        acc1[i] = __builtin_fmaf(t1[i], g1, acc1[i]);
+      }
+    }
+  };
+
+  WChunk wb[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) wb[j] = load_w(j);
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      chunk(wb[c % P], c);
+      if (c + P < NCH) wb[c % P] = load_w(c + P);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (int c = 0; c < n; c += P) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        if (c + j < n) chunk(wb[j], c + j);
+        wb[j] = load_w(c + j + P);
+      }
+    }
+  }
+
+  // K-split partials of the real rows meet in LDS; wave 0 finishes.
+  __shared__ float red[kDecKSplit - 1][2][MR][16];
+  if (wave > 0 && lane < 16) {
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      red[wave - 1][0][i][lane] = acc0[i];
+      red[wave - 1][1][i][lane] = acc1[i];
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || lane >= 16) return;
+#pragma unroll
+  for (int w = 0; w < kDecKSplit - 1; ++w) {
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      acc0[i] += red[w][0][i][lane];
+      acc1[i] += red[w][1][i][lane];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MR; ++i) {
+    const int f = __builtin_amdgcn_readlane(frow, i);  // the block's row i
+    if (f < 0 || f >= MK) continue;
+    const float g = acc0[i], u = acc1[i];
+    const float v = g / (1.0f + __expf(-g)) * u;
+    a.act_out[(int64_t)f * I + 16 * pair + lane] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+// x rows staged per thread before the routing (H = 7168: 896 16-byte vectors
+// per row, at most 4 per thread); for M > 2 the registers this takes are
+// needed by the routing, so the rows are loaded after it.
+constexpr int kXPerThread = 4;
+constexpr int kXEarlyRows = 2;
+
+template <int VPL, int NCH, int MR>
 __global__ __launch_bounds__(64 * kDecKSplit) __attribute__((amdgpu_waves_per_eu(4)))
 void fc1_decode_kernel(DecodeArgs d) {
   __shared__ SmallRoute sh;
+  extern __shared__ uint4 xs[];  // [M][row16]: the batch's x rows
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int M = d.fc.M, E = d.fc.E, k = d.fc.k;
+  const int M = d.fc.M, E = d.fc.E, k = d.fc.k, H = d.fc.H;
   const int MK = M * k;
   const int npairs = d.fc.I / 16;
   const int blk = blockIdx.x / npairs;
   const int pair = blockIdx.x % npairs;
+  const int hv = H / 8;        // 16-byte vectors per x row
+  const int row16 = hv + 1;    // padded LDS row stride: rows start on different banks
+  const uint4* xg = reinterpret_cast<const uint4*>(d.fc.act_in);
+
+  // The x loads do not depend on the routing: issue them first.
+  constexpr bool kEarly = NCH > 0 && MR <= kXEarlyRows;
+  uint4 xr[MR][kXPerThread];
+  if constexpr (kEarly) {
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+      for (int v = 0; v < kXPerThread; ++v) {
+        const int i = threadIdx.x + v * 64 * kDecKSplit;
+        xr[r][v] = (i < hv) ? xg[(int64_t)r * hv + i] : make_uint4(0, 0, 0, 0);
+      }
+  }
 
   if (wave < M) topk_token<VPL>(d.logits, wave, E, k, sh.ids, sh.w);
-  __syncthreads();
 
+  if constexpr (kEarly) {
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+      for (int v = 0; v < kXPerThread; ++v) {
+        const int i = threadIdx.x + v * 64 * kDecKSplit;
+        if (i < hv) xs[r * row16 + i] = xr[r][v];
+      }
+  } else {
+    for (int i = threadIdx.x; i < M * hv; i += blockDim.x) xs[(i / hv) * row16 + i % hv] = xg[i];
+  }
+  __syncthreads();
   // Assignment f sits in lane f. `before` = earlier assignments of the same
   // expert (its row within the expert's block), `first` = first occurrence.
   // A token never repeats an expert, so for M = 1 every lane is a first.
@@ -114,18 +269,18 @@ void fc1_decode_kernel(DecodeArgs d) {
   unsigned long long mb = firsts;
   for (int i = 0; i < blk; ++i) mb &= mb - 1;
   const int eb = __builtin_amdgcn_readlane(e, __builtin_ctzll(mb));
-  int frow[1] = {MK};
+  int frow = MK;
   for (int r = 0; r < M; ++r) {
     const unsigned long long m = __ballot(e == eb && before == r);
-    if ((lane & 15) == r && m) frow[0] = __builtin_ctzll(m);
+    if ((lane & 15) == r && m) frow = __builtin_ctzll(m);
   }
-  fc_block<1, kDecKSplit, kDecP1, NCH, true>(d.fc, eb, pair, frow, wave, lane);
+  fc1_decode_body<MR, NCH>(d, xs, row16, eb, pair, frow, wave, lane);
 }
 
-// One 16-row tile of a pair, for one activation row: per group, one MFMA for
-// -136*sum(x), one for the tile, scaled into the sum.
+// One 16-row tile of a pair, for one activation row (D row 0, lanes 0..15):
+// per group, one MFMA for -136*sum(x), one for the tile, scaled into the sum.
 __device__ __forceinline__ void mma_chunk_tile(uint4 q, uint2 sc, const uint4 (&xa)[4], const bf16x8_t neg136,
-                                               f32x4_t& acc) {
+                                               float& acc) {
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
   const uint32_t sw[2] = {sc.x, sc.y};
@@ -136,8 +291,7 @@ __device__ __forceinline__ void mma_chunk_tile(uint4 q, uint2 sc, const uint4 (&
     const bf16x8_t xv = as_bf16x8(xa[j]);
     const f32x4_t off = mfma16x16x32(xv, neg136, zero4);
     const f32x4_t t = mfma16x16x32(xv, b, off);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(t[i], g, acc[i]);
+    acc = __builtin_fmaf(t[0], g, acc);
   }
 }
 
@@ -167,8 +321,9 @@ void fc2_decode_kernel(DecodeArgs d) {
   const int n = I / kChunkK;
   const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(H, I) +
                          (int64_t)pair * n * kPairChunkBytes + h * kTileBytes;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)n * kPairChunkBytes);
-  const uint32_t oq = 16u * lane, os = kTileNibbleBytes + 8u * (lane & 15);
+  // Only D row 0 (lanes 0..15) is used: lanes 16..63 read their scales out of
+  // range (zeros, no memory access).
+  const uint32_t oq = 16u * lane, os = lane < 16 ? kTileNibbleBytes + 8u * lane : kOutOfRange;
   const int row16 = I / 8;
   const uint4* src = reinterpret_cast<const uint4*>(a.act_in) + (int64_t)f * row16;
   uint4* dst = xrows + j * row16;
@@ -176,10 +331,11 @@ void fc2_decode_kernel(DecodeArgs d) {
   constexpr int P2 = KW > 8 ? 4 : 6;
   uint4 qb[P2];
   uint2 sb[P2];
-  auto load = [&](int slot, int c) {
-    const uint32_t base = (uint32_t)c * kPairChunkBytes;  // past the K range: zeros
-    qb[slot] = bload16(wr, base + oq);
-    sb[slot] = bload8(wr, base + os);
+  auto load = [&](int slot, int c) {  // a chunk past the K range has no bytes in range: zeros
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(wbase + (int64_t)c * kPairChunkBytes, c < n ? (uint32_t)kTileBytes : 0u);
+    qb[slot] = bload16(wr, oq);
+    sb[slot] = bload8(wr, os);
   };
   // Issue order: the activation row, then the first P2 weight chunks, so that
   // staging the row waits only for its own loads.
@@ -202,7 +358,7 @@ void fc2_decode_kernel(DecodeArgs d) {
   const uint4* xl = dst + (lane >> 4);
 
   const bf16x8_t neg136 = as_bf16x8(make_uint4(kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair));
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float acc = 0.f;
   // A loop, not straight-line code: unrolled, the scheduler hoists every
   // chunk's LDS reads and spills; looped, the memory waits stay exact because
   // the only loads in flight are the weight ring's.
@@ -219,7 +375,7 @@ void fc2_decode_kernel(DecodeArgs d) {
     }
   }
   // D row 0 (the token) sits in lanes 0..15, element 0
-  if (lane < 16) part[j][lane] = wf * acc[0];
+  if (lane < 16) part[j][lane] = wf * acc;
   __syncthreads();
   if (threadIdx.x < 16) {
     float s = 0.f;
@@ -228,16 +384,32 @@ void fc2_decode_kernel(DecodeArgs d) {
   }
 }
 
+template <int VPL, int MR>
+hipError_t launch_fc1_decode(const DecodeArgs& d, unsigned grid, uint32_t xlds, hipStream_t stream, hipEvent_t e0,
+                             hipEvent_t e1) {
+  // H = 7168 (56 chunks, 14 per wave): straight-line chunk code
+  if (d.fc.H == 56 * kChunkK && (d.fc.H / 8 + 64 * kDecKSplit - 1) / (64 * kDecKSplit) <= kXPerThread)
+    launch_kernel(fc1_decode_kernel<VPL, 56 / kDecKSplit, MR>, grid, 64 * kDecKSplit, xlds, stream, e0, e1, d);
+  else
+    launch_kernel(fc1_decode_kernel<VPL, 0, MR>, grid, 64 * kDecKSplit, xlds, stream, e0, e1, d);
+  return hipGetLastError();
+}
+
 template <int VPL>
 hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int M = d.fc.M, E = d.fc.E, k = d.fc.k;
   const int nblk = M * k < E ? M * k : E;
   const unsigned grid1 = (unsigned)(nblk * (d.fc.I / 16));
-  if (d.fc.H == 56 * kChunkK && 56 % kDecKSplit == 0)
-    launch_kernel(fc1_decode_kernel<VPL, 56 / kDecKSplit>, grid1, 64 * kDecKSplit, 0, stream, e0, e1, d);
-  else
-    launch_kernel(fc1_decode_kernel<VPL, 0>, grid1, 64 * kDecKSplit, 0, stream, e0, e1, d);
-  hipError_t err = hipGetLastError();
+  const uint32_t xlds = (uint32_t)(M * (d.fc.H / 8 + 1) * 16);  // staged x rows
+  hipError_t err = hipSuccess;
+  switch (M) {
+    case 1: err = launch_fc1_decode<VPL, 1>(d, grid1, xlds, stream, e0, e1); break;
+    case 2: err = launch_fc1_decode<VPL, 2>(d, grid1, xlds, stream, e0, e1); break;
+    case 3: err = launch_fc1_decode<VPL, 3>(d, grid1, xlds, stream, e0, e1); break;
+    default: err = launch_fc1_decode<VPL, 4>(d, grid1, xlds, stream, e0, e1); break;
+  }
+  if (err != hipSuccess) return err;
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   DecodeArgs d2 = d;
   d2.fc.act_in = d.fc.act_out;

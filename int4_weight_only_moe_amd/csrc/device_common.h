@@ -23,14 +23,18 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h16) {
 // code 2p+1 in bits [16+4p, 16+4p+4)) become eight bf16 values 128 + u:
 // OR-ing a code into the mantissa of bf16 128.0 (0x4300, ulp 1) is exact.
 // Since q = u - 8, each value equals q + 136; the 136 * sum(x) excess is
-// removed by the caller.
+// removed by the caller. The mask and the exponent bits are held in
+// registers (gfx9 VOP3 encodings take no literal), so each output dword is
+// one v_and_or_b32.
 __device__ __forceinline__ bf16x8_t dequant_u4_plus128(uint32_t w) {
-  uint32_t p0 = (w & 0x000F000Fu) | 0x43004300u;
-  uint32_t p1 = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  uint32_t p2 = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  uint32_t p3 = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
-  uint4 v = make_uint4(p0, p1, p2, p3);
-  return __builtin_bit_cast(bf16x8_t, v);
+  uint32_t m, c;
+  asm("s_mov_b32 %0, 0xf000f" : "=s"(m));
+  asm("v_mov_b32 %0, 0x43004300" : "=v"(c));
+  const uint32_t p0 = (w & m) | c;
+  const uint32_t p1 = ((w >> 4) & m) | c;
+  const uint32_t p2 = ((w >> 8) & m) | c;
+  const uint32_t p3 = ((w >> 12) & m) | c;
+  return __builtin_bit_cast(bf16x8_t, make_uint4(p0, p1, p2, p3));
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }

@@ -73,7 +73,8 @@ __device__ __forceinline__ void fc_epilogue(const FcArgs& a, const int pair, con
                                             const bool (&sact)[S], const f32x4_t (&acc0)[S],
                                             const f32x4_t (&acc1)[S], const int lane) {
   const int MK = a.M * a.k;
-  const int col = lane & 15;
+  // recomputed here rather than kept live across the main loop
+  const int col = (int)__lane_id() & 15;
   if constexpr (kFc1) {
     const int I = a.I;
 #pragma unroll
@@ -140,17 +141,20 @@ __device__ __forceinline__ void fc_block(const FcArgs& a, const int e, const int
 
   const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(N, K) +
                          ((int64_t)pair * nkc + kc0) * kPairChunkBytes;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)n * kPairChunkBytes);
   const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
   const uint32_t os0 = kTileNibbleBytes + 8u * (lane & 15), os1 = kTileBytes + kTileNibbleBytes + 8u * (lane & 15);
 
+  // One buffer descriptor per chunk (scalar arithmetic), so the per-lane
+  // offsets stay four constant registers; a chunk at or past n has no bytes
+  // in range and reads zeros.
   auto load_w = [&](int c) {
-    const uint32_t base = (uint32_t)c * kPairChunkBytes;  // past n: reads zeros
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(wbase + (int64_t)c * kPairChunkBytes, c < n ? (uint32_t)kPairChunkBytes : 0u);
     WChunk w;
-    w.q0 = bload16(wr, base + oq0);
-    w.q1 = bload16(wr, base + oq1);
-    w.s0 = bload8(wr, base + os0);
-    w.s1 = bload8(wr, base + os1);
+    w.q0 = bload16(wr, oq0);
+    w.q1 = bload16(wr, oq1);
+    w.s0 = bload8(wr, os0);
+    w.s1 = bload8(wr, os1);
     return w;
   };
   auto load_x = [&](uint4 (&xa)[S][4], int c) {

@@ -78,6 +78,14 @@ hipError_t launch_fc2(const FcArgs& a, hipStream_t stream);
 constexpr int kMaxTopK = 16;
 constexpr int kDecodeMaxTokens = 4;
 constexpr int kDecodeMaxAssign = 64;  // M * k
+// The decode kernels stage the batch's x rows (FC1) and the k activation
+// rows of a token (FC2) in LDS; shapes whose rows do not fit take the
+// general path.
+constexpr int64_t kDecodeMaxStagedBytes = 56 * 1024;
+inline bool decode_path_fits(int64_t M, int64_t H, int64_t I, int64_t k) {
+  return M >= 1 && M <= kDecodeMaxTokens && M * k <= kDecodeMaxAssign &&
+         M * (H / 8 + 1) * 16 <= kDecodeMaxStagedBytes && k * I * 2 <= kDecodeMaxStagedBytes;
+}
 struct DecodeArgs {
   FcArgs fc;               // FC1 view: act_in = x, wpacked = W13, act_out = act, out = output
   const float* logits;     // [M, E]

@@ -51,7 +51,7 @@ struct AlignShared {
   int wcnt[kAlignWaves][kMaxExperts];
 };
 
-__device__ void align_body(AlignShared& sh, const int32_t* __restrict__ ids, int MK, int E,
+__device__ __forceinline__ void align_body(AlignShared& sh, const int32_t* __restrict__ ids, int MK, int E,
                            int block_m, int32_t* __restrict__ sorted_ids,
                            int32_t* __restrict__ block_expert, int32_t* __restrict__ offsets,
                            int32_t* __restrict__ npp_out) {

@@ -104,7 +104,7 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 }
 
 template <int VPL>
-__device__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
                            int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
                            int32_t* ids_copy = nullptr) {
   const int lane = threadIdx.x & 63;
