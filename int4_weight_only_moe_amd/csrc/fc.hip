@@ -83,9 +83,11 @@ void fc_kernel(FcArgs a) {
 // (one wave each, full K) and stages the block's activation chunk in LDS once
 // for all of them. The -136*sum(x) correction of each (row, group) is summed
 // while staging and enters the MFMA as its accumulator input, so no MFMA is
-// spent on it. Workgroup ids are remapped so that each XCD (workgroups are
-// dealt to the 8 XCDs round-robin) walks a contiguous range of blocks: a
-// block's activations and an expert's weights then stay in one XCD's L2.
+// spent on it. Workgroups are dealt to the 8 XCDs round-robin; the id
+// mapping gives XCD x the blocks x, x+8, x+16, ... with all pair groups of a
+// block on that XCD, back to back: a block's activations are read from that
+// XCD's L2 by its pair groups, and an expert with many blocks (skewed
+// routing) is spread over all XCDs instead of loading one of them.
 //
 // Per chunk step c (one barrier per step):
 //   issue the activation loads of chunk c+P and the weight loads of c+P
@@ -96,10 +98,7 @@ constexpr int kWideP = 2;                   // chunks in flight per wave (even: 
 constexpr int kRowVecs = kChunkK / 8;       // 16-byte vectors of a row's chunk slice
 constexpr int kRowPad = kRowVecs + 1;       // +16 B per row: conflict-free A reads
 
-__device__ __forceinline__ int xcd_remap(int p, int G) {
-  const int g8 = G / 8, rem = G % 8, x = p % 8, i = p / 8;
-  return x * g8 + (x < rem ? x : rem) + i;
-}
+constexpr int kXcds = 8;
 
 template <int S, bool kFc1>
 __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
@@ -124,10 +123,12 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
       z[i] = make_uint4(0, 0, 0, 0);
   }
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  // the grid holds a multiple of 8 blocks; the ones past cap have no rows
   const int npg = npairs / kWideNP;
-  const int blk = L / npg;
-  const int pair = (L % npg) * kWideNP + wave;
+  const int xcd = blockIdx.x % kXcds, gi = blockIdx.x / kXcds;
+  const int blk = (gi / npg) * kXcds + xcd;
+  const int pair = (gi % npg) * kWideNP + wave;
+  if ((int64_t)blk * BM >= a.cap) return;
   const int32_t* rows = a.sorted_ids + (int64_t)blk * BM;
   int frow[S];
 #pragma unroll
@@ -277,7 +278,7 @@ hipError_t launch_fc(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEven
   const int64_t grid = nblk * (N / kPairRows);
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool wide = (N / kPairRows) % kWideNP == 0;  // pairs split evenly over the wide workgroups
-  const unsigned wgrid = (unsigned)(nblk * (N / kPairRows / kWideNP));
+  const unsigned wgrid = (unsigned)((nblk + kXcds - 1) / kXcds * kXcds * (N / kPairRows / kWideNP));
   switch (a.block_m) {
     case 16: launch<1, 4, 3, kFc1>(a, (unsigned)grid, stream, e0, e1); break;
     case 32:
