@@ -18,7 +18,8 @@ MoE layers); each step reads copy i % R.
 Timing: W untimed warm-up steps, then K steps bracketed by
 torch.cuda.synchronize(), queued behind a GPU spin so that they run back to
 back as under a HIP graph; HIP events on the launch stream bracket the K
-steps and every FC1 launch (for the roofline figure). The same K steps
+steps; K more steps carry events around every FC1 launch (for the roofline
+figure). The same K steps
 replayed from one captured HIP graph are reported as context. The CPU oracle is timed on a bounded sample of
 the same workload (cpu_baseline).
 
@@ -195,13 +196,17 @@ class Bench:
                        stage_events=None if ev is None else (ev[0].handle, ev[1].handle))
 
     def run(self, name, steps, warmup, replicas):
-        """W eager warm-up steps, then K timed steps launched back to back.
+        """W eager warm-up steps, then K timed steps launched back to back, then
+        K more steps with HIP events on the FC1 stage.
 
         The Python host needs longer to launch a step than the GPU needs to run
         it at small M, so the timed steps are queued behind a GPU spin of known
         length: by the time the GPU reaches the start event, every step is
         already in the queue and runs without host gaps (as under a HIP graph).
-        Events on the launch stream bracket the K steps and each FC1 launch.
+        The first K steps carry no instrumentation (they give the per-call
+        time); the second K steps each record a pair of events around their
+        FC1 kernel (the kernel's own start and end timestamps) for the roofline
+        figure of that kernel.
         """
         torch = self.torch
         c = self.prepare(name)
@@ -212,19 +217,23 @@ class Bench:
             self.step(c, self.layers[i % R])
         host_per_step = (time.perf_counter() - h0) / max(warmup, 1)
         torch.cuda.synchronize()
-        evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         spin_s = min(2.0, 2.0 * host_per_step * steps + 2e-3)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         torch.cuda._sleep(int(spin_s * 2.4e9))
         start.record()
         for i in range(steps):
-            self.step(c, self.layers[i % R], evs[i])
+            self.step(c, self.layers[i % R])
         stop.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         total_ms = start.elapsed_time(stop)
+        evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
+        torch.cuda._sleep(int(spin_s * 2.4e9))
+        for i in range(steps):
+            self.step(c, self.layers[i % R], evs[i])
+        torch.cuda.synchronize()
         fc1_us = float(np.mean([a.elapsed_ms(b) for a, b in evs])) * 1e3
         return c, total_ms / steps, fc1_us, wall
 

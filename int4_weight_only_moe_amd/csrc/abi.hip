@@ -122,11 +122,14 @@ int64_t moe_w4a16_workspace_bytes(int32_t M, int32_t E, int32_t H, int32_t I, in
 
 int32_t moe_w4a16_preferred_block_m(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
   if (check_layer(M, E, H, I, top_k) != MOE_OK) return -1;
-  // Expected tokens per touched expert decides how many 16-row sub-tiles a
-  // block should carry: one block per expert whenever that stays <= 64 rows.
+  // Measured on the 384-expert layer (M = 9 ... 1024): 32-row blocks (the
+  // wide kernel, one LDS-staged activation chunk shared by 16 tile pairs)
+  // beat 16-row blocks from M = 9 up, and 64-row blocks only pay off once an
+  // expert averages more than ~24 rows. Batches of a few assignments keep
+  // 16-row blocks: the wide kernel would launch too few workgroups.
   const double per_expert = (double)M * top_k / E;
-  if (per_expert <= 8.0) return 16;
-  if (per_expert <= 20.0) return 32;
+  if ((int64_t)M * top_k <= 32) return 16;
+  if (per_expert <= 24.0) return 32;
   return 64;
 }
 

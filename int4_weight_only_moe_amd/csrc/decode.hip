@@ -45,18 +45,23 @@ struct SmallRoute {
   int32_t rowf[kDecodeMaxAssign][kDecodeMaxTokens];  // their f, ascending
 };
 
-// FC1 of one (expert, tile pair) for the M <= 4 rows of a block. Lane l < 16
-// holds D rows 0..3 (the block's rows) of column l of both tiles; lanes 16..63
-// hold padding rows, so only lanes 0..15 load scales and only the MR real
-// rows are scaled into the sums. The A operand of lane l is the staged x row
-// of its block row (row 0 for padding rows: finite values whose D rows are
-// never used).
+// FC1 of one (expert, tile pair) for the MR = M <= 4 tokens of the batch:
+// D row r is token r, whether or not it routes to expert e (the MFMA computes
+// 16 rows anyway; only the rows of tokens that route to e are stored). Lane
+// l < 16 holds D rows 0..3 of column l of both tiles; lanes 16..63 hold
+// padding rows, so only lanes 0..15 load scales and only the MR token rows
+// are scaled into the sums. The A operand of lane l is the staged x row of
+// token l % 16 (token 0 for padding rows: finite values whose D rows are
+// never used). The accumulator input of each group's MFMA is the staged
+// -136 * (group sum) of the four token rows (xcorr4[group] = one float per
+// token, zero past M), so that every MFMA is a product with the weights.
+// tokf: lane r < MR holds the assignment f of token r to expert e, or -1.
 template <int MR, int NCH>
 __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4* __restrict__ xs, int row16,
-                                                const int e, const int pair, const int frow, const int wave,
-                                                const int lane) {
+                                                const f32x4_t* __restrict__ xcorr4, const int e, const int pair,
+                                                const int tokf, const int wave, const int lane) {
   const FcArgs& a = d.fc;
-  const int H = a.H, I = a.I, MK = a.M * a.k;
+  const int H = a.H, I = a.I;
   const int nkc = H / kChunkK;
   const int kc0 = wave * nkc / kDecKSplit;
   const int n = NCH > 0 ? NCH : (wave + 1) * nkc / kDecKSplit - kc0;
@@ -69,8 +74,9 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
   const uint32_t os1 = lane < 16 ? kTileBytes + kTileNibbleBytes + 8u * lane : kOutOfRange;
 
   // x of this lane's row, at this wave's first chunk and this lane's K offset
-  const int xrow = (frow >= 0 && frow < MK) ? frow / a.k : 0;
+  const int xrow = (lane & 15) < MR ? (lane & 15) : 0;
   const uint4* xl = xs + xrow * row16 + kc0 * (kChunkK / 8) + (lane >> 4);
+  const f32x4_t* cr = xcorr4 + kc0 * (kChunkK / kGroup);  // this wave's first group
 
   // One buffer descriptor per chunk (scalar arithmetic), so the per-lane
   // offsets stay four constant registers; a chunk at or past n has no
@@ -79,16 +85,14 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
     const __amdgpu_buffer_rsrc_t wr =
         make_rsrc(wbase + (int64_t)c * kPairChunkBytes, c < n ? (uint32_t)kPairChunkBytes : 0u);
     WChunk w;
-    w.q0 = bload16(wr, oq0);
-    w.q1 = bload16(wr, oq1);
-    w.s0 = bload8(wr, os0);
-    w.s1 = bload8(wr, os1);
+    w.q0 = bload16<kPolicyWeights>(wr, oq0);
+    w.q1 = bload16<kPolicyWeights>(wr, oq1);
+    w.s0 = bload8<kPolicyWeights>(wr, os0);
+    w.s1 = bload8<kPolicyWeights>(wr, os1);
     return w;
   };
 
   constexpr int P = dec_p1(MR);
-  const bf16x8_t neg136 = as_bf16x8(make_uint4(kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair));
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   float acc0[MR], acc1[MR];
 #pragma unroll
   for (int i = 0; i < MR; ++i) acc0[i] = acc1[i] = 0.f;
@@ -105,7 +109,7 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
       const bf16x8_t b1 = dequant_u4_plus128(q1[j]);
       const float g0 = f16_bits_to_f32((s0w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
       const float g1 = f16_bits_to_f32((s1w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-      const f32x4_t off = mfma16x16x32(xv, neg136, zero4);
+      const f32x4_t off = cr[c * (kChunkK / kGroup) + j];
       const f32x4_t t0 = mfma16x16x32(xv, b0, off);
       const f32x4_t t1 = mfma16x16x32(xv, b1, off);
 #pragma unroll
@@ -157,8 +161,8 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
   }
 #pragma unroll
   for (int i = 0; i < MR; ++i) {
-    const int f = __builtin_amdgcn_readlane(frow, i);  // the block's row i
-    if (f < 0 || f >= MK) continue;
+    const int f = __builtin_amdgcn_readlane(tokf, i);  // token i's assignment to e
+    if (f < 0) continue;
     const float g = acc0[i], u = acc1[i];
     const float v = g / (1.0f + __expf(-g)) * u;
     a.act_out[(int64_t)f * I + 16 * pair + lane] = (uint16_t)f32_to_bf16_bits(v);
@@ -175,7 +179,7 @@ template <int VPL, int NCH, int MR>
 __global__ __launch_bounds__(64 * kDecKSplit) __attribute__((amdgpu_waves_per_eu(4)))
 void fc1_decode_kernel(DecodeArgs d) {
   __shared__ SmallRoute sh;
-  extern __shared__ uint4 xs[];  // [M][row16]: the batch's x rows
+  extern __shared__ uint4 xs[];  // [M][row16]: the batch's x rows, then xcorr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int M = d.fc.M, E = d.fc.E, k = d.fc.k, H = d.fc.H;
@@ -185,6 +189,10 @@ void fc1_decode_kernel(DecodeArgs d) {
   const int pair = blockIdx.x % npairs;
   const int hv = H / 8;        // 16-byte vectors per x row
   const int row16 = hv + 1;    // padded LDS row stride: rows start on different banks
+  const int ng = H / kGroup;   // quantisation groups per row
+  // [ng] x 4 tokens: -136 * group sums, zero for tokens past M
+  f32x4_t* xcorr4 = reinterpret_cast<f32x4_t*>(xs + M * row16);
+  float* xcorr = reinterpret_cast<float*>(xcorr4);
   const uint4* xg = reinterpret_cast<const uint4*>(d.fc.act_in);
 
   // The x loads do not depend on the routing: issue them first.
@@ -202,17 +210,33 @@ void fc1_decode_kernel(DecodeArgs d) {
 
   if (wave < M) topk_token<VPL>(d.logits, wave, E, k, sh.ids, sh.w);
 
+  // Stage the rows and their group corrections: the 4 vectors of a group sit
+  // in 4 consecutive threads (hv and the block size are multiples of 4, so a
+  // quad is either wholly inside a row or wholly past its end).
   if constexpr (kEarly) {
 #pragma unroll
     for (int r = 0; r < MR; ++r)
 #pragma unroll
       for (int v = 0; v < kXPerThread; ++v) {
         const int i = threadIdx.x + v * 64 * kDecKSplit;
-        if (i < hv) xs[r * row16 + i] = xr[r][v];
+        const float corr = group_corr_quad(xr[r][v]);
+        if (i < hv) {
+          xs[r * row16 + i] = xr[r][v];
+          if ((i & 3) == 0) xcorr[4 * (i >> 2) + r] = corr;
+        }
       }
   } else {
-    for (int i = threadIdx.x; i < M * hv; i += blockDim.x) xs[(i / hv) * row16 + i % hv] = xg[i];
+    for (int i = threadIdx.x; i < M * hv; i += blockDim.x) {
+      const uint4 v = xg[i];
+      const int r = i / hv, c = i % hv;
+      xs[r * row16 + c] = v;
+      const float corr = group_corr_quad(v);
+      if ((c & 3) == 0) xcorr[4 * (c >> 2) + r] = corr;
+    }
   }
+  if (M < kDecodeMaxTokens)
+    for (int g = threadIdx.x; g < ng; g += blockDim.x)
+      for (int r = M; r < kDecodeMaxTokens; ++r) xcorr[4 * g + r] = 0.f;
   __syncthreads();
   // Assignment f sits in lane f. `before` = earlier assignments of the same
   // expert (its row within the expert's block), `first` = first occurrence.
@@ -265,23 +289,22 @@ void fc1_decode_kernel(DecodeArgs d) {
 
   if (blk >= nd) return;
   // FC1 takes the distinct experts in order of first occurrence: block blk is
-  // the expert of the blk-th first occurrence; this lane's row (lane % 16) of it
+  // the expert of the blk-th first occurrence
   unsigned long long mb = firsts;
   for (int i = 0; i < blk; ++i) mb &= mb - 1;
   const int eb = __builtin_amdgcn_readlane(e, __builtin_ctzll(mb));
-  int frow = MK;
-  for (int r = 0; r < M; ++r) {
-    const unsigned long long m = __ballot(e == eb && before == r);
-    if ((lane & 15) == r && m) frow = __builtin_ctzll(m);
-  }
-  fc1_decode_body<MR, NCH>(d, xs, row16, eb, pair, frow, wave, lane);
+  // lane r < M: the assignment of token r to expert eb (a token lists an expert at most once)
+  int tokf = -1;
+  if (lane < M)
+    for (int j = 0; j < k; ++j) tokf = (sh.ids[lane * k + j] == eb) ? lane * k + j : tokf;
+  fc1_decode_body<MR, NCH>(d, xs, row16, xcorr4, eb, pair, tokf, wave, lane);
 }
 
 // One 16-row tile of a pair, for one activation row (D row 0, lanes 0..15):
-// per group, one MFMA for -136*sum(x), one for the tile, scaled into the sum.
-__device__ __forceinline__ void mma_chunk_tile(uint4 q, uint2 sc, const uint4 (&xa)[4], const bf16x8_t neg136,
+// per group, one MFMA whose accumulator input is the row's -136 * (group
+// sum) (replicated over the four D rows a lane holds), scaled into the sum.
+__device__ __forceinline__ void mma_chunk_tile(uint4 q, uint2 sc, const uint4 (&xa)[4], const f32x4_t (&corr)[4],
                                                float& acc) {
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
   const uint32_t sw[2] = {sc.x, sc.y};
 #pragma unroll
@@ -289,8 +312,7 @@ __device__ __forceinline__ void mma_chunk_tile(uint4 q, uint2 sc, const uint4 (&
     const bf16x8_t b = dequant_u4_plus128(qq[j]);
     const float g = f16_bits_to_f32((sw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
     const bf16x8_t xv = as_bf16x8(xa[j]);
-    const f32x4_t off = mfma16x16x32(xv, neg136, zero4);
-    const f32x4_t t = mfma16x16x32(xv, b, off);
+    const f32x4_t t = mfma16x16x32(xv, b, corr[j]);
     acc = __builtin_fmaf(t[0], g, acc);
   }
 }
@@ -300,9 +322,10 @@ __device__ __forceinline__ void mma_chunk_tile(uint4 q, uint2 sc, const uint4 (&
 template <int ROWV, int KW>  // KW: waves per workgroup the launch bounds allow (>= top_k)
 __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(4)))
 void fc2_decode_kernel(DecodeArgs d) {
-  // Each wave's activation row (I bf16) is staged in LDS once; per chunk the
-  // A operand comes from LDS, so registers hold only the weight stream.
-  extern __shared__ uint4 xrows[];  // [k][I / 8]
+  // Each wave's activation row (I bf16) is staged in LDS once, with its
+  // -136 * (group sum) corrections; per chunk the A operand comes from LDS, so
+  // registers hold only the weight stream.
+  extern __shared__ uint4 xrows[];  // [k][I / 8], then the corrections [k][I / 32] (x4)
   __shared__ float part[KW][16];
   const int lane = threadIdx.x & 63;
   const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // routing slot
@@ -325,8 +348,10 @@ void fc2_decode_kernel(DecodeArgs d) {
   // range (zeros, no memory access).
   const uint32_t oq = 16u * lane, os = lane < 16 ? kTileNibbleBytes + 8u * lane : kOutOfRange;
   const int row16 = I / 8;
+  const int ng = I / kGroup;
   const uint4* src = reinterpret_cast<const uint4*>(a.act_in) + (int64_t)f * row16;
   uint4* dst = xrows + j * row16;
+  f32x4_t* corr = reinterpret_cast<f32x4_t*>(xrows + k * row16) + j * ng;
 
   constexpr int P2 = KW > 8 ? 4 : 6;
   uint4 qb[P2];
@@ -334,8 +359,8 @@ void fc2_decode_kernel(DecodeArgs d) {
   auto load = [&](int slot, int c) {  // a chunk past the K range has no bytes in range: zeros
     const __amdgpu_buffer_rsrc_t wr =
         make_rsrc(wbase + (int64_t)c * kPairChunkBytes, c < n ? (uint32_t)kTileBytes : 0u);
-    qb[slot] = bload16(wr, oq);
-    sb[slot] = bload8(wr, os);
+    qb[slot] = bload16<kPolicyWeights>(wr, oq);
+    sb[slot] = bload8<kPolicyWeights>(wr, os);
   };
   // Issue order: the activation row, then the first P2 weight chunks, so that
   // staging the row waits only for its own loads.
@@ -346,9 +371,19 @@ void fc2_decode_kernel(DecodeArgs d) {
 #pragma unroll
     for (int s = 0; s < P2; ++s) load(s, s);
 #pragma unroll
-    for (int r = 0; r < ROWV; ++r) dst[lane + 64 * r] = xs[r];
+    for (int r = 0; r < ROWV; ++r) {
+      dst[lane + 64 * r] = xs[r];
+      const float cg = group_corr_quad(xs[r]);
+      if ((lane & 3) == 0) corr[(lane + 64 * r) >> 2] = f32x4_t{cg, cg, cg, cg};
+    }
   } else {
-    for (int i = lane; i < row16; i += 64) dst[i] = ok ? src[i] : make_uint4(0, 0, 0, 0);
+    // row16 is a multiple of 4: a quad of lanes is wholly inside the row or past it
+    for (int i = lane; i < row16; i += 64) {
+      const uint4 v = ok ? src[i] : make_uint4(0, 0, 0, 0);
+      dst[i] = v;
+      const float cg = group_corr_quad(v);
+      if ((i & 3) == 0) corr[i >> 2] = f32x4_t{cg, cg, cg, cg};
+    }
 #pragma unroll
     for (int s = 0; s < P2; ++s) load(s, s);
   }
@@ -357,7 +392,6 @@ void fc2_decode_kernel(DecodeArgs d) {
   // row (rows 1..15 of D are not used), so no lane needs a zero fill
   const uint4* xl = dst + (lane >> 4);
 
-  const bf16x8_t neg136 = as_bf16x8(make_uint4(kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair));
   float acc = 0.f;
   // A loop, not straight-line code: unrolled, the scheduler hoists every
   // chunk's LDS reads and spills; looped, the memory waits stay exact because
@@ -367,9 +401,13 @@ void fc2_decode_kernel(DecodeArgs d) {
     for (int s = 0; s < P2; ++s) {
       if (c + s < n) {
         uint4 xa[4];
+        f32x4_t cg[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) xa[g] = xl[(c + s) * (kChunkK / 8) + 4 * g];
-        mma_chunk_tile(qb[s], sb[s], xa, neg136, acc);
+        for (int g = 0; g < 4; ++g) {
+          xa[g] = xl[(c + s) * (kChunkK / 8) + 4 * g];
+          cg[g] = corr[(c + s) * (kChunkK / kGroup) + g];
+        }
+        mma_chunk_tile(qb[s], sb[s], xa, cg, acc);
       }
       load(s, c + s + P2);
     }
@@ -400,7 +438,7 @@ hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t
   const int M = d.fc.M, E = d.fc.E, k = d.fc.k;
   const int nblk = M * k < E ? M * k : E;
   const unsigned grid1 = (unsigned)(nblk * (d.fc.I / 16));
-  const uint32_t xlds = (uint32_t)(M * (d.fc.H / 8 + 1) * 16);  // staged x rows
+  const uint32_t xlds = (uint32_t)decode_fc1_lds_bytes(M, d.fc.H);  // staged x rows + corrections
   hipError_t err = hipSuccess;
   switch (M) {
     case 1: err = launch_fc1_decode<VPL, 1>(d, grid1, xlds, stream, e0, e1); break;
@@ -416,7 +454,7 @@ hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t
   d2.fc.wpacked = d.w2;
   const unsigned grid2 = (unsigned)(M * (d.fc.H / 16));
   const bool i2048 = d.fc.I == 2048;  // the 384-expert layer: 4 row vectors per lane
-  const size_t lds = (size_t)k * d.fc.I * 2;  // the k activation rows
+  const size_t lds = (size_t)decode_fc2_lds_bytes(d.fc.I, k);  // the k activation rows + corrections
   if (k <= 8) {
     if (i2048) fc2_decode_kernel<4, 8><<<grid2, 64 * k, lds, stream>>>(d2);
     else fc2_decode_kernel<0, 8><<<grid2, 64 * k, lds, stream>>>(d2);

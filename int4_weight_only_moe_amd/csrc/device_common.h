@@ -25,11 +25,14 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h16) {
 // Since q = u - 8, each value equals q + 136; the 136 * sum(x) excess is
 // removed by the caller. The mask and the exponent bits are held in
 // registers (gfx9 VOP3 encodings take no literal), so each output dword is
-// one v_and_or_b32.
+// one v_and_or_b32: the empty asm statements only hide the constants' values
+// from the optimiser (which would otherwise fold them back into literals);
+// they emit no instruction, so every register write stays visible to the
+// compiler's hazard checks (an instruction written in inline asm is not).
 __device__ __forceinline__ bf16x8_t dequant_u4_plus128(uint32_t w) {
-  uint32_t m, c;
-  asm("s_mov_b32 %0, 0xf000f" : "=s"(m));
-  asm("v_mov_b32 %0, 0x43004300" : "=v"(c));
+  uint32_t m = 0xf000fu, c = 0x43004300u;
+  asm("" : "+s"(m));
+  asm("" : "+v"(c));
   const uint32_t p0 = (w & m) | c;
   const uint32_t p1 = ((w >> 4) & m) | c;
   const uint32_t p2 = ((w >> 8) & m) | c;

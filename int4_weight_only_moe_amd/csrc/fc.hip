@@ -100,46 +100,17 @@ constexpr int kRowPad = kRowVecs + 1;       // +16 B per row: conflict-free A re
 
 constexpr int kXcds = 8;
 
-template <int S, bool kFc1>
-__global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
-  constexpr int BM = 16 * S;
-  constexpr int kThreads = 64 * kWideNP;
-  constexpr int kItems = BM * kRowVecs;  // multiple of 64: whole waves stage or idle
+// The chunk loop and epilogue of one wide workgroup (block blk of expert e,
+// this wave's pair), with the weight loads issued under cache policy kPolicy.
+template <int S, bool kFc1, int kPolicy>
+__device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const int pair, const int (&frow)[S],
+                                             const int sf, const bool stager, const int srow, const int svec,
+                                             uint4 (&xt)[2][16 * S][kRowPad], f32x4_t (&xs4)[2][4][4 * S]) {
   constexpr int P = kWideP;
-  __shared__ uint4 xt[2][BM][kRowPad];
-  __shared__ f32x4_t xs4[2][4][BM / 4];  // -136 * group sums: [slot][group][4-row quad]
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
   const int K = kFc1 ? a.H : a.I;
   const int N = kFc1 ? 2 * a.I : a.H;
-  const int npairs = N / kPairRows;
   const int MK = a.M * a.k;
-
-  if constexpr (kFc1) {  // clear FC2's accumulator
-    uint4* z = reinterpret_cast<uint4*>(a.acc);
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < a.zero_words16; i += stride)
-      z[i] = make_uint4(0, 0, 0, 0);
-  }
-
-  // the grid holds a multiple of 8 blocks; the ones past cap have no rows
-  const int npg = npairs / kWideNP;
-  const int xcd = blockIdx.x % kXcds, gi = blockIdx.x / kXcds;
-  const int blk = (gi / npg) * kXcds + xcd;
-  const int pair = (gi % npg) * kWideNP + wave;
-  if ((int64_t)blk * BM >= a.cap) return;
-  const int32_t* rows = a.sorted_ids + (int64_t)blk * BM;
-  int frow[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) frow[s] = rows[16 * s + (lane & 15)];
-  const bool stager = tid < kItems;
-  const int srow = tid / kRowVecs, svec = tid % kRowVecs;
-  const int sf = stager ? rows[srow] : MK;
-  const int npp = __builtin_amdgcn_readfirstlane(*a.npp);
-  const int e = __builtin_amdgcn_readfirstlane(a.block_expert[blk]);
-  if (blk * BM >= npp) return;
-  if (e < 0 || e >= a.E) return;
 
   bool sact[S];
 #pragma unroll
@@ -158,10 +129,10 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
   auto load_w = [&](int c) {
     const uint32_t base = (uint32_t)c * kPairChunkBytes;  // past the K range: zeros
     WChunk w;
-    w.q0 = bload16(wr, base + oq0);
-    w.q1 = bload16(wr, base + oq1);
-    w.s0 = bload8(wr, base + os0);
-    w.s1 = bload8(wr, base + os1);
+    w.q0 = bload16<kPolicy>(wr, base + oq0);
+    w.q1 = bload16<kPolicy>(wr, base + oq1);
+    w.s0 = bload8<kPolicy>(wr, base + os0);
+    w.s1 = bload8<kPolicy>(wr, base + os1);
     return w;
   };
   auto load_x = [&](int c) { return bload16(xr, (c < n) ? soff + (uint32_t)c * (kChunkK * 2) : kOutOfRange); };
@@ -169,14 +140,8 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
   auto store_x = [&](uint4 v, int slot) {
     if (!stager) return;
     xt[slot][srow][svec] = v;
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sum += __uint_as_float(w4[i] << 16) + __uint_as_float(w4[i] & 0xFFFF0000u);
-    sum += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(sum), 0xB1, 0xf, 0xf, false));
-    sum += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(sum), 0x4E, 0xf, 0xf, false));
-    if ((svec & 3) == 0) reinterpret_cast<float*>(&xs4[slot][svec >> 2][0])[srow] = -136.0f * sum;
+    const float corr = group_corr_quad(v);
+    if ((svec & 3) == 0) reinterpret_cast<float*>(&xs4[slot][svec >> 2][0])[srow] = corr;
   };
 
   f32x4_t acc0[S], acc1[S];
@@ -237,6 +202,57 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
     }
   }
   fc_epilogue<S, kFc1>(a, pair, frow, sact, acc0, acc1, lane);
+}
+
+
+template <int S, bool kFc1>
+__global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
+  constexpr int BM = 16 * S;
+  constexpr int kThreads = 64 * kWideNP;
+  constexpr int kItems = BM * kRowVecs;  // multiple of 64: whole waves stage or idle
+  __shared__ uint4 xt[2][BM][kRowPad];   // the block's activation chunk, double-buffered
+  __shared__ f32x4_t xs4[2][4][BM / 4];  // -136 * group sums: [slot][group][4-row quad]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = kFc1 ? 2 * a.I : a.H;
+  const int npairs = N / kPairRows;
+  const int MK = a.M * a.k;
+
+  if constexpr (kFc1) {  // clear FC2's accumulator
+    uint4* z = reinterpret_cast<uint4*>(a.acc);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < a.zero_words16; i += stride)
+      z[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  // the grid holds a multiple of 8 blocks; the ones past cap have no rows
+  const int npg = npairs / kWideNP;
+  const int xcd = blockIdx.x % kXcds, gi = blockIdx.x / kXcds;
+  const int blk = (gi / npg) * kXcds + xcd;
+  const int pair = (gi % npg) * kWideNP + wave;
+  if ((int64_t)blk * BM >= a.cap) return;
+  const int32_t* rows = a.sorted_ids + (int64_t)blk * BM;
+  int frow[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) frow[s] = rows[16 * s + (lane & 15)];
+  const bool stager = tid < kItems;
+  const int srow = tid / kRowVecs, svec = tid % kRowVecs;
+  const int sf = stager ? rows[srow] : MK;
+  const int npp = __builtin_amdgcn_readfirstlane(*a.npp);
+  const int e = __builtin_amdgcn_readfirstlane(a.block_expert[blk]);
+  if (blk * BM >= npp) return;
+  if (e < 0 || e >= a.E) return;
+
+  // Weights are streamed non-temporally (read once per call) unless the
+  // expert has more than one block: then its other blocks re-read them and
+  // they are kept in the caches.
+  const bool reuse = (blk > 0 && a.block_expert[blk - 1] == e) ||
+                     ((blk + 1) * BM < npp && a.block_expert[blk + 1] == e);
+  if (__builtin_amdgcn_readfirstlane((int)reuse))
+    fc_wide_body<S, kFc1, kPolicyDefault>(a, e, pair, frow, sf, stager, srow, svec, xt, xs4);
+  else
+    fc_wide_body<S, kFc1, kPolicyWeights>(a, e, pair, frow, sf, stager, srow, svec, xt, xs4);
 }
 
 // out = bf16(acc), 8 values per thread.

@@ -81,10 +81,15 @@ constexpr int kDecodeMaxAssign = 64;  // M * k
 // The decode kernels stage the batch's x rows (FC1) and the k activation
 // rows of a token (FC2) in LDS; shapes whose rows do not fit take the
 // general path.
-constexpr int64_t kDecodeMaxStagedBytes = 56 * 1024;
+// The staged rows also carry their -136 * (group sum) corrections: FC1 one
+// float4 per group (the batch's 4 token slots), FC2 one float4 per group and
+// row (the value replicated, the accumulator input of one MFMA).
+constexpr int64_t kDecodeMaxStagedBytes = 64 * 1024;
+inline int64_t decode_fc1_lds_bytes(int64_t M, int64_t H) { return M * (H / 8 + 1) * 16 + (H / 32) * 16; }
+inline int64_t decode_fc2_lds_bytes(int64_t I, int64_t k) { return k * (I * 2 + (I / 32) * 16); }
 inline bool decode_path_fits(int64_t M, int64_t H, int64_t I, int64_t k) {
   return M >= 1 && M <= kDecodeMaxTokens && M * k <= kDecodeMaxAssign &&
-         M * (H / 8 + 1) * 16 <= kDecodeMaxStagedBytes && k * I * 2 <= kDecodeMaxStagedBytes;
+         decode_fc1_lds_bytes(M, H) <= kDecodeMaxStagedBytes && decode_fc2_lds_bytes(I, k) <= kDecodeMaxStagedBytes;
 }
 struct DecodeArgs {
   FcArgs fc;               // FC1 view: act_in = x, wpacked = W13, act_out = act, out = output

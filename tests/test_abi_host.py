@@ -74,8 +74,10 @@ def test_workspace_bytes():
 
 def test_preferred_block_m():
     assert moe.moe_w4a16_preferred_block_m(1, 384, 7168, 2048, 8) == 16
-    assert moe.moe_w4a16_preferred_block_m(90, 384, 7168, 2048, 8) == 16
-    assert moe.moe_w4a16_preferred_block_m(512, 384, 7168, 2048, 8) == 32
+    assert moe.moe_w4a16_preferred_block_m(4, 384, 7168, 2048, 8) == 16
+    assert moe.moe_w4a16_preferred_block_m(9, 384, 7168, 2048, 8) == 32
+    assert moe.moe_w4a16_preferred_block_m(90, 384, 7168, 2048, 8) == 32
+    assert moe.moe_w4a16_preferred_block_m(1024, 384, 7168, 2048, 8) == 32
     assert moe.moe_w4a16_preferred_block_m(4096, 384, 7168, 2048, 8) == 64
 
 
