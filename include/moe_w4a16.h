@@ -137,8 +137,9 @@ int moe_w4a16_unpack(const void* packed, int32_t E, int32_t N, int32_t K, int32_
 
 /*
  * moe_w4a16_workspace_bytes (host): scratch the forward needs for M tokens:
- * an fp32 [M, H] accumulator and the bf16 [M*top_k, I] FC1 activations, each
- * padded to 256 bytes. Returns -1 on invalid sizes.
+ * an fp32 [M, H] accumulator, the bf16 [M*top_k, I] FC1 activations, and
+ * the tile table of the tiled grouped GEMM (256 bytes + (2*M*top_k + 16) x
+ * 8 bytes), each padded to 256 bytes. Returns -1 on invalid sizes.
  */
 int64_t moe_w4a16_workspace_bytes(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k);
 

@@ -144,6 +144,15 @@ static int check_fc(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, i
   return MOE_OK;
 }
 
+// The tiled grouped GEMM (up to 128-row tiles) takes over from the block
+// kernels once experts average this many assignments.
+#ifndef MOE_TILED_MIN_PER_EXPERT
+#define MOE_TILED_MIN_PER_EXPERT 16.0
+#endif
+static bool use_tiled(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
+  return moe::tile_path_supported(H, I) && (double)M * top_k / E >= MOE_TILED_MIN_PER_EXPERT;
+}
+
 static moe::FcArgs fc_args(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
                            int64_t cap, const int32_t* sorted_ids, const int32_t* block_expert,
                            const int32_t* npp, void* workspace) {
@@ -158,6 +167,11 @@ static moe::FcArgs fc_args(int32_t M, int32_t E, int32_t H, int32_t I, int32_t t
   a.M = M; a.E = E; a.H = H; a.I = I; a.k = top_k; a.block_m = block_m;
   a.cap = cap;
   a.zero_words16 = (int64_t)M * H * 4 / 16;
+  if (use_tiled(M, E, H, I, top_k)) {
+    a.tiles = (int2*)(ws + L.tiles_off);
+    a.ntiles = (int32_t*)(ws + L.ntiles_off);
+    a.max_tiles = (int)moe::tile_grid_tiles(M, E, top_k, block_m, cap);
+  }
   return a;
 }
 

@@ -289,6 +289,15 @@ void launch(const FcArgs& a, unsigned grid, hipStream_t stream, hipEvent_t e0, h
 
 template <bool kFc1>
 hipError_t launch_fc(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  if (a.tiles) {  // tiled path: FC1 first writes the tile table FC2 reuses
+    hipError_t err = hipSuccess;
+    if constexpr (kFc1) err = launch_tile_plan(a, stream);
+    if (err == hipSuccess) err = launch_fc_tiled<kFc1>(a, stream, e0, e1);
+    if (err != hipSuccess || kFc1) return err;
+    const int64_t n8 = (int64_t)a.M * a.H / 8;
+    finalize_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, stream>>>(a.acc, a.out, n8);
+    return hipGetLastError();
+  }
   const int N = kFc1 ? 2 * a.I : a.H;
   const int64_t nblk = a.cap / a.block_m;
   const int64_t grid = nblk * (N / kPairRows);

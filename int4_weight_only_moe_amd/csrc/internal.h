@@ -29,16 +29,30 @@ __host__ __device__ inline int64_t packed_bytes_per_expert(int64_t N, int64_t K)
   return (N / kPairRows) * (K / kChunkK) * kPairChunkBytes;
 }
 
-// Workspace layout of the forward: [acc fp32 M x H][act bf16 M*k x I]
+// Tiles of the tiled grouped GEMM (fc_tile.hip): up to 128 rows of one
+// expert, in 16-row sub-tiles. Table entry: (first row in the sorted list,
+// meta = sub-tiles | reuse flag | expert << 8). A sub-tile has kTileRows rows.
+constexpr int kTileMaxRows = 64;
+constexpr int kTileNsubMask = 15;
+constexpr int kTileReuseBit = 16;
+constexpr int kTileExpertShift = 8;
+// Upper bound of the tile count for any block_m (a tile starts at every
+// expert change and every 128 rows of the block_m-padded list).
+inline int64_t tile_table_entries(int64_t M, int64_t k) { return 2 * M * k + 16; }
+
+// Workspace layout of the forward:
+// [acc fp32 M x H][act bf16 M*k x I][tile count int32 (16 B)][tile table int2]
 struct WorkspaceLayout {
-  int64_t acc_off, act_off, total;
+  int64_t acc_off, act_off, ntiles_off, tiles_off, total;
 };
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 inline WorkspaceLayout workspace_layout(int64_t M, int64_t H, int64_t I, int64_t k) {
   WorkspaceLayout w;
   w.acc_off = 0;
   w.act_off = align256(M * H * 4);
-  w.total = w.act_off + align256(M * k * I * 2);
+  w.ntiles_off = w.act_off + align256(M * k * I * 2);
+  w.tiles_off = w.ntiles_off + 256;
+  w.total = w.tiles_off + align256(tile_table_entries(M, k) * 8);
   return w;
 }
 
@@ -66,6 +80,10 @@ struct FcArgs {
   int M, E, H, I, k, block_m;
   int64_t cap;
   int64_t zero_words16;         // FC1: 16-byte words of acc to clear
+  // tiled path only (tiles != nullptr): the tile table FC1's plan writes
+  int2* tiles;                  // [max_tiles]
+  int32_t* ntiles;              // [1]
+  int max_tiles;                // grid tiles (a multiple of 8)
 };
 
 // ev_start / ev_stop (may be null) take the FC1 kernel's own start and end
@@ -73,6 +91,13 @@ struct FcArgs {
 hipError_t launch_fc1(const FcArgs& a, hipStream_t stream, hipEvent_t ev_start = nullptr,
                       hipEvent_t ev_stop = nullptr);
 hipError_t launch_fc2(const FcArgs& a, hipStream_t stream);
+
+// Tiled path (fc_tile.hip).
+bool tile_path_supported(int64_t H, int64_t I);
+int64_t tile_grid_tiles(int64_t M, int64_t E, int64_t k, int64_t block_m, int64_t cap);
+hipError_t launch_tile_plan(const FcArgs& a, hipStream_t stream);
+template <bool kFc1>
+hipError_t launch_fc_tiled(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1);
 
 // Decode path (tiny batches): routing fused into FC1, output-stationary FC2.
 constexpr int kMaxTopK = 16;

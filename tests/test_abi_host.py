@@ -67,7 +67,8 @@ def test_workspace_bytes():
     def a256(v):
         return (v + 255) // 256 * 256
     M, E, H, I, k = 1024, 384, 7168, 2048, 8
-    want = a256(M * H * 4) + a256(M * k * I * 2)
+    # fp32 accumulator, bf16 activations, tile count, tile table (2*M*k + 16 entries of 8 bytes)
+    want = a256(M * H * 4) + a256(M * k * I * 2) + 256 + a256((2 * M * k + 16) * 8)
     assert moe.moe_w4a16_workspace_bytes(M, E, H, I, k) == want
     assert moe.moe_w4a16_workspace_bytes(1, E, 7000, I, k) == -1
 

@@ -1,0 +1,53 @@
+"""The tiled grouped GEMM, which the forward takes once experts average at
+least 16 assignments (and every pair group and K-chunk count divides evenly):
+every element against the oracle on shapes whose experts hold from one small
+tile up to several 128-row tiles, with partial tiles of every sub-tile count,
+all block sizes, and skewed routing (a per-expert logit bias) that piles
+hundreds of rows onto a few experts."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_common import assert_output_close, assert_route_matches, device_layer, oracle_experts, route_host, run_layer
+
+pytestmark = pytest.mark.gpu
+
+SMALL = wl.LayerShape(E=8, H=256, I=256, k=2)
+WIDER = wl.LayerShape(E=32, H=512, I=512, k=4)
+
+TILED = [
+    # (shape, M, bias sigma, weight seed, token seed)
+    (SMALL, 64, 0.0, 11, 12),    # 16 assignments per expert: tiles of 1-2 sub-tiles
+    (SMALL, 300, 0.0, 11, 13),   # ~75 per expert: 5-sub-tile tiles (run as 8)
+    (SMALL, 700, 2.0, 11, 14),   # skewed: several 128-row tiles on the hot experts
+    (WIDER, 160, 1.0, 15, 16),   # 20 per expert, mildly skewed
+]
+
+
+@pytest.mark.parametrize("case", range(len(TILED)))
+@pytest.mark.parametrize("block_m", [16, 32, 64])
+def test_tiled_full_parity(case, block_m):
+    shape, M, sigma, wseed, tseed = TILED[case]
+    assert M * shape.k / shape.E >= 16
+    print(f"tiled {shape} M={M} sigma={sigma} block_m={block_m}", flush=True)
+    layer = device_layer(shape, wseed)
+    t = wl.tokens(shape, M, tseed, sigma)
+    rb, out = run_layer(layer, t.logits, t.x_bits, block_m)
+    ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, block_m)
+    counts = np.bincount(ids.reshape(-1), minlength=shape.E)
+    print(f"tiled: rows per expert {sorted(counts.tolist(), reverse=True)[:6]}", flush=True)
+    x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)
+    ref = oracle.moe_forward(x, ids, w, oracle_experts(shape, wseed))
+    assert np.all(np.isfinite(out))
+    assert_output_close(out, ref, f"tiled {shape} M={M} B={block_m}")
+
+
+def test_tiled_skew_has_multi_tile_experts():
+    """The skewed case really exercises experts with several 128-row tiles."""
+    shape, M, sigma, _, tseed = TILED[2]
+    t = wl.tokens(shape, M, tseed, sigma)
+    ids, _ = oracle.route(t.logits, shape.k)
+    counts = np.bincount(ids.reshape(-1), minlength=shape.E)
+    assert counts.max() > 2 * 128
+    assert any(c % 128 and (c % 128) // 16 + 1 in (3, 5, 6, 7) for c in counts)
