@@ -63,11 +63,14 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
   const FcArgs& a = d.fc;
   const int H = a.H, I = a.I;
   const int nkc = H / kChunkK;
-  const int kc0 = wave * nkc / kDecKSplit;
-  const int n = NCH > 0 ? NCH : (wave + 1) * nkc / kDecKSplit - kc0;
+  // The waves take the pair's chunks in turn (wave w: chunks w, w + 4, ...),
+  // so a workgroup reads its pair as one contiguous stream (measured: 4
+  // separate 32 KB streams per workgroup left waves 1-3 far behind wave 0).
+  const int n = NCH > 0 ? NCH : (nkc - wave + kDecKSplit - 1) / kDecKSplit;
+  constexpr int64_t kStride = (int64_t)kDecKSplit * kPairChunkBytes;
 
   const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(2 * I, H) +
-                         ((int64_t)pair * nkc + kc0) * kPairChunkBytes;
+                         ((int64_t)pair * nkc + wave) * kPairChunkBytes;
   const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
   // lanes 16..63 read their scales out of range: zeros, no memory access
   const uint32_t os0 = lane < 16 ? kTileNibbleBytes + 8u * lane : kOutOfRange;
@@ -75,15 +78,15 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
 
   // x of this lane's row, at this wave's first chunk and this lane's K offset
   const int xrow = (lane & 15) < MR ? (lane & 15) : 0;
-  const uint4* xl = xs + xrow * row16 + kc0 * (kChunkK / 8) + (lane >> 4);
-  const f32x4_t* cr = xcorr4 + kc0 * (kChunkK / kGroup);  // this wave's first group
+  const uint4* xl = xs + xrow * row16 + wave * (kChunkK / 8) + (lane >> 4);
+  const f32x4_t* cr = xcorr4 + wave * (kChunkK / kGroup);  // this wave's first group
 
   // One buffer descriptor per chunk (scalar arithmetic), so the per-lane
   // offsets stay four constant registers; a chunk at or past n has no
   // bytes in range and reads zeros.
   auto load_w = [&](int c) {
     const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc(wbase + (int64_t)c * kPairChunkBytes, c < n ? (uint32_t)kPairChunkBytes : 0u);
+        make_rsrc(wbase + (int64_t)c * kStride, c < n ? (uint32_t)kPairChunkBytes : 0u);
     WChunk w;
     w.q0 = bload16<kPolicyWeights>(wr, oq0);
     w.q1 = bload16<kPolicyWeights>(wr, oq1);
@@ -104,12 +107,12 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
     const uint32_t s1w[2] = {w.s1.x, w.s1.y};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16x8_t xv = as_bf16x8(xl[c * (kChunkK / 8) + 4 * j]);
+      const bf16x8_t xv = as_bf16x8(xl[c * kDecKSplit * (kChunkK / 8) + 4 * j]);
       const bf16x8_t b0 = dequant_u4_plus128(q0[j]);
       const bf16x8_t b1 = dequant_u4_plus128(q1[j]);
       const float g0 = f16_bits_to_f32((s0w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
       const float g1 = f16_bits_to_f32((s1w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-      const f32x4_t off = cr[c * (kChunkK / kGroup) + j];
+      const f32x4_t off = cr[c * kDecKSplit * (kChunkK / kGroup) + j];
       const f32x4_t t0 = mfma16x16x32(xv, b0, off);
       const f32x4_t t1 = mfma16x16x32(xv, b1, off);
 #pragma unroll
@@ -336,10 +339,20 @@ void fc2_decode_kernel(DecodeArgs d) {
   const int tile = blockIdx.x % ntiles;
   const int pair = tile >> 1, h = tile & 1;
   const int f = t * k + j;
+  const int row16 = I / 8;
+  const int ng = I / kGroup;
+  // The activation row does not depend on the routing: its loads go out
+  // before the wait for this slot's expert id (which the weight stream needs).
+  const uint4* src = reinterpret_cast<const uint4*>(a.act_in) + (int64_t)f * row16;
+  uint4 xs[ROWV > 0 ? ROWV : 1];
+  if constexpr (ROWV > 0) {
+#pragma unroll
+    for (int r = 0; r < ROWV; ++r) xs[r] = src[lane + 64 * r];
+  }
   const int ef = __builtin_amdgcn_readfirstlane(d.topk_ids[f]);
   const bool ok = ef >= 0 && ef < a.E;  // always, for ids from the routing kernels
   const int e = ok ? ef : 0;
-  const float wf = ok ? d.topk_weights[f] : 0.f;
+  const float wf = ok ? d.topk_weights[f] : 0.f;  // 0: an invalid id contributes nothing
 
   const int n = I / kChunkK;
   const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(H, I) +
@@ -347,9 +360,6 @@ void fc2_decode_kernel(DecodeArgs d) {
   // Only D row 0 (lanes 0..15) is used: lanes 16..63 read their scales out of
   // range (zeros, no memory access).
   const uint32_t oq = 16u * lane, os = lane < 16 ? kTileNibbleBytes + 8u * lane : kOutOfRange;
-  const int row16 = I / 8;
-  const int ng = I / kGroup;
-  const uint4* src = reinterpret_cast<const uint4*>(a.act_in) + (int64_t)f * row16;
   uint4* dst = xrows + j * row16;
   f32x4_t* corr = reinterpret_cast<f32x4_t*>(xrows + k * row16) + j * ng;
 
@@ -365,9 +375,6 @@ void fc2_decode_kernel(DecodeArgs d) {
   // Issue order: the activation row, then the first P2 weight chunks, so that
   // staging the row waits only for its own loads.
   if constexpr (ROWV > 0) {
-    uint4 xs[ROWV];
-#pragma unroll
-    for (int r = 0; r < ROWV; ++r) xs[r] = ok ? src[lane + 64 * r] : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < P2; ++s) load(s, s);
 #pragma unroll
@@ -379,7 +386,7 @@ void fc2_decode_kernel(DecodeArgs d) {
   } else {
     // row16 is a multiple of 4: a quad of lanes is wholly inside the row or past it
     for (int i = lane; i < row16; i += 64) {
-      const uint4 v = ok ? src[i] : make_uint4(0, 0, 0, 0);
+      const uint4 v = src[i];
       dst[i] = v;
       const float cg = group_corr_quad(v);
       if ((i & 3) == 0) corr[i >> 2] = f32x4_t{cg, cg, cg, cg};
@@ -387,7 +394,8 @@ void fc2_decode_kernel(DecodeArgs d) {
 #pragma unroll
     for (int s = 0; s < P2; ++s) load(s, s);
   }
-  __syncthreads();
+  // No workgroup barrier: each wave reads back only the row and corrections
+  // it staged itself, and a wave's LDS operations complete in order.
   // lane l reads K values 8*(l/16).. of each group; every A row is the token's
   // row (rows 1..15 of D are not used), so no lane needs a zero fill
   const uint4* xl = dst + (lane >> 4);
