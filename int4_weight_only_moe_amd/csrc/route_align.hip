@@ -24,6 +24,7 @@ constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kFusedMaxTokens = 16;
+constexpr int kIdsPerLane = 8;  // expert ids a lane loads at once in the grouping passes
 constexpr int kTopkWavesPerBlock = 4;
 
 template <int VPL>
@@ -38,18 +39,37 @@ __global__ __launch_bounds__(64 * kTopkWavesPerBlock) void topk_kernel(
 // Grouping by one workgroup of kAlignThreads threads.
 //   counts     histogram of the expert ids (LDS atomics: order-free);
 //   offsets    exclusive scan of the counts rounded up to block_m;
-//   placement  assignments are taken in chunks of kAlignThreads in ascending f;
-//              a lane's rank among equal experts of its wave comes from
-//              comparing against every lane of the wave in lane order, and
-//              earlier waves and chunks add their counts, so each expert's
-//              list is in ascending f without any order-dependent atomic.
+//   placement  each wave takes a contiguous range of f in ascending order;
+//              a lane's rank among equal experts of its 64-lane step is the
+//              number of lower lanes holding its expert (a ballot per bit of
+//              the expert id), and earlier waves and steps add their counts,
+//              so each expert's list is in ascending f without any
+//              order-dependent atomic.
 struct AlignShared {
   int cnt[kMaxExperts];
   int off[kMaxExperts + 1];
-  int run[kMaxExperts];
   int wave_tot[kAlignWaves];
   int wcnt[kAlignWaves][kMaxExperts];
 };
+
+// Lanes of the wave whose key equals this lane's, for keys below 2^nbits:
+// one ballot per key bit, each lane keeping the lanes that agree with it on
+// that bit, starting from the lanes in `live`. Wave-uniform control flow only.
+__device__ __forceinline__ uint64_t equal_key_lanes(int key, int nbits, uint64_t live) {
+  uint64_t m = live;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return m;
+}
+
+// Set bits of m in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 __device__ __forceinline__ void align_body(AlignShared& sh, const int32_t* __restrict__ ids, int MK, int E,
                            int block_m, int32_t* __restrict__ sorted_ids,
@@ -58,15 +78,36 @@ __device__ __forceinline__ void align_body(AlignShared& sh, const int32_t* __res
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < E) {
     sh.cnt[tid] = 0;
-    sh.run[tid] = 0;
     if (MK > 64) {
 #pragma unroll
       for (int w = 0; w < kAlignWaves; ++w) sh.wcnt[w][tid] = 0;
     }
   }
   __syncthreads();
-  for (int f = tid; f < MK; f += kAlignThreads) {
-    int e = ids[f];
+  // Wave w owns the contiguous assignment range [f0, f1) (placement below
+  // keeps ascending f inside it). The ids are read kIdsPerLane per lane at a
+  // time, all loads in flight before the first use; the pass counts both the
+  // expert totals and the wave's own per-expert counts.
+  const int seg = ((MK + kAlignWaves - 1) / kAlignWaves + 63) / 64 * 64;
+  const int f0 = wave * seg, f1 = (f0 + seg < MK) ? f0 + seg : MK;
+  if (MK > 64) {
+    for (int fb = f0; fb < f1; fb += 64 * kIdsPerLane) {
+      int ev[kIdsPerLane];
+#pragma unroll
+      for (int i = 0; i < kIdsPerLane; ++i) {
+        const int f = fb + 64 * i + lane;
+        ev[i] = f < f1 ? ids[f] : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < kIdsPerLane; ++i) {
+        if (ev[i] >= 0 && ev[i] < E) {
+          atomicAdd(&sh.cnt[ev[i]], 1);
+          atomicAdd(&sh.wcnt[wave][ev[i]], 1);
+        }
+      }
+    }
+  } else if (tid < MK) {
+    const int e = ids[tid];
     if (e >= 0 && e < E) atomicAdd(&sh.cnt[e], 1);
   }
   __syncthreads();
@@ -104,50 +145,53 @@ __device__ __forceinline__ void align_body(AlignShared& sh, const int32_t* __res
   }
 
   // stable placement
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
   if (MK <= 64) {
     // one wave's worth: rank among equal experts of the earlier lanes only
     if (wave == 0) {
-      const int e = (lane < MK) ? ids[lane] : -1;
-      int before = 0;
-#pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        const int ej = __builtin_amdgcn_readlane(e, j);
-        before += (j < lane && ej == e) ? 1 : 0;
-      }
-      if (e >= 0 && e < E) sorted_ids[sh.off[e] + before] = lane;
+      int e = (lane < MK) ? ids[lane] : -1;
+      e = (e >= E) ? -1 : e;
+      const uint64_t same = equal_key_lanes(e, nbits, __ballot(e >= 0));
+      if (e >= 0) sorted_ids[sh.off[e] + lanes_below(same)] = lane;
     }
     return;
   }
-  for (int base = 0; base < MK; base += kAlignThreads) {
-    const int f = base + tid;
-    int e = (f < MK) ? ids[f] : -1;
-    if (e >= E) e = -1;
-    int before = 0, tot = 0;
+  // The waves' per-expert counts (counted with the totals above) become,
+  // by a scan over the waves per expert, each wave's first position in the
+  // expert's list; each wave then walks its range 64 lanes at a time, in
+  // order, placing each assignment at its wave's running position plus its
+  // rank among the equal experts of earlier lanes, and advances the running
+  // positions.
+  if (tid < E) {
+    int run = sh.off[tid];
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const int c = sh.wcnt[w][tid];
+      sh.wcnt[w][tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int fb = f0; fb < f1; fb += 64 * kIdsPerLane) {
+    int ev[kIdsPerLane];
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      const int m = (ej == e) ? 1 : 0;
-      tot += m;
-      before += (j < lane) ? m : 0;
+    for (int i = 0; i < kIdsPerLane; ++i) {
+      const int f = fb + 64 * i + lane;
+      const int e = f < f1 ? ids[f] : -1;
+      ev[i] = (e >= E) ? -1 : e;
     }
-    if (e >= 0 && before == tot - 1) sh.wcnt[wave][e] = tot;
-    __syncthreads();
-    if (e >= 0) {
-      int pos = sh.off[e] + sh.run[e] + before;
-      for (int w = 0; w < wave; ++w) pos += sh.wcnt[w][e];
-      sorted_ids[pos] = f;
-    }
-    if (base + kAlignThreads >= MK) break;  // last chunk: nothing to carry
-    __syncthreads();
-    if (tid < E) {
-      int s = 0;
-      for (int w = 0; w < kAlignWaves; ++w) {
-        s += sh.wcnt[w][tid];
-        sh.wcnt[w][tid] = 0;
+#pragma unroll
+    for (int i = 0; i < kIdsPerLane; ++i) {
+      const int e = ev[i];
+      const uint64_t same = equal_key_lanes(e, nbits, __ballot(e >= 0));
+      const int before = lanes_below(same), tot = __builtin_popcountll(same);
+      if (e >= 0) {
+        // every lane reads the running position before the group's last lane
+        // advances it (one wave: its LDS operations complete in order)
+        const int base = sh.wcnt[wave][e];
+        sorted_ids[base + before] = fb + 64 * i + lane;
+        if (before == tot - 1) sh.wcnt[wave][e] = base + tot;
       }
-      sh.run[tid] += s;
     }
-    __syncthreads();
   }
 }
 
