@@ -120,8 +120,9 @@ class HipEvent:
         return t.value
 
     def __del__(self):
-        if HipEvent._hip is not None and self.ev:
-            HipEvent._hip.hipEventDestroy(self.ev)
+        hip = getattr(type(self), "_hip", None)  # module globals may be gone at interpreter exit
+        if hip is not None and self.ev:
+            hip.hipEventDestroy(self.ev)
 
 
 class Bench:

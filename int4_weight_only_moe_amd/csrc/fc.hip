@@ -106,22 +106,15 @@ template <int S, bool kFc1, int kPolicy>
 __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const int pair, const int (&frow)[S],
                                              const int sf, const bool stager, const int srow, const int svec,
                                              uint4 (&xt)[2][16 * S][kRowPad], f32x4_t (&xs4)[2][4][4 * S]) {
+  // A deeper ring does not fit: at 4 chunks the compiler spills, and a
+  // scratch reload inside the loop waits for every weight load in flight.
   constexpr int P = kWideP;
   const int lane = threadIdx.x & 63;
   const int K = kFc1 ? a.H : a.I;
   const int N = kFc1 ? 2 * a.I : a.H;
   const int MK = a.M * a.k;
 
-  bool sact[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) sact[s] = __builtin_amdgcn_readfirstlane(frow[s]) < MK;
-
   const int n = K / kChunkK;
-  const int rows_total = kFc1 ? a.M : MK;
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.act_in, (uint32_t)rows_total * (uint32_t)K * 2u);
-  const bool svalid = stager && sf >= 0 && sf < MK;
-  const uint32_t soff = svalid ? ((uint32_t)(kFc1 ? sf / a.k : sf) * (uint32_t)K + 8u * svec) * 2u : kOutOfRange;
-
   const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(N, K) + (int64_t)pair * n * kPairChunkBytes;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)n * kPairChunkBytes);
   const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
@@ -135,6 +128,32 @@ __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const
     w.s1 = bload8<kPolicy>(wr, base + os1);
     return w;
   };
+  // The weight stream goes out first: it does not wait for the row ids that
+  // the activation loads and the sub-tile flags need (the scheduling barrier
+  // keeps those waits below the loads).
+  WChunk wb[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) wb[j] = load_w(j);
+  __builtin_amdgcn_sched_barrier(0);
+  // The row ids pass through empty volatile asm statements here: otherwise
+  // the compiler hoists their uses (the same in both cache-policy copies of
+  // this body) above the copies' branch, and so above the weight loads.
+  int sfv = sf;
+  asm volatile("" : "+v"(sfv));
+  int frv[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    frv[s] = frow[s];
+    asm volatile("" : "+v"(frv[s]));
+  }
+
+  bool sact[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) sact[s] = __builtin_amdgcn_readfirstlane(frv[s]) < MK;
+  const int rows_total = kFc1 ? a.M : MK;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.act_in, (uint32_t)rows_total * (uint32_t)K * 2u);
+  const bool svalid = stager && sfv >= 0 && sfv < MK;
+  const uint32_t soff = svalid ? ((uint32_t)(kFc1 ? sfv / a.k : sfv) * (uint32_t)K + 8u * svec) * 2u : kOutOfRange;
   auto load_x = [&](int c) { return bload16(xr, (c < n) ? soff + (uint32_t)c * (kChunkK * 2) : kOutOfRange); };
   // store one staged vector and its share of the group sum (4 vectors = 1 group)
   auto store_x = [&](uint4 v, int slot) {
@@ -150,13 +169,9 @@ __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const
     acc0[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     acc1[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  WChunk wb[P];
   uint4 xg[P];
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    xg[j] = load_x(j);
-    wb[j] = load_w(j);
-  }
+  for (int j = 0; j < P; ++j) xg[j] = load_x(j);
   store_x(xg[0], 0);
   __syncthreads();
 
@@ -201,7 +216,7 @@ __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const
       }
     }
   }
-  fc_epilogue<S, kFc1>(a, pair, frow, sact, acc0, acc1, lane);
+  fc_epilogue<S, kFc1>(a, pair, frv, sact, acc0, acc1, lane);
 }
 
 
@@ -232,6 +247,9 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
   const int blk = (gi / npg) * kXcds + xcd;
   const int pair = (gi % npg) * kWideNP + wave;
   if ((int64_t)blk * BM >= a.cap) return;
+  // All of the block's metadata is read in one round trip (the block list
+  // entries of the neighbours too, for the cache policy below) before any
+  // of it is used.
   const int32_t* rows = a.sorted_ids + (int64_t)blk * BM;
   int frow[S];
 #pragma unroll
@@ -241,14 +259,15 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
   const int sf = stager ? rows[srow] : MK;
   const int npp = __builtin_amdgcn_readfirstlane(*a.npp);
   const int e = __builtin_amdgcn_readfirstlane(a.block_expert[blk]);
+  const int e_prev = blk > 0 ? __builtin_amdgcn_readfirstlane(a.block_expert[blk - 1]) : -1;
+  const int e_next = (int64_t)(blk + 1) * BM < a.cap ? __builtin_amdgcn_readfirstlane(a.block_expert[blk + 1]) : -1;
   if (blk * BM >= npp) return;
   if (e < 0 || e >= a.E) return;
 
   // Weights are streamed non-temporally (read once per call) unless the
   // expert has more than one block: then its other blocks re-read them and
   // they are kept in the caches.
-  const bool reuse = (blk > 0 && a.block_expert[blk - 1] == e) ||
-                     ((blk + 1) * BM < npp && a.block_expert[blk + 1] == e);
+  const bool reuse = e_prev == e || ((blk + 1) * BM < npp && e_next == e);
   if (__builtin_amdgcn_readfirstlane((int)reuse))
     fc_wide_body<S, kFc1, kPolicyDefault>(a, e, pair, frow, sf, stager, srow, svec, xt, xs4);
   else

@@ -15,7 +15,9 @@
 //   * a plan kernel cuts each expert's row range (block_m-padded, from
 //     moe_route_align) into tiles of up to 64 rows: a tile starts at every
 //     expert change and at every 64-row boundary of the padded list, so an
-//     expert holding hundreds of rows gets several 64-row tiles;
+//     expert holding hundreds of rows gets several 64-row tiles; a tile
+//     counts only the 16-row sub-tiles that hold a row (padding is not
+//     multiplied);
 //   * a workgroup = one tile x 8 tile pairs (one per wave, full K); the
 //     tile's activation chunk (up to 64 rows x 128 channels) is staged once
 //     in a padded LDS double buffer and read by all 8 waves; two workgroups
@@ -50,7 +52,8 @@ constexpr int kTXcds = 8;
 // ---------------------------------------------------------------------------
 // Plan: one workgroup turns the block list into the tile list.
 __global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restrict__ block_expert,
-                                                        const int32_t* __restrict__ npp_p, int block_m,
+                                                        const int32_t* __restrict__ sorted_ids,
+                                                        const int32_t* __restrict__ npp_p, int block_m, int MK,
                                                         int max_tiles, int2* __restrict__ tiles,
                                                         int32_t* __restrict__ ntiles_out) {
   __shared__ int wave_cnt[16];
@@ -77,7 +80,10 @@ __global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restri
       // the tile runs to the next full-tile boundary or the end of the expert
       int nb = 1;
       while (nb < bpt - b % bpt && b + nb < nblk && block_expert[b + nb] == e) ++nb;
-      const int nsub = nb * block_m / kTileRows;
+      // sub-tiles that hold a row: an expert's padding sits at the end of its
+      // range, so they are a prefix of the tile's
+      int nsub = nb * block_m / kTileRows;
+      while (nsub > 1 && sorted_ids[b * block_m + (nsub - 1) * kTileRows] >= MK) --nsub;
       const bool reuse = (b > 0 && block_expert[b - 1] == e) || (b + nb < nblk && block_expert[b + nb] == e);
       tiles[t] = make_int2(b * block_m, nsub | (reuse ? kTileReuseBit : 0) | (e << kTileExpertShift));
     }
@@ -110,14 +116,27 @@ __device__ __forceinline__ void fc_tile_body(const FcArgs& a, const int e, const
   const int n = K / kChunkK;
   const int32_t* rows = a.sorted_ids + row0;
 
-  // This lane's row of every sub-tile (sub-tiles past nsub have none).
-  int frow[S];
-  bool sact[S];
+  const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(N, K) + (int64_t)pair * n * kPairChunkBytes;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)n * kPairChunkBytes);
+  const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
+  const uint32_t os0 = kTileNibbleBytes + 8u * (lane & 15), os1 = kTileBytes + kTileNibbleBytes + 8u * (lane & 15);
+  auto load_w = [&](int c) {
+    const uint32_t base = (uint32_t)c * kPairChunkBytes;  // past the K range: zeros
+    WChunk w;
+    w.q0 = bload16<kPolicy>(wr, base + oq0);
+    w.q1 = bload16<kPolicy>(wr, base + oq1);
+    w.s0 = bload8<kPolicy>(wr, base + os0);
+    w.s1 = bload8<kPolicy>(wr, base + os1);
+    return w;
+  };
+
+  // The weight stream goes out first: it does not wait for the row ids that
+  // the activation loads need (the scheduling barrier keeps those waits
+  // below the loads).
+  WChunk wb[P];
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    sact[s] = s < nsub;
-    frow[s] = sact[s] ? rows[16 * s + (lane & 15)] : MK;
-  }
+  for (int j = 0; j < P; ++j) wb[j] = load_w(j);
+  __builtin_amdgcn_sched_barrier(0);
 
   // Staging: item i = (row i / 16, vector i % 16) of the chunk.
   const int rows_total = kFc1 ? a.M : MK;
@@ -147,20 +166,6 @@ __device__ __forceinline__ void fc_tile_body(const FcArgs& a, const int e, const
     }
   };
 
-  const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(N, K) + (int64_t)pair * n * kPairChunkBytes;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)n * kPairChunkBytes);
-  const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
-  const uint32_t os0 = kTileNibbleBytes + 8u * (lane & 15), os1 = kTileBytes + kTileNibbleBytes + 8u * (lane & 15);
-  auto load_w = [&](int c) {
-    const uint32_t base = (uint32_t)c * kPairChunkBytes;  // past the K range: zeros
-    WChunk w;
-    w.q0 = bload16<kPolicy>(wr, base + oq0);
-    w.q1 = bload16<kPolicy>(wr, base + oq1);
-    w.s0 = bload8<kPolicy>(wr, base + os0);
-    w.s1 = bload8<kPolicy>(wr, base + os1);
-    return w;
-  };
-
   const bf16x8_t neg136 = as_bf16x8(make_uint4(kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair));
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4_t acc0[S], acc1[S];
@@ -169,9 +174,6 @@ __device__ __forceinline__ void fc_tile_body(const FcArgs& a, const int e, const
     acc0[s] = zero4;
     acc1[s] = zero4;
   }
-  WChunk wb[P];
-#pragma unroll
-  for (int j = 0; j < P; ++j) wb[j] = load_w(j);
   // Activation chunks are loaded kXD steps before they are stored to LDS
   // (kXD register sets alternating with the step parity; one for 4
   // sub-tiles, whose accumulators need the registers).
@@ -242,6 +244,15 @@ __device__ __forceinline__ void fc_tile_body(const FcArgs& a, const int e, const
       }
     }
   }
+  // This lane's row of every sub-tile (sub-tiles past nsub have none), read
+  // here rather than kept live across the main loop.
+  int frow[S];
+  bool sact[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    sact[s] = s < nsub;
+    frow[s] = sact[s] ? rows[16 * s + (lane & 15)] : MK;
+  }
   fc_epilogue<S, kFc1>(a, pair, frow, sact, acc0, acc1, lane);
 }
 
@@ -274,9 +285,14 @@ __global__ __launch_bounds__(64 * kTW) __attribute__((amdgpu_waves_per_eu(4))) v
   const int xcd = blockIdx.x % kTXcds, gi = blockIdx.x / kTXcds;
   const int tile = (gi / npg) * kTXcds + xcd;
   const int pair = (gi % npg) * kTW + wave;
-  const int ntiles = __builtin_amdgcn_readfirstlane(*a.ntiles);
-  if (tile >= ntiles) return;
+  // the table has max_tiles entries (those past ntiles are not used): the
+  // entry and the count are read in one round trip (the empty asm needs both
+  // before the check, so the entry's load is not sunk below it)
+  if (tile >= a.max_tiles) return;
   const int2 te = a.tiles[tile];
+  const int ntiles = *a.ntiles;
+  asm volatile("" ::"s"(te.x), "s"(te.y), "s"(ntiles));
+  if (tile >= ntiles) return;
   const int row0 = __builtin_amdgcn_readfirstlane(te.x);
   const int meta = __builtin_amdgcn_readfirstlane(te.y);
   const int nsub = meta & kTileNsubMask;
@@ -306,8 +322,8 @@ bool tile_path_supported(int64_t H, int64_t I) {
 }
 
 hipError_t launch_tile_plan(const FcArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, stream, a.block_expert, a.npp, a.block_m,
-                     a.max_tiles, a.tiles, a.ntiles);
+  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, stream, a.block_expert, a.sorted_ids, a.npp,
+                     a.block_m, a.M * a.k, a.max_tiles, a.tiles, a.ntiles);
   return hipGetLastError();
 }
 
