@@ -16,9 +16,9 @@ through R copies of the layer's weights at different addresses (a model with R
 MoE layers); each step reads copy i % R.
 
 Timing: W untimed warm-up steps, then K steps bracketed by
-torch.cuda.synchronize(), queued behind a GPU spin so that they run back to
-back as under a HIP graph; HIP events on the launch stream bracket the K
-steps; K more steps carry events around every FC1 launch (for the roofline
+torch.cuda.synchronize(), queued behind a GPU spin of device copies (busy, so
+the clock stays up) and max(10, K/4) untimed steps so that they run back to back as
+under a HIP graph; HIP events on the launch stream bracket the K steps; K more steps carry events around every FC1 launch (for the roofline
 figure). The same K steps
 replayed from one captured HIP graph are reported as context. The CPU oracle is timed on a bounded sample of
 the same workload (cpu_baseline).
@@ -49,11 +49,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_k26_m1_traffic.json")
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--replicas", type=int, default=8)
     p.add_argument("--workload", default=HEADLINE)
-    p.add_argument("--sweep-steps", type=int, default=30)
+    p.add_argument("--sweep-steps", type=int, default=200)
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy", action="store_true",
@@ -127,6 +127,7 @@ class HipEvent:
 
 class Bench:
     def __init__(self, replicas: int):
+        self._spin_bufs = None
         import torch
         import int4_weight_only_moe_amd as moe
         import workloads as wl
@@ -196,6 +197,25 @@ class Bench:
         self.moe.layer(c["logits"], c["x"], c["rb"], s.I, layer[0], layer[1], workspace=c["ws"], out=c["out"],
                        stage_events=None if ev is None else (ev[0].handle, ev[1].handle))
 
+    def spin(self, seconds):
+        """Keep the GPU busy for about `seconds` ahead of the host: device
+        copies of 512 MB (each far more GPU time than host time to launch).
+        An idle wait would let the clock drop, and the first timed steps
+        would then run slower than in steady operation."""
+        torch = self.torch
+        if self._spin_bufs is None:
+            self._spin_bufs = (torch.empty(1 << 29, dtype=torch.uint8, device="cuda"),
+                               torch.empty(1 << 29, dtype=torch.uint8, device="cuda"))
+            self._spin_bufs[0].fill_(1)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for _ in range(8):
+                self._spin_bufs[1].copy_(self._spin_bufs[0])
+            torch.cuda.synchronize()
+            self._spin_copy_s = (time.perf_counter() - t) / 8
+        for _ in range(max(1, int(seconds / self._spin_copy_s))):
+            self._spin_bufs[1].copy_(self._spin_bufs[0])
+
     def run(self, name, steps, warmup, replicas):
         """W eager warm-up steps, then K timed steps launched back to back, then
         K more steps with HIP events on the FC1 stage.
@@ -204,6 +224,9 @@ class Bench:
         it at small M, so the timed steps are queued behind a GPU spin of known
         length: by the time the GPU reaches the start event, every step is
         already in the queue and runs without host gaps (as under a HIP graph).
+        The spin is device copies (an idle wait lets the clock drop), and
+        untimed steps between it and the start event bring the pipeline into
+        its steady state.
         The first K steps carry no instrumentation (they give the per-call
         time); the second K steps each record a pair of events around their
         FC1 kernel (the kernel's own start and end timestamps) for the roofline
@@ -218,20 +241,33 @@ class Bench:
             self.step(c, self.layers[i % R])
         host_per_step = (time.perf_counter() - h0) / max(warmup, 1)
         torch.cuda.synchronize()
-        spin_s = min(2.0, 2.0 * host_per_step * steps + 2e-3)
+        # Untimed steps queued between the spin and the start event: the
+        # timed region starts in steady operation.
+        ramp = max(10, steps // 4)
+        # generous cover: a host that falls behind the GPU would put launch
+        # gaps into the timed region (checked below)
+        spin_s = min(4.0, 4.0 * host_per_step * (steps + ramp) + 5e-3)
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        torch.cuda._sleep(int(spin_s * 2.4e9))
+        self.spin(spin_s)
+        for i in range(ramp):
+            self.step(c, self.layers[i % R])
         start.record()
         for i in range(steps):
             self.step(c, self.layers[i % R])
         stop.record()
+        enqueue_s = time.perf_counter() - t0
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        if enqueue_s > spin_s:
+            print(f"# warning: {name}: enqueueing took {enqueue_s * 1e3:.1f} ms, longer than the "
+                  f"{spin_s * 1e3:.1f} ms spin; the timed steps may include host gaps", file=sys.stderr)
         total_ms = start.elapsed_time(stop)
         evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
-        torch.cuda._sleep(int(spin_s * 2.4e9))
+        self.spin(spin_s)
+        for i in range(ramp):
+            self.step(c, self.layers[i % R])
         for i in range(steps):
             self.step(c, self.layers[i % R], evs[i])
         torch.cuda.synchronize()
