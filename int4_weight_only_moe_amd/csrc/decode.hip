@@ -16,10 +16,14 @@
 //                      routing and grouping outputs (experts ascending) in
 //                      the format moe_route_align produces.
 //   fc2_decode_kernel  output-stationary FC2: one workgroup per (token,
-//                      16-column tile of the output), one wave per routing
-//                      slot j streaming the W2 tile of expert ids[t, j]; the k
-//                      slot results meet in LDS and are summed in slot order
-//                      with their routing weights, then rounded once to bf16.
+//                      32-column tile pair of the output; for top-k > 8 one
+//                      16-column tile), one wave per (routing slot j, tile)
+//                      streaming the W2 tile of expert ids[t, j]; the k slot
+//                      results of a tile meet in LDS and are summed in slot
+//                      order with their routing weights, then rounded once to
+//                      bf16. A pair per workgroup reads whole 2304-byte
+//                      chunks, and at M = 1 gives 224 equal workgroups rather
+//                      than 448 on 256 CUs.
 //                      No atomics, no accumulator to clear, no finalize
 //                      kernel, and the float result is deterministic.
 // Each expert is read once per token that routes to it; with M <= 4 tokens
@@ -304,40 +308,49 @@ void fc1_decode_kernel(DecodeArgs d) {
 }
 
 // One 16-row tile of a pair, for one activation row (D row 0, lanes 0..15):
-// per group, one MFMA whose accumulator input is the row's -136 * (group
-// sum) (replicated over the four D rows a lane holds), scaled into the sum.
-__device__ __forceinline__ void mma_chunk_tile(uint4 q, uint2 sc, const uint4 (&xa)[4], const f32x4_t (&corr)[4],
-                                               float& acc) {
+// per group, one MFMA of the row with the codes (q + 136), all four issued
+// back to back; then each group's -136 * (group sum) correction (cr, one
+// float per group, the same for every lane) is added and the sum scaled
+// into that group's own running sum (no dependence between the groups).
+__device__ __forceinline__ void mma_chunk_tile(uint4 q, uint2 sc, const uint4 (&xa)[4], const float4 cr,
+                                               float (&accj)[4]) {
   const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
   const uint32_t sw[2] = {sc.x, sc.y};
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t t[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t[j] = mfma16x16x32(as_bf16x8(xa[j]), dequant_u4_plus128(qq[j]), zero4);
+  const float crj[4] = {cr.x, cr.y, cr.z, cr.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const bf16x8_t b = dequant_u4_plus128(qq[j]);
     const float g = f16_bits_to_f32((sw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-    const bf16x8_t xv = as_bf16x8(xa[j]);
-    const f32x4_t t = mfma16x16x32(xv, b, corr[j]);
-    acc = __builtin_fmaf(t[0], g, acc);
+    accj[j] = __builtin_fmaf(t[j][0] + crj[j], g, accj[j]);
   }
 }
 
 // ROWV: 16-byte vectors of the activation row each lane stages, when the
 // launcher knows it (I = 64 * 8 * ROWV); 0 = any I (staged by a loop).
-template <int ROWV, int KW>  // KW: waves per workgroup the launch bounds allow (>= top_k)
+// TPW = 16-column tiles per workgroup: 2 = both tiles of a pair (waves
+// w < k take tile 0, the others tile 1), so that a workgroup reads the pair's
+// chunks whole (2304 contiguous bytes) rather than every other 1152 bytes.
+template <int ROWV, int KW, int TPW>  // KW: waves per workgroup the launch bounds allow (>= TPW * top_k)
 __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(4)))
 void fc2_decode_kernel(DecodeArgs d) {
-  // Each wave's activation row (I bf16) is staged in LDS once, with its
-  // -136 * (group sum) corrections; per chunk the A operand comes from LDS, so
-  // registers hold only the weight stream.
-  extern __shared__ uint4 xrows[];  // [k][I / 8], then the corrections [k][I / 32] (x4)
+  // The activation row (I bf16) of each routing slot is staged in LDS once,
+  // with its -136 * (group sum) corrections; per chunk the A operand comes
+  // from LDS, so registers hold only the weight stream.
+  extern __shared__ uint4 xrows[];  // [k][I / 8], then the corrections [k][I / 32] (one float each)
   __shared__ float part[KW][16];
   const int lane = threadIdx.x & 63;
-  const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // routing slot
   const FcArgs& a = d.fc;
   const int H = a.H, I = a.I, k = a.k;
-  const int ntiles = H / 16;
-  const int t = blockIdx.x / ntiles;
-  const int tile = blockIdx.x % ntiles;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = w % k, hh = w / k;  // routing slot, tile within the workgroup
+  const int ngrp = H / (16 * TPW);
+  const int t = blockIdx.x / ngrp;
+  const int tile = (blockIdx.x % ngrp) * TPW + hh;
   const int pair = tile >> 1, h = tile & 1;
+  const bool stager = hh == 0;  // one wave per slot stages the row
   const int f = t * k + j;
   const int row16 = I / 8;
   const int ng = I / kGroup;
@@ -346,8 +359,10 @@ void fc2_decode_kernel(DecodeArgs d) {
   const uint4* src = reinterpret_cast<const uint4*>(a.act_in) + (int64_t)f * row16;
   uint4 xs[ROWV > 0 ? ROWV : 1];
   if constexpr (ROWV > 0) {
+    if (stager) {
 #pragma unroll
-    for (int r = 0; r < ROWV; ++r) xs[r] = src[lane + 64 * r];
+      for (int r = 0; r < ROWV; ++r) xs[r] = src[lane + 64 * r];
+    }
   }
   const int ef = __builtin_amdgcn_readfirstlane(d.topk_ids[f]);
   const bool ok = ef >= 0 && ef < a.E;  // always, for ids from the routing kernels
@@ -361,9 +376,9 @@ void fc2_decode_kernel(DecodeArgs d) {
   // range (zeros, no memory access).
   const uint32_t oq = 16u * lane, os = lane < 16 ? kTileNibbleBytes + 8u * lane : kOutOfRange;
   uint4* dst = xrows + j * row16;
-  f32x4_t* corr = reinterpret_cast<f32x4_t*>(xrows + k * row16) + j * ng;
+  float* corr = reinterpret_cast<float*>(xrows + k * row16) + j * ng;
 
-  constexpr int P2 = KW > 8 ? 4 : 6;
+  constexpr int P2 = KW > 8 ? 2 : 6;  // chunks in flight per wave: with 16 waves, 2 measured best (4: +3 %, 6: +13 %)
   uint4 qb[P2];
   uint2 sb[P2];
   auto load = [&](int slot, int c) {  // a chunk past the K range has no bytes in range: zeros
@@ -377,56 +392,74 @@ void fc2_decode_kernel(DecodeArgs d) {
   if constexpr (ROWV > 0) {
 #pragma unroll
     for (int s = 0; s < P2; ++s) load(s, s);
+    if (stager) {
 #pragma unroll
-    for (int r = 0; r < ROWV; ++r) {
-      dst[lane + 64 * r] = xs[r];
-      const float cg = group_corr_quad(xs[r]);
-      if ((lane & 3) == 0) corr[(lane + 64 * r) >> 2] = f32x4_t{cg, cg, cg, cg};
+      for (int r = 0; r < ROWV; ++r) {
+        dst[lane + 64 * r] = xs[r];
+        const float cg = group_corr_quad(xs[r]);
+        if ((lane & 3) == 0) corr[(lane + 64 * r) >> 2] = cg;
+      }
     }
   } else {
-    // row16 is a multiple of 4: a quad of lanes is wholly inside the row or past it
-    for (int i = lane; i < row16; i += 64) {
-      const uint4 v = src[i];
-      dst[i] = v;
-      const float cg = group_corr_quad(v);
-      if ((i & 3) == 0) corr[i >> 2] = f32x4_t{cg, cg, cg, cg};
+    if (stager) {
+      // row16 is a multiple of 4: a quad of lanes is wholly inside the row or past it
+      for (int i = lane; i < row16; i += 64) {
+        const uint4 v = src[i];
+        dst[i] = v;
+        const float cg = group_corr_quad(v);
+        if ((i & 3) == 0) corr[i >> 2] = cg;
+      }
     }
 #pragma unroll
     for (int s = 0; s < P2; ++s) load(s, s);
   }
-  // No workgroup barrier: each wave reads back only the row and corrections
-  // it staged itself, and a wave's LDS operations complete in order.
+  // With one tile per workgroup each wave reads back only the row it staged
+  // itself (a wave's LDS operations complete in order): no barrier. With two,
+  // the second tile's waves read rows the first tile's waves staged.
+  if constexpr (TPW > 1) __syncthreads();
   // lane l reads K values 8*(l/16).. of each group; every A row is the token's
   // row (rows 1..15 of D are not used), so no lane needs a zero fill
   const uint4* xl = dst + (lane >> 4);
 
-  float acc = 0.f;
+  // The LDS operands of chunk c + 1 are read before chunk c is computed
+  // (the last chunk re-reads its own: no branch, no read past the row).
+  const float4* corr4 = reinterpret_cast<const float4*>(corr);  // 4 groups = one chunk
+  uint4 xn[4];
+  float4 crn;
+  auto lds_load = [&](int cc) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) xn[g] = xl[cc * (kChunkK / 8) + 4 * g];
+    crn = corr4[cc];
+  };
+  lds_load(0);
+  float accj[4] = {0.f, 0.f, 0.f, 0.f};
   // A loop, not straight-line code: unrolled, the scheduler hoists every
   // chunk's LDS reads and spills; looped, the memory waits stay exact because
   // the only loads in flight are the weight ring's.
   for (int c = 0; c < n; c += P2) {
 #pragma unroll
     for (int s = 0; s < P2; ++s) {
-      if (c + s < n) {
+      const int cc = c + s;
+      if (cc < n) {
         uint4 xa[4];
-        f32x4_t cg[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          xa[g] = xl[(c + s) * (kChunkK / 8) + 4 * g];
-          cg[g] = corr[(c + s) * (kChunkK / kGroup) + g];
-        }
-        mma_chunk_tile(qb[s], sb[s], xa, cg, acc);
+        for (int g = 0; g < 4; ++g) xa[g] = xn[g];
+        const float4 cr = crn;
+        lds_load(cc + 1 < n ? cc + 1 : cc);
+        mma_chunk_tile(qb[s], sb[s], xa, cr, accj);
       }
-      load(s, c + s + P2);
+      load(s, cc + P2);
     }
   }
+  const float acc = (accj[0] + accj[1]) + (accj[2] + accj[3]);
   // D row 0 (the token) sits in lanes 0..15, element 0
-  if (lane < 16) part[j][lane] = wf * acc;
+  if (lane < 16) part[w][lane] = wf * acc;
   __syncthreads();
-  if (threadIdx.x < 16) {
+  if (threadIdx.x < 16 * TPW) {
+    const int th = threadIdx.x >> 4, col = threadIdx.x & 15;
     float s = 0.f;
-    for (int q = 0; q < k; ++q) s += part[q][threadIdx.x];
-    a.out[(int64_t)t * H + 32 * pair + 16 * h + threadIdx.x] = (uint16_t)f32_to_bf16_bits(s);
+    for (int q = 0; q < k; ++q) s += part[th * k + q][col];
+    a.out[(int64_t)t * H + 16 * ((blockIdx.x % ngrp) * TPW + th) + col] = (uint16_t)f32_to_bf16_bits(s);
   }
 }
 
@@ -460,14 +493,20 @@ hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t
   DecodeArgs d2 = d;
   d2.fc.act_in = d.fc.act_out;
   d2.fc.wpacked = d.w2;
-  const unsigned grid2 = (unsigned)(M * (d.fc.H / 16));
   const bool i2048 = d.fc.I == 2048;  // the 384-expert layer: 4 row vectors per lane
   const size_t lds = (size_t)decode_fc2_lds_bytes(d.fc.I, k);  // the k activation rows + corrections
-  if (k <= 8) {
-    if (i2048) fc2_decode_kernel<4, 8><<<grid2, 64 * k, lds, stream>>>(d2);
-    else fc2_decode_kernel<0, 8><<<grid2, 64 * k, lds, stream>>>(d2);
+  if (k <= 8) {  // a whole pair per workgroup: 2k <= 16 waves (measured 12 % faster than one tile)
+    const unsigned grid2 = (unsigned)(M * (d.fc.H / 32));
+    if (i2048) fc2_decode_kernel<4, 16, 2><<<grid2, 128 * k, lds, stream>>>(d2);
+    else fc2_decode_kernel<0, 16, 2><<<grid2, 128 * k, lds, stream>>>(d2);
   } else {
-    fc2_decode_kernel<0, kMaxTopK><<<grid2, 64 * k, lds, stream>>>(d2);
+    const unsigned grid2 = (unsigned)(M * (d.fc.H / 16));
+    if (k <= 8) {
+      if (i2048) fc2_decode_kernel<4, 8, 1><<<grid2, 64 * k, lds, stream>>>(d2);
+      else fc2_decode_kernel<0, 8, 1><<<grid2, 64 * k, lds, stream>>>(d2);
+    } else {
+      fc2_decode_kernel<0, kMaxTopK, 1><<<grid2, 64 * k, lds, stream>>>(d2);
+    }
   }
   return hipGetLastError();
 }

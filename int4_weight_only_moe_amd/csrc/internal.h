@@ -111,7 +111,7 @@ constexpr int kDecodeMaxAssign = 64;  // M * k
 // row (the value replicated, the accumulator input of one MFMA).
 constexpr int64_t kDecodeMaxStagedBytes = 64 * 1024;
 inline int64_t decode_fc1_lds_bytes(int64_t M, int64_t H) { return M * (H / 8 + 1) * 16 + (H / 32) * 16; }
-inline int64_t decode_fc2_lds_bytes(int64_t I, int64_t k) { return k * (I * 2 + (I / 32) * 16); }
+inline int64_t decode_fc2_lds_bytes(int64_t I, int64_t k) { return k * (I * 2 + (I / 32) * 4); }
 inline bool decode_path_fits(int64_t M, int64_t H, int64_t I, int64_t k) {
   return M >= 1 && M <= kDecodeMaxTokens && M * k <= kDecodeMaxAssign &&
          decode_fc1_lds_bytes(M, H) <= kDecodeMaxStagedBytes && decode_fc2_lds_bytes(I, k) <= kDecodeMaxStagedBytes;

@@ -124,6 +124,7 @@ K26_SAMPLES = {
     "k26_m9": [0, 4, 8],
     "k26_m90": [0, 57, 89],
     "k26_m256": [0, 255],
+    "k26_m512": [0, 300, 511],
     "k26_m1024": [0, 700, 1023],
     "k26_m1024_skew": [0, 1023],
 }
