@@ -60,10 +60,10 @@ struct SmallRoute {
 // -136 * (group sum) of the four token rows (xcorr4[group] = one float per
 // token, zero past M), so that every MFMA is a product with the weights.
 // tokf: lane r < MR holds the assignment f of token r to expert e, or -1.
-template <int MR, int NCH>
+template <int MR, int NCH, typename Pre>
 __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4* __restrict__ xs, int row16,
                                                 const f32x4_t* __restrict__ xcorr4, const int e, const int pair,
-                                                const int tokf, const int wave, const int lane) {
+                                                const int tokf, const int wave, const int lane, Pre&& pre) {
   const FcArgs& a = d.fc;
   const int H = a.H, I = a.I;
   const int nkc = H / kChunkK;
@@ -130,6 +130,7 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
   WChunk wb[P];
 #pragma unroll
   for (int j = 0; j < P; ++j) wb[j] = load_w(j);
+  pre();  // work that may overlap the first weight loads (it must leave xs staged)
   if constexpr (NCH > 0) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -215,96 +216,126 @@ void fc1_decode_kernel(DecodeArgs d) {
       }
   }
 
-  if (wave < M) topk_token<VPL>(d.logits, wave, E, k, sh.ids, sh.w);
+  // Staging of the rows and their group corrections, then a barrier.
+  auto stage = [&]() {
+    // Stage the rows and their group corrections: the 4 vectors of a group sit
+    // in 4 consecutive threads (hv and the block size are multiples of 4, so a
+    // quad is either wholly inside a row or wholly past its end).
+    if constexpr (kEarly) {
+  #pragma unroll
+      for (int r = 0; r < MR; ++r)
+  #pragma unroll
+        for (int v = 0; v < kXPerThread; ++v) {
+          const int i = threadIdx.x + v * 64 * kDecKSplit;
+          const float corr = group_corr_quad(xr[r][v]);
+          if (i < hv) {
+            xs[r * row16 + i] = xr[r][v];
+            if ((i & 3) == 0) xcorr[4 * (i >> 2) + r] = corr;
+          }
+        }
+    } else {
+      for (int i = threadIdx.x; i < M * hv; i += blockDim.x) {
+        const uint4 v = xg[i];
+        const int r = i / hv, c = i % hv;
+        xs[r * row16 + c] = v;
+        const float corr = group_corr_quad(v);
+        if ((c & 3) == 0) xcorr[4 * (c >> 2) + r] = corr;
+      }
+    }
+    if (M < kDecodeMaxTokens)
+      for (int g = threadIdx.x; g < ng; g += blockDim.x)
+        for (int r = M; r < kDecodeMaxTokens; ++r) xcorr[4 * g + r] = 0.f;
+    __syncthreads();
+  };
+  // The grouping of the routed batch (from sh.ids, after the barrier):
+  // workgroup 0 writes the routing and grouping outputs.
+  auto group = [&](int& e, unsigned long long& firsts) {
+    // Assignment f sits in lane f. `before` = earlier assignments of the same
+    // expert (its row within the expert's block), `first` = first occurrence.
+    // A token never repeats an expert, so for M = 1 every lane is a first.
+    e = (lane < MK) ? sh.ids[lane] : -1;
+    int before = 0, tot = 1;
+    if (M > 1) {
+      tot = 0;
+      for (int j = 0; j < MK; ++j) {
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        tot += (ej == e) ? 1 : 0;
+        before += (j < lane && ej == e) ? 1 : 0;
+      }
+    }
+    const bool first = e >= 0 && before == 0;
+    firsts = __ballot(first);
+    const int nd = __builtin_popcountll(firsts);
 
-  // Stage the rows and their group corrections: the 4 vectors of a group sit
-  // in 4 consecutive threads (hv and the block size are multiples of 4, so a
-  // quad is either wholly inside a row or wholly past its end).
-  if constexpr (kEarly) {
-#pragma unroll
-    for (int r = 0; r < MR; ++r)
-#pragma unroll
-      for (int v = 0; v < kXPerThread; ++v) {
-        const int i = threadIdx.x + v * 64 * kDecKSplit;
-        const float corr = group_corr_quad(xr[r][v]);
-        if (i < hv) {
-          xs[r * row16 + i] = xr[r][v];
-          if ((i & 3) == 0) xcorr[4 * (i >> 2) + r] = corr;
+    if (blockIdx.x == 0) {  // routing + grouping outputs, block_m-padded like moe_route_align
+      int rank = 0;         // distinct experts smaller than e: the ascending order
+      for (int j = 0; j < MK; ++j) {
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        rank += (((firsts >> j) & 1ull) && ej < e) ? 1 : 0;
+      }
+      const int B = d.block_m;
+      if (wave == 0 && e >= 0) {
+        sh.rowf[rank][before] = lane;
+        if (first) {
+          sh.list[rank] = e;
+          sh.cnt[rank] = tot;
         }
       }
-  } else {
-    for (int i = threadIdx.x; i < M * hv; i += blockDim.x) {
-      const uint4 v = xg[i];
-      const int r = i / hv, c = i % hv;
-      xs[r * row16 + c] = v;
-      const float corr = group_corr_quad(v);
-      if ((c & 3) == 0) xcorr[4 * (c >> 2) + r] = corr;
-    }
-  }
-  if (M < kDecodeMaxTokens)
-    for (int g = threadIdx.x; g < ng; g += blockDim.x)
-      for (int r = M; r < kDecodeMaxTokens; ++r) xcorr[4 * g + r] = 0.f;
-  __syncthreads();
-  // Assignment f sits in lane f. `before` = earlier assignments of the same
-  // expert (its row within the expert's block), `first` = first occurrence.
-  // A token never repeats an expert, so for M = 1 every lane is a first.
-  const int e = (lane < MK) ? sh.ids[lane] : -1;
-  int before = 0, tot = 1;
-  if (M > 1) {
-    tot = 0;
-    for (int j = 0; j < MK; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      tot += (ej == e) ? 1 : 0;
-      before += (j < lane && ej == e) ? 1 : 0;
-    }
-  }
-  const bool first = e >= 0 && before == 0;
-  const unsigned long long firsts = __ballot(first);
-  const int nd = __builtin_popcountll(firsts);
-
-  if (blockIdx.x == 0) {  // routing + grouping outputs, block_m-padded like moe_route_align
-    int rank = 0;         // distinct experts smaller than e: the ascending order
-    for (int j = 0; j < MK; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      rank += (((firsts >> j) & 1ull) && ej < e) ? 1 : 0;
-    }
-    const int B = d.block_m;
-    if (wave == 0 && e >= 0) {
-      sh.rowf[rank][before] = lane;
-      if (first) {
-        sh.list[rank] = e;
-        sh.cnt[rank] = tot;
+      __syncthreads();
+      for (int i = threadIdx.x; i < MK; i += blockDim.x) {
+        d.topk_ids[i] = sh.ids[i];
+        d.topk_weights[i] = sh.w[i];
       }
+      for (int x = threadIdx.x; x <= E; x += blockDim.x) {
+        int below = 0;
+        for (int q = 0; q < nd; ++q) below += (sh.list[q] < x) ? 1 : 0;
+        d.expert_offsets[x] = B * below;  // every touched expert holds <= M <= B rows: one block
+      }
+      if (threadIdx.x == 0) *d.npp_out = B * nd;
+      for (int pos = threadIdx.x; pos < nd * B; pos += blockDim.x) {
+        const int q = pos / B, r = pos % B;
+        d.sorted_ids[pos] = (r < sh.cnt[q]) ? sh.rowf[q][r] : MK;
+      }
+      for (int q = threadIdx.x; q < nd; q += blockDim.x) d.block_expert[q] = sh.list[q];
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < MK; i += blockDim.x) {
-      d.topk_ids[i] = sh.ids[i];
-      d.topk_weights[i] = sh.w[i];
-    }
-    for (int x = threadIdx.x; x <= E; x += blockDim.x) {
-      int below = 0;
-      for (int q = 0; q < nd; ++q) below += (sh.list[q] < x) ? 1 : 0;
-      d.expert_offsets[x] = B * below;  // every touched expert holds <= M <= B rows: one block
-    }
-    if (threadIdx.x == 0) *d.npp_out = B * nd;
-    for (int pos = threadIdx.x; pos < nd * B; pos += blockDim.x) {
-      const int q = pos / B, r = pos % B;
-      d.sorted_ids[pos] = (r < sh.cnt[q]) ? sh.rowf[q][r] : MK;
-    }
-    for (int q = threadIdx.x; q < nd; q += blockDim.x) d.block_expert[q] = sh.list[q];
-  }
+    return nd;
+  };
 
-  if (blk >= nd) return;
-  // FC1 takes the distinct experts in order of first occurrence: block blk is
-  // the expert of the blk-th first occurrence
-  unsigned long long mb = firsts;
-  for (int i = 0; i < blk; ++i) mb &= mb - 1;
-  const int eb = __builtin_amdgcn_readlane(e, __builtin_ctzll(mb));
-  // lane r < M: the assignment of token r to expert eb (a token lists an expert at most once)
-  int tokf = -1;
-  if (lane < M)
-    for (int j = 0; j < k; ++j) tokf = (sh.ids[lane * k + j] == eb) ? lane * k + j : tokf;
-  fc1_decode_body<MR, NCH>(d, xs, row16, xcorr4, eb, pair, tokf, wave, lane);
+  if constexpr (MR == 1) {
+    // One token: its k experts are distinct and workgroup blk takes slot blk.
+    // Every wave routes the token itself and stops at its slot's take, so its
+    // weight loads go out before the row is staged and without waiting for
+    // the other slots; wave 0 of workgroup 0 routes completely (the routing
+    // outputs).
+    const bool full = blockIdx.x == 0 && wave == 0;
+    const int eb = topk_route<VPL>(d.logits, 0, E, k, full ? k : blk + 1, blk, full ? sh.ids : nullptr, sh.w);
+    const int tokf = lane == 0 ? blk : -1;
+    fc1_decode_body<MR, NCH>(d, xs, row16, xcorr4, eb, pair, tokf, wave, lane, [&]() {
+      stage();
+      if (blockIdx.x == 0) {
+        int e;
+        unsigned long long firsts;
+        (void)group(e, firsts);
+      }
+    });
+  } else {
+    if (wave < M) topk_token<VPL>(d.logits, wave, E, k, sh.ids, sh.w);
+    stage();
+    int e;
+    unsigned long long firsts;
+    const int nd = group(e, firsts);
+    if (blk >= nd) return;
+    // FC1 takes the distinct experts in order of first occurrence: block blk is
+    // the expert of the blk-th first occurrence
+    unsigned long long mb = firsts;
+    for (int i = 0; i < blk; ++i) mb &= mb - 1;
+    const int eb = __builtin_amdgcn_readlane(e, __builtin_ctzll(mb));
+    // lane r < M: the assignment of token r to expert eb (a token lists an expert at most once)
+    int tokf = -1;
+    if (lane < M)
+      for (int j = 0; j < k; ++j) tokf = (sh.ids[lane * k + j] == eb) ? lane * k + j : tokf;
+    fc1_decode_body<MR, NCH>(d, xs, row16, xcorr4, eb, pair, tokf, wave, lane, []() {});
+  }
 }
 
 // One 16-row tile of a pair, for one activation row (D row 0, lanes 0..15):

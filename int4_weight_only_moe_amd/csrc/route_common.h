@@ -103,65 +103,92 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return umin(g[0], g[1]);
 }
 
+// One wave's routing state for a token: lane l holds the order keys of
+// experts l, l+64, ... (VPL of them); 0 = absent or already taken.
 template <int VPL>
-__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
-                           int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-                           int32_t* ids_copy = nullptr) {
+__device__ __forceinline__ void topk_keys(const float* __restrict__ row, int E, uint32_t (&key)[VPL]) {
   const int lane = threadIdx.x & 63;
-  // Lane l holds experts l, l+64, ...: keys (0 = none) sorted descending with
-  // their expert index, equal keys keeping ascending expert order. Each round
-  // takes the wave maximum of the lane heads (32-bit: a few cross-lane
-  // steps); a ballot finds the lane holding it, ties between lanes go to the
-  // smallest expert index; that lane drops its head.
-  uint32_t key[VPL], ex[VPL];
-  const float* row = logits + (int64_t)t * E;
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = v * 64 + lane;
     key[v] = (e < E) ? order_key(row[e]) : 0u;
-    ex[v] = (uint32_t)e;
   }
+}
+
+// Takes the largest remaining key (equal keys: the lower expert index) and
+// returns its expert, the same in every lane; its key becomes 0. Each lane
+// offers its largest key (strict comparison: the lowest v, i.e. the lowest
+// expert, among equal ones), the wave maximum picks the key (a few
+// cross-lane steps), and a ballot finds the lanes offering it: between lanes
+// the lower expert index wins.
+template <int VPL>
+__device__ __forceinline__ int topk_take(uint32_t (&key)[VPL], uint32_t& taken_key) {
+  const int lane = threadIdx.x & 63;
+  uint32_t lm = key[0];
+  int lv = 0;
 #pragma unroll
-  for (int i = 1; i < VPL; ++i) {
-#pragma unroll
-    for (int j = i; j > 0; --j) {
-      const bool sw = key[j] > key[j - 1];  // strict: equal keys keep ascending e
-      const uint32_t k0 = sw ? key[j] : key[j - 1], k1 = sw ? key[j - 1] : key[j];
-      const uint32_t e0 = sw ? ex[j] : ex[j - 1], e1 = sw ? ex[j - 1] : ex[j];
-      key[j - 1] = k0; key[j] = k1; ex[j - 1] = e0; ex[j] = e1;
-    }
+  for (int v = 1; v < VPL; ++v) {
+    const bool gt = key[v] > lm;
+    lm = gt ? key[v] : lm;
+    lv = gt ? v : lv;
   }
-  uint32_t my_key = 0, my_e = 0;
-  for (int r = 0; r < k; ++r) {
-    const uint32_t m = wave_max_u32(key[0]);
-    unsigned long long hold = __ballot(key[0] == m);
-    if (__builtin_popcountll(hold) > 1) {  // equal logits in several lanes
-      const uint32_t emin = wave_min_u32(key[0] == m ? ex[0] : 0xFFFFFFFFu);
-      hold = __ballot(key[0] == m && ex[0] == emin);
-    }
-    const int wl = __builtin_ctzll(hold);
-    const uint32_t we = __builtin_amdgcn_readlane(ex[0], wl);
-    if (lane == wl) {
+  const uint32_t m = wave_max_u32(lm);
+  const uint32_t le = (uint32_t)(lv * 64 + lane);
+  unsigned long long hold = __ballot(lm == m);
+  if (__builtin_popcountll(hold) > 1) {  // equal logits in several lanes
+    const uint32_t emin = wave_min_u32(lm == m ? le : 0xFFFFFFFFu);
+    hold = __ballot(lm == m && le == emin);
+  }
+  const int wl = __builtin_ctzll(hold);
+  const int we = __builtin_amdgcn_readlane((int)le, wl);
 #pragma unroll
-      for (int v = 0; v + 1 < VPL; ++v) {
-        key[v] = key[v + 1];
-        ex[v] = ex[v + 1];
-      }
-      key[VPL - 1] = 0u;
-    }
+  for (int v = 0; v < VPL; ++v) key[v] = (lane == wl && v == lv) ? 0u : key[v];
+  taken_key = m;
+  return we;
+}
+
+// Routes token t with one wave: `rounds` takes (k for the full routing), and
+// the expert of take number `slot` is returned. With out_ids non-null the
+// routing is complete (rounds = k) and lanes < k write expert and weight of
+// their slot: weights = softmax over the k kept logits. (Each wave that
+// needs only slot s stops after s + 1 takes.)
+template <int VPL>
+__device__ __forceinline__ int topk_route(const float* __restrict__ logits, int t, int E, int k, int rounds,
+                                          int slot, int32_t* __restrict__ out_ids, float* __restrict__ out_w,
+                                          int32_t* ids_copy = nullptr) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[VPL];
+  topk_keys<VPL>(logits + (int64_t)t * E, E, key);
+  uint32_t my_key = 0;
+  int my_e = 0, e_slot = 0;
+  for (int r = 0; r < rounds; ++r) {
+    uint32_t m;
+    const int we = topk_take<VPL>(key, m);
+    e_slot = (r == slot) ? we : e_slot;
     if (lane == r) {
       my_key = m;
       my_e = we;
     }
   }
-  const float l0 = key_value(__builtin_amdgcn_readfirstlane(my_key));
-  const float exv = (lane < k) ? expf(key_value(my_key) - l0) : 0.0f;
-  const float sum = wave_sum(exv);
-  if (lane < k) {
-    topk_ids[(int64_t)t * k + lane] = (int)my_e;
-    topk_w[(int64_t)t * k + lane] = exv / sum;
-    if (ids_copy) ids_copy[t * k + lane] = (int)my_e;
+  if (out_ids) {
+    const float l0 = key_value(__builtin_amdgcn_readfirstlane(my_key));
+    const float exv = (lane < k) ? expf(key_value(my_key) - l0) : 0.0f;
+    const float sum = wave_sum(exv);
+    if (lane < k) {
+      out_ids[(int64_t)t * k + lane] = my_e;
+      out_w[(int64_t)t * k + lane] = exv / sum;
+      if (ids_copy) ids_copy[t * k + lane] = my_e;
+    }
   }
+  return e_slot;
+}
+
+// One wave routes token t completely: topk_ids / topk_w [t*k + j] for j < k.
+template <int VPL>
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int k,
+                                           int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                                           int32_t* ids_copy = nullptr) {
+  topk_route<VPL>(logits, t, E, k, k, 0, topk_ids, topk_w, ids_copy);
 }
 
 }  // namespace moe
