@@ -286,6 +286,18 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
     st = hip_status(moe::launch_fc1(a, s, ev0, ev1));
   }
   if (st != MOE_OK) return st;
+  if (moe::token_fc2_fits(M, I, top_k)) {  // small batches: FC2 per token, no accumulator
+    moe::DecodeArgs d2{};
+    d2.fc = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
+                    workspace);
+    d2.fc.act_in = d2.fc.act_out;  // FC1's activations
+    d2.fc.act_out = nullptr;
+    d2.fc.wpacked = (const uint8_t*)w2_packed;
+    d2.fc.out = out_bf16;
+    d2.topk_ids = topk_ids;
+    d2.topk_weights = topk_weights;
+    return hip_status(moe::launch_fc2_tokens(d2, s));
+  }
   return moe_w4a16_fc2(M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
                        num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
 }

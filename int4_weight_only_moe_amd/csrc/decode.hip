@@ -524,14 +524,24 @@ hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t
   DecodeArgs d2 = d;
   d2.fc.act_in = d.fc.act_out;
   d2.fc.wpacked = d.w2;
-  const bool i2048 = d.fc.I == 2048;  // the 384-expert layer: 4 row vectors per lane
-  const size_t lds = (size_t)decode_fc2_lds_bytes(d.fc.I, k);  // the k activation rows + corrections
+  return launch_fc2_tokens(d2, stream);
+}
+
+}  // namespace
+
+// FC2 + combine, output-stationary: act rows d.fc.act_in [M*k, I] (row f =
+// token t, slot j), expert ids and weights from d.topk_ids / d.topk_weights,
+// W2 in d.fc.wpacked, bf16 output d.fc.out [M, H].
+hipError_t launch_fc2_tokens(const DecodeArgs& d2, hipStream_t stream) {
+  const int M = d2.fc.M, k = d2.fc.k;
+  const bool i2048 = d2.fc.I == 2048;  // the 384-expert layer: 4 row vectors per lane
+  const size_t lds = (size_t)decode_fc2_lds_bytes(d2.fc.I, k);  // the k activation rows + corrections
   if (k <= 8) {  // a whole pair per workgroup: 2k <= 16 waves (measured 12 % faster than one tile)
-    const unsigned grid2 = (unsigned)(M * (d.fc.H / 32));
+    const unsigned grid2 = (unsigned)(M * (d2.fc.H / 32));
     if (i2048) fc2_decode_kernel<4, 16, 2><<<grid2, 128 * k, lds, stream>>>(d2);
     else fc2_decode_kernel<0, 16, 2><<<grid2, 128 * k, lds, stream>>>(d2);
   } else {
-    const unsigned grid2 = (unsigned)(M * (d.fc.H / 16));
+    const unsigned grid2 = (unsigned)(M * (d2.fc.H / 16));
     if (k <= 8) {
       if (i2048) fc2_decode_kernel<4, 8, 1><<<grid2, 64 * k, lds, stream>>>(d2);
       else fc2_decode_kernel<0, 8, 1><<<grid2, 64 * k, lds, stream>>>(d2);
@@ -541,8 +551,6 @@ hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t
   }
   return hipGetLastError();
 }
-
-}  // namespace
 
 hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int E = d.fc.E;

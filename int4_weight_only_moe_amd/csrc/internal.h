@@ -130,6 +130,20 @@ struct DecodeArgs {
 };
 // ev_start / ev_stop (may be null) take the routing+FC1 kernel's own timestamps.
 hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+// FC2 + combine per token (output-stationary, no accumulator): act rows in
+// d.fc.act_in, ids / weights in d.topk_ids / d.topk_weights, output d.fc.out.
+hipError_t launch_fc2_tokens(const DecodeArgs& d, hipStream_t stream);
+// Batches up to this many tokens take launch_fc2_tokens in moe_w4a16_layer:
+// it reads each (token, slot)'s expert once, so repeated experts are read
+// again, but it needs no accumulator, atomics or finalize kernel and splits
+// into M * H / 32 equal workgroups (no partly filled last round).
+#ifndef MOE_TOKEN_FC2_MAX_TOKENS
+#define MOE_TOKEN_FC2_MAX_TOKENS 16
+#endif
+constexpr int kTokenFc2MaxTokens = MOE_TOKEN_FC2_MAX_TOKENS;
+inline bool token_fc2_fits(int64_t M, int64_t I, int64_t k) {
+  return M <= kTokenFc2MaxTokens && k <= kDecodeMaxAssign && decode_fc2_lds_bytes(I, k) <= kDecodeMaxStagedBytes;
+}
 
 // Launch with optional kernel-timestamp events.
 template <typename... KArgs, typename... Args>

@@ -35,7 +35,7 @@ def run_layer_call(layer, logits, x_bits, block_m, reps=1):
 
 
 @pytest.mark.parametrize("shape_name", list(SHAPES))
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9, 16, 17])
 @pytest.mark.parametrize("block_m", [16, 64])
 def test_layer_matches_oracle(shape_name, M, block_m):
     shape, seed = SHAPES[shape_name]
@@ -67,6 +67,24 @@ def test_layer_k26_decode_sizes():
                                  oracle_experts(s, 2026, keep=0), tokens_subset=rows)
         rel, mx = assert_output_close(outs[0][rows], ref[rows], f"k26 M={M}")
         print(f"layer k26 M={M}: rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("M", [9, 16, 17, 90])
+def test_layer_k26_grouped_sizes(M):
+    """The layer call past the decode sizes, as the benchmark times it: FC2 per
+    token up to 16 tokens, the grouped FC2 and its finalize above."""
+    layer = k26_layer()
+    s = layer.shape
+    block_m = moe.moe_w4a16_preferred_block_m(M, s.E, s.H, s.I, s.k)
+    t = wl.tokens(s, M, 5150 + M)
+    rb, outs = run_layer_call(layer, t.logits, t.x_bits, block_m)
+    ids, w = assert_route_matches(route_host(rb), t.logits, s.E, s.k, block_m)
+    assert np.all(np.isfinite(outs[0]))
+    rows = [0, M // 2, M - 1]
+    ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,
+                             oracle_experts(s, 2026, keep=0), tokens_subset=rows)
+    rel, mx = assert_output_close(outs[0][rows], ref[rows], f"k26 layer M={M}")
+    print(f"layer k26 M={M} B={block_m}: rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
 
 
 def test_layer_k26_m1_closed_form():
