@@ -96,6 +96,20 @@ def test_empty_batch_is_a_no_op():
     torch.cuda.synchronize()
 
 
+def test_empty_batch_layer_is_a_no_op():
+    shape = wl.TINY
+    layer = device_layer(shape, 0)
+    rb = moe.alloc_route_buffers(0, shape.E, shape.k, 16)
+    out = torch.full((0, shape.H), 1.0, dtype=torch.bfloat16, device="cuda")
+    x = torch.empty((0, shape.H), dtype=torch.bfloat16, device="cuda")
+    logits = torch.empty((0, shape.E), dtype=torch.float32, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    moe.moe_w4a16_layer(logits, x, shape.I, shape.k, 16, rb.topk_ids, rb.topk_weights, rb.sorted_token_ids,
+                        rb.block_expert_ids, rb.expert_offsets, rb.num_tokens_post_pad, layer.w13, layer.w2,
+                        ws, out, cap=rb.cap)
+    torch.cuda.synchronize()
+
+
 def test_output_guard_bands_and_reuse():
     """Output rows outside [0, M) untouched; a second, smaller call reuses the workspace."""
     shape = wl.LayerShape(E=16, H=512, I=256, k=4)
