@@ -209,7 +209,9 @@ int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int
  * workgroup (workgroup 0 also writes the routing/grouping outputs), and FC2
  * is output-stationary (each output tile sums its token's top_k expert
  * results in slot order in one workgroup: no atomics, and the bf16 output is
- * then identical on every call). Larger batches take the four-kernel path.
+ * then identical on every call). Up to 16 tokens the output-stationary FC2
+ * also follows the grouped FC1 (no accumulator and no finalize kernel);
+ * larger batches take the grouped FC2 of moe_w4a16_forward.
  *   stage_events  NULL, or two hipEvent_t that receive the start and end
  *                 timestamps of the FC1-stage kernel itself (for M <= 4 the
  *                 routing is part of it), for timing that stage.
