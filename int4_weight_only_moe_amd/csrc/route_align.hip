@@ -163,11 +163,14 @@ __device__ __forceinline__ void align_body(AlignShared& sh, const int32_t* __res
   // rank among the equal experts of earlier lanes, and advances the running
   // positions.
   if (tid < E) {
+    int c[kAlignWaves];  // all reads first: they go out together
+#pragma unroll
+    for (int w = 0; w < kAlignWaves; ++w) c[w] = sh.wcnt[w][tid];
     int run = sh.off[tid];
+#pragma unroll
     for (int w = 0; w < kAlignWaves; ++w) {
-      const int c = sh.wcnt[w][tid];
       sh.wcnt[w][tid] = run;
-      run += c;
+      run += c[w];
     }
   }
   __syncthreads();
@@ -181,6 +184,7 @@ __device__ __forceinline__ void align_body(AlignShared& sh, const int32_t* __res
     }
 #pragma unroll
     for (int i = 0; i < kIdsPerLane; ++i) {
+      if (fb + 64 * i >= f1) break;  // wave-uniform: the rest of the batch is past the range
       const int e = ev[i];
       const uint64_t same = equal_key_lanes(e, nbits, __ballot(e >= 0));
       const int before = lanes_below(same), tot = __builtin_popcountll(same);
