@@ -286,7 +286,7 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
     st = hip_status(moe::launch_fc1(a, s, ev0, ev1));
   }
   if (st != MOE_OK) return st;
-  if (moe::token_fc2_fits(M, I, top_k)) {  // small batches: FC2 per token, no accumulator
+  if (moe::token_fc2_fits(M, E, I, top_k)) {  // small batches: FC2 per token, no accumulator
     moe::DecodeArgs d2{};
     d2.fc = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
                     workspace);
