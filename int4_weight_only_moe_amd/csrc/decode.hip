@@ -14,7 +14,9 @@
 //                      rows of the block it owns, then runs the FC1 tile body
 //                      of the grouped GEMM; workgroup 0 also writes the
 //                      routing and grouping outputs (experts ascending) in
-//                      the format moe_route_align produces.
+//                      the format moe_route_align produces. For one token
+//                      every wave routes it only as far as its own slot and
+//                      issues its weight loads before the row is staged.
 //   fc2_decode_kernel  output-stationary FC2: one workgroup per (token,
 //                      32-column tile pair of the output; for top-k > 8 one
 //                      16-column tile), one wave per (routing slot j, tile)
@@ -23,9 +25,10 @@
 //                      order with their routing weights, then rounded once to
 //                      bf16. A pair per workgroup reads whole 2304-byte
 //                      chunks, and at M = 1 gives 224 equal workgroups rather
-//                      than 448 on 256 CUs.
-//                      No atomics, no accumulator to clear, no finalize
-//                      kernel, and the float result is deterministic.
+//                      than 448 on 256 CUs. No atomics, no accumulator to
+//                      clear, no finalize kernel, and the float result is
+//                      deterministic. (The layer call also runs it after the
+//                      grouped FC1 for small batches.)
 // Each expert is read once per token that routes to it; with M <= 4 tokens
 // and top-8 of 384 experts, repeats are rare, so the weight traffic stays the
 // touched experts' bytes.
@@ -60,6 +63,8 @@ struct SmallRoute {
 // -136 * (group sum) of the four token rows (xcorr4[group] = one float per
 // token, zero past M), so that every MFMA is a product with the weights.
 // tokf: lane r < MR holds the assignment f of token r to expert e, or -1.
+// pre() runs once the first weight loads are in flight; when it returns, the
+// rows and corrections must be staged and visible to every wave (barrier).
 template <int MR, int NCH, typename Pre>
 __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4* __restrict__ xs, int row16,
                                                 const f32x4_t* __restrict__ xcorr4, const int e, const int pair,
