@@ -23,6 +23,7 @@ MID_SHAPES = [
     (wl.LayerShape(E=64, H=1024, I=384, k=6), 100, 3, 4),
     (wl.LayerShape(E=32, H=384, I=640, k=1), 70, 5, 6),
     (wl.LayerShape(E=4, H=256, I=128, k=4), 200, 7, 8),   # every expert gets every token: many blocks
+    (wl.LayerShape(E=1024, H=256, I=128, k=16), 50, 9, 10),  # the largest E and top-k the ABI takes
 ]
 
 

@@ -19,6 +19,7 @@ SHAPES = {
     "mid": (wl.LayerShape(E=64, H=1024, I=384, k=6), 3),
     "k16": (wl.LayerShape(E=32, H=256, I=128, k=16), 4),   # M*k up to 64
     "k1": (wl.LayerShape(E=32, H=384, I=640, k=1), 5),
+    "e1024": (wl.LayerShape(E=1024, H=256, I=128, k=8), 6),  # 16 logits per lane in the top-k
 }
 
 
