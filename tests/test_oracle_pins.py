@@ -289,3 +289,26 @@ def test_gate_up_order_matters():
     assert not np.allclose(a, b)
     h = W13 @ x
     np.testing.assert_allclose(a, W2 @ (h[: shape.I] / (1 + np.exp(-h[: shape.I])) * h[shape.I:]), rtol=1e-14)
+
+
+def test_workload_recipe_pins(golden_dir):
+    """The seeded inputs follow the written recipe, and the oracle's routing and
+    grouping of them match values derived independently from that recipe."""
+    g = load(golden_dir, "recipe.json")
+    t = wl.workload_tokens(wl.WORKLOADS["tiny"])
+    ids, w = oracle.route(t.logits, wl.TINY.k)
+    T = g["tiny"]
+    assert ids[:4].tolist() == T["ids_rows_0_3"]
+    assert np.bincount(ids.reshape(-1), minlength=wl.TINY.E).tolist() == T["counts"]
+    assert np.allclose(w[0], T["w_row0"], atol=1e-8)
+    assert [format(int(v), "04x") for v in t.x_bits[0, :4]] == T["x_bits_row0"]
+    assert oracle.align(ids, wl.TINY.E, 16)["num_tokens_post_pad"] == T["npp_b16"]
+    for name, p in g["k26"].items():
+        tt = wl.workload_tokens(wl.WORKLOADS[name])
+        ids, _ = oracle.route(tt.logits, wl.K26.k)
+        counts = np.bincount(ids.reshape(-1), minlength=wl.K26.E)
+        assert int((counts > 0).sum()) == p["D"], name
+        assert int(counts.max()) == p["max"], name
+        assert oracle.align(ids, wl.K26.E, 32)["num_tokens_post_pad"] == p["npp_b32"], name
+        if "ids_row0" in p:
+            assert ids[0].tolist() == p["ids_row0"], name
