@@ -142,6 +142,9 @@ K26_SAMPLES = {
     "k26_m512": [0, 300, 511],
     "k26_m1024": [0, 700, 1023],
     "k26_m1024_skew": [0, 1023],
+    "k26_m2048": [0, 2047],
+    "k26_m4096": [1, 4095],
+    "k26_m8192": [0, 5000, 8191],
 }
 
 

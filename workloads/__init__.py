@@ -83,6 +83,12 @@ WORKLOADS = {
     "k26_m1024": Workload("k26_m1024", K26, 1024, 2026, 1024, note="dense multi-stream chunk"),
     "k26_m1024_skew": Workload("k26_m1024_skew", K26, 1024, 2026, 2048, bias_sigma=2.0,
                                note="router logits + per-expert bias N(0, 2)"),
+    # prefill chunks: past M ~ 4200 tokens the layer's arithmetic intensity
+    # crosses the MI355X ridge (the grouped GEMM turns from streaming weights
+    # into matrix work)
+    "k26_m2048": Workload("k26_m2048", K26, 2048, 2026, 2048, note="prefill chunk"),
+    "k26_m4096": Workload("k26_m4096", K26, 4096, 2026, 4096, note="prefill chunk"),
+    "k26_m8192": Workload("k26_m8192", K26, 8192, 2026, 8192, note="prefill chunk"),
 }
 
 
