@@ -42,7 +42,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
 HEADLINE = "k26_m1"
-SWEEP = ["k26_m9", "k26_m90", "k26_m256", "k26_m512", "k26_m1024", "k26_m1024_skew",
+SWEEP = ["k26_m4", "k26_m9", "k26_m90", "k26_m256", "k26_m512", "k26_m1024", "k26_m1024_skew",
          "k26_m2048", "k26_m4096", "k26_m8192"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_k26_m1_traffic.json")
 

@@ -204,17 +204,25 @@ int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int
  * "The Throughput Lever: Quantifying the MoE GEMM and Mapping the Road to
  * B300", section "The B300 Analysis: When the Bottleneck Flips": at decode
  * sizes fixed per-step costs such as kernel launches dominate once the GEMM
- * runs at HBM speed. For M <= 4 and M*top_k <= 64 this call therefore runs
- * two kernels instead of four: the routing is recomputed inside every FC1
- * workgroup (workgroup 0 also writes the routing/grouping outputs), and FC2
- * is output-stationary (each output tile sums its token's top_k expert
- * results in slot order in one workgroup: no atomics, and the bf16 output is
- * then identical on every call). Up to 16 tokens the output-stationary FC2
- * also follows the grouped FC1 (no accumulator and no finalize kernel);
- * larger batches take the grouped FC2 of moe_w4a16_forward.
+ * runs at HBM speed. Small batches therefore run two kernels instead of
+ * four, with the routing and grouping inside the FC1 kernel (one of its
+ * workgroups also writes the routing/grouping outputs):
+ *   - M <= 2 (M*top_k <= 64): the decode path; every FC1 workgroup routes the
+ *     batch, and FC2 is output-stationary (each output tile sums its token's
+ *     top_k expert results in slot order in one workgroup: no atomics, and
+ *     the bf16 output is then identical on every call);
+ *   - M <= 16 and M*top_k <= 256 while few experts are touched (the grouped
+ *     FC1 would fill at most 1.5 rounds of the device's CUs; on the
+ *     384-expert top-8 layer M = 3..6): a persistent FC1 kernel that routes
+ *     once per workgroup and splits the work into small items;
+ *   - else M <= 4 with M*top_k <= 64: the decode path.
+ * Up to 16 tokens the output-stationary FC2 follows the FC1 while the
+ * M*top_k expert reads stay within 1.2x the expected number of distinct
+ * experts (no accumulator and no finalize kernel); otherwise the grouped FC2
+ * of moe_w4a16_forward.
  *   stage_events  NULL, or two hipEvent_t that receive the start and end
- *                 timestamps of the FC1-stage kernel itself (for M <= 4 the
- *                 routing is part of it), for timing that stage.
+ *                 timestamps of the FC1-stage kernel itself (on the two-kernel
+ *                 paths the routing is part of it), for timing that stage.
  */
 int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
                     int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights,

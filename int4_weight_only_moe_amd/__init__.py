@@ -84,9 +84,11 @@ def forward(x: torch.Tensor, rb: RouteBuffers, I: int, w13_packed: torch.Tensor,
 def layer(logits: torch.Tensor, x: torch.Tensor, rb: RouteBuffers, I: int, w13_packed: torch.Tensor,
           w2_packed: torch.Tensor, workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
           stream=None, stage_events=None) -> torch.Tensor:
-    """Routing + expert MLPs in one call: two kernels for M <= 4 (routing inside
-    FC1, FC2 per token), three up to 16 tokens (routing, grouped FC1, FC2 per
-    token), and routing + grouped FC1 + grouped FC2 + finalize above."""
+    """Routing + expert MLPs in one call. Two kernels while few experts are
+    touched (routing inside FC1, FC2 per token: M <= 2 on the decode path,
+    up to 16 tokens on the routed FC1), else three up to 16 tokens (routing,
+    grouped FC1, FC2 per token), and routing + grouped FC1 + grouped FC2 +
+    finalize above."""
     M, H = x.shape
     if workspace is None:
         workspace = torch.empty(max(moe_w4a16_workspace_bytes(M, rb.E, H, I, rb.top_k), 16),

@@ -256,7 +256,10 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t ev0 = stage_events ? (hipEvent_t)stage_events[0] : nullptr;
   hipEvent_t ev1 = stage_events ? (hipEvent_t)stage_events[1] : nullptr;
-  if (moe::decode_path_fits(M, H, I, top_k)) {
+  // decode path for one or two tokens; then the routed FC1 while few experts
+  // are touched; the decode path where it fits; else the four kernels
+  const bool routed = moe::routed_fc1_preferred(M, E, I, top_k);
+  if (moe::decode_path_fits(M, H, I, top_k) && (M <= 2 || !routed)) {
     moe::DecodeArgs d{};
     d.fc = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
                    workspace);
@@ -275,10 +278,27 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
     d.block_m = block_m;
     return hip_status(moe::launch_decode(d, s, ev0, ev1));
   }
-  st = moe_route_align(logits, M, E, top_k, block_m, topk_ids, topk_weights, sorted_token_ids, block_expert_ids,
-                       expert_offsets, num_tokens_post_pad, cap, stream);
-  if (st != MOE_OK) return st;
-  {
+  const bool token_fc2 = moe::token_fc2_fits(M, E, I, top_k);
+  if (routed) {  // routing and grouping inside FC1's workgroups
+    moe::DecodeArgs d{};
+    d.fc = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
+                   workspace);
+    d.fc.act_in = x_bf16;
+    d.fc.wpacked = (const uint8_t*)w13_packed;
+    if (token_fc2) d.fc.zero_words16 = 0;  // the per-token FC2 has no accumulator
+    d.logits = logits;
+    d.topk_ids = topk_ids;
+    d.topk_weights = topk_weights;
+    d.sorted_ids = sorted_token_ids;
+    d.block_expert = block_expert_ids;
+    d.expert_offsets = expert_offsets;
+    d.npp_out = num_tokens_post_pad;
+    d.block_m = block_m;
+    st = hip_status(moe::launch_fc1_routed(d, s, ev0, ev1));
+  } else {
+    st = moe_route_align(logits, M, E, top_k, block_m, topk_ids, topk_weights, sorted_token_ids, block_expert_ids,
+                         expert_offsets, num_tokens_post_pad, cap, stream);
+    if (st != MOE_OK) return st;
     moe::FcArgs a = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
                             num_tokens_post_pad, workspace);
     a.act_in = x_bf16;
@@ -286,7 +306,7 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
     st = hip_status(moe::launch_fc1(a, s, ev0, ev1));
   }
   if (st != MOE_OK) return st;
-  if (moe::token_fc2_fits(M, E, I, top_k)) {  // small batches: FC2 per token, no accumulator
+  if (token_fc2) {  // small batches: FC2 per token, no accumulator
     moe::DecodeArgs d2{};
     d2.fc = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
                     workspace);

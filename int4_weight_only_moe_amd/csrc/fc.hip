@@ -33,6 +33,7 @@
 #include "internal.h"
 #include "device_common.h"
 #include "fc_common.h"
+#include "route_common.h"
 
 namespace moe {
 namespace {
@@ -274,6 +275,282 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
     fc_wide_body<S, kFc1, kPolicyWeights>(a, e, pair, frow, sf, stager, srow, svec, xt, xs4);
 }
 
+// FC1 of a small batch (M <= 16 tokens) with the routing and grouping done
+// inside the kernel ("The Throughput Lever: Quantifying the MoE GEMM and
+// Mapping the Road to B300", section "The B300 Analysis: When the Bottleneck
+// Flips": at small batches the fixed per-step costs, a separate routing
+// launch among them, weigh most).
+//
+// Prologue, once per workgroup: waves 0..M-1 route one token each; a bitmap
+// of the touched experts in LDS ranks them. Top-k experts are distinct, so
+// no expert gets more than M <= 16 rows: every touched expert is exactly one
+// block (of any block_m), the blocks are the touched experts in ascending
+// order, and a block's rows are that expert's assignments in ascending f.
+//
+// Work: items (block, group of kRoutedSlots tile pairs), dealt round-robin
+// to resident workgroups (one per CU). A workgroup's 16 waves are
+// kRoutedSlots pairs x kRoutedKSplit K ranges; the activations come straight
+// from L2 into registers (as in fc_block: a 16-row tile holds one or two
+// real rows here; staging them in LDS with a barrier per chunk measured
+// slower). The small items (the pairs of one block are split 32 ways) keep
+// the last round short: with a few dozen experts touched, the wide kernel's
+// 8 workgroups of 16 pairs per expert leave most CUs idle in a second round.
+// A wave's last P chunk loads already fetch its next item's first chunks, so
+// the weight stream does not drain across the partial-sum reduction and the
+// epilogue.
+//
+// Workgroup 0 writes the routing and grouping outputs after its items,
+// exactly as moe_route_align lays them out for block_m (FC2, their consumer,
+// is the next kernel).
+constexpr int kRoutedMaxTokens = 16;
+constexpr int kRoutedMaxAssign = 256;
+constexpr int kRoutedMaxExperts = 1024;
+constexpr int kRoutedWaves = 16;
+constexpr int kRoutedKSplit = 4;                            // waves per tile pair
+constexpr int kRoutedSlots = kRoutedWaves / kRoutedKSplit;  // tile pairs per item
+constexpr int kRoutedP = 2;                                 // chunks in flight per wave
+
+// One wave's share of an item: expert, tile pair, the row of lane % 16 and
+// its activation offset (kOutOfRange for padding).
+struct RoutedWork {
+  const uint8_t* w;  // this wave's first chunk of the pair
+  uint32_t wbytes;   // bytes of a chunk to read: kPairChunkBytes, 0 for no item (reads zeros)
+  int pair, frow;
+  uint32_t xoff;
+};
+
+template <int VPL, int NCH>
+__global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArgs d) {
+  constexpr int P = kRoutedP, KS = kRoutedKSplit;
+  constexpr int kThreads = 64 * kRoutedWaves;
+  __shared__ int32_t ids[kRoutedMaxAssign];
+  __shared__ float wts[kRoutedMaxAssign];
+  __shared__ uint32_t bits[kRoutedMaxExperts / 32];      // touched experts
+  __shared__ int32_t before[kRoutedMaxExperts / 32 + 1];  // touched experts in the words below
+  __shared__ f32x4_t red[2][KS - 1][kRoutedSlots][2][64];  // K-range partial sums, by item parity
+  __shared__ int32_t blk_e[kRoutedMaxAssign];               // expert of each block
+  __shared__ int32_t blk_rows[kRoutedMaxAssign][16];        // rows of each block, padded with M*k
+
+  const FcArgs& a = d.fc;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = wave % KS, slot = wave / KS;
+  const int M = a.M, E = a.E, k = a.k, MK = M * k, H = a.H;
+  const int nwords = (E + 31) / 32;
+
+  if (a.zero_words16 > 0) {  // clear FC2's accumulator when the grouped FC2 follows
+    uint4* z = reinterpret_cast<uint4*>(a.acc);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < a.zero_words16; i += stride)
+      z[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  if (tid < nwords) bits[tid] = 0u;
+  if (wave < M) topk_token<VPL>(d.logits, wave, E, k, ids, wts);
+  __syncthreads();
+  for (int f = tid; f < MK; f += kThreads) atomicOr(&bits[ids[f] >> 5], 1u << (ids[f] & 31));
+  __syncthreads();
+  if (wave == 0) {  // exclusive prefix of the words' popcounts (nwords <= 32)
+    const int c = lane < nwords ? __builtin_popcount(bits[lane]) : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (lane < nwords) before[lane] = incl - c;
+    if (lane == nwords - 1) before[nwords] = incl;
+  }
+  __syncthreads();
+  // LDS values read here are the same in every lane: readfirstlane keeps
+  // the loop counts and the weight addresses in scalar registers.
+  const int nd = __builtin_amdgcn_readfirstlane(before[nwords]);  // touched experts = blocks
+  auto rank = [&](int x) {  // touched experts below x
+    const int wx = x >> 5, b = x & 31;
+    return before[wx] + __builtin_popcount(bits[wx] & ((1u << b) - 1u));
+  };
+  // block tables: the expert of rank r is block r; its rows are its
+  // assignments in ascending f (one ballot per 64 assignments), then padding
+  for (int x = tid; x < E; x += kThreads)
+    if ((bits[x >> 5] >> (x & 31)) & 1u) blk_e[rank(x)] = x;
+  __syncthreads();
+  for (int b = wave; b < nd; b += kRoutedWaves) {
+    const int e = blk_e[b];
+    int base = 0;
+    for (int f0 = 0; f0 < MK; f0 += 64) {
+      const int f = f0 + lane;
+      const bool hit = f < MK && ids[f] == e;
+      const uint64_t hm = __ballot(hit);
+      if (hit) blk_rows[b][base + lanes_below(hm)] = f;
+      base += __builtin_popcountll(hm);
+    }
+    if (lane >= base && lane < 16) blk_rows[b][lane] = MK;
+  }
+  __syncthreads();
+
+  const int nkc = H / kChunkK;
+  const int kc0 = kq * nkc / KS;
+  const int n = NCH > 0 ? NCH : (kq + 1) * nkc / KS - kc0;  // this wave's chunks
+  const int ipb = 2 * a.I / kPairRows / kRoutedSlots;        // items per block
+  const int nitems = nd * ipb;
+  const int64_t wexp = packed_bytes_per_expert(2 * a.I, H);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.act_in, (uint32_t)M * (uint32_t)H * 2u);
+  const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
+  const uint32_t os0 = kTileNibbleBytes + 8u * (lane & 15), os1 = kTileBytes + kTileNibbleBytes + 8u * (lane & 15);
+
+  auto work_of = [&](int item) {
+    const int blk = item / ipb;
+    RoutedWork r;
+    r.pair = (item % ipb) * kRoutedSlots + slot;
+    const int e = __builtin_amdgcn_readfirstlane(blk_e[blk]);
+    r.frow = blk_rows[blk][lane & 15];
+    r.w = a.wpacked + (int64_t)e * wexp + ((int64_t)r.pair * nkc + kc0) * kPairChunkBytes;
+    r.wbytes = kPairChunkBytes;
+    r.xoff = r.frow < MK ? ((uint32_t)(r.frow / k) * (uint32_t)H + 8u * (lane >> 4) + (uint32_t)kc0 * kChunkK) * 2u
+                         : kOutOfRange;
+    return r;
+  };
+  // one buffer descriptor per chunk (scalar arithmetic); a chunk at or past
+  // n has no bytes in range and reads zeros
+  auto load_w = [&](const RoutedWork& r, int c) {
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(r.w + (int64_t)c * kPairChunkBytes, c < n ? r.wbytes : 0u);
+    WChunk w;
+    w.q0 = bload16<kPolicyWeights>(wr, oq0);
+    w.q1 = bload16<kPolicyWeights>(wr, oq1);
+    w.s0 = bload8<kPolicyWeights>(wr, os0);
+    w.s1 = bload8<kPolicyWeights>(wr, os1);
+    return w;
+  };
+  auto load_x = [&](uint4 (&xa)[1][4], const RoutedWork& r, int c) {
+    const uint32_t o = (c < n) ? r.xoff + (uint32_t)c * kChunkXBytes : kOutOfRange;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xa[0][j] = bload16(xr, o + 64u * j);
+  };
+
+  const bf16x8_t neg136 = as_bf16x8(make_uint4(kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair));
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const bool sact[1] = {true};  // a touched expert has at least one row
+  WChunk wb[P];
+  uint4 xb[P][1][4];
+  int item = blockIdx.x, par = 0;
+  RoutedWork cur;
+  if (item < nitems) {
+    cur = work_of(item);
+    if constexpr (NCH > 0) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        wb[j] = load_w(cur, j);
+        load_x(xb[j], cur, j);
+      }
+    }
+  }
+  while (item < nitems) {
+    const int next = item + (int)gridDim.x;
+    const bool has_next = next < nitems;
+    RoutedWork nx = cur;  // past the last item: loads of no bytes
+    nx.wbytes = 0u;
+    nx.xoff = kOutOfRange;
+    if (has_next) nx = work_of(next);
+    f32x4_t acc0[1] = {zero4}, acc1[1] = {zero4};
+    if constexpr (NCH > 0) {
+      // straight-line (exact memory waits); the last P steps load the next
+      // item's first chunks
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        mma_chunk<1>(wb[c % P], xb[c % P], sact, neg136, acc0, acc1);
+        if (c + P < NCH) {
+          wb[c % P] = load_w(cur, c + P);
+          load_x(xb[c % P], cur, c + P);
+        } else {
+          wb[c % P] = load_w(nx, c + P - NCH);
+          load_x(xb[c % P], nx, c + P - NCH);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // bound live ranges to one chunk
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        wb[j] = load_w(cur, j);
+        load_x(xb[j], cur, j);
+      }
+      for (int c = 0; c < n; c += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          if (c + j < n) mma_chunk<1>(wb[j], xb[j], sact, neg136, acc0, acc1);
+          wb[j] = load_w(cur, c + j + P);
+          load_x(xb[j], cur, c + j + P);
+        }
+      }
+    }
+    // sum the K ranges' partials; the K-range-0 wave of each pair runs the
+    // epilogue (the buffer alternates by item, so the next item's writes
+    // cannot overtake these reads: they come after the next barrier)
+    if (kq > 0) {
+      red[par][kq - 1][slot][0][lane] = acc0[0];
+      red[par][kq - 1][slot][1][lane] = acc1[0];
+    }
+    __syncthreads();
+    if (kq == 0) {
+#pragma unroll
+      for (int q = 0; q < KS - 1; ++q) {
+        acc0[0] += red[par][q][slot][0][lane];
+        acc1[0] += red[par][q][slot][1][lane];
+      }
+      const int frow[1] = {cur.frow};
+      fc_epilogue<1, true>(a, cur.pair, frow, sact, acc0, acc1, lane);
+    }
+    item = next;
+    cur = nx;
+    par ^= 1;
+  }
+
+  if (blockIdx.x == 0) {  // routing + grouping outputs, in block_m-row blocks
+    const int bm = d.block_m;
+    for (int f = tid; f < MK; f += kThreads) {
+      d.topk_ids[f] = ids[f];
+      d.topk_weights[f] = wts[f];
+    }
+    for (int i = tid; i < nd * bm; i += kThreads) {
+      const int b = i / bm, p = i % bm;
+      d.sorted_ids[i] = p < 16 ? blk_rows[b][p] : MK;
+    }
+    for (int b = tid; b < nd; b += kThreads) d.block_expert[b] = blk_e[b];
+    for (int x = tid; x <= E; x += kThreads) d.expert_offsets[x] = bm * (x < E ? rank(x) : nd);
+    if (tid == 0) *d.npp_out = bm * nd;
+  }
+}
+
+// Workgroups of the routed FC1: one per compute unit (its register use
+// allows one 16-wave workgroup per CU), at most one per work item.
+inline int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+inline int64_t routed_grid(int64_t max_items) {
+  const int64_t cus = device_cus();
+  return max_items < cus ? max_items : cus;
+}
+
+template <int VPL>
+hipError_t launch_routed_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  const int64_t MK = (int64_t)d.fc.M * d.fc.k;
+  const int64_t nblk = MK < d.fc.E ? MK : d.fc.E;
+  const unsigned grid = (unsigned)routed_grid(nblk * (2 * d.fc.I / kPairRows / kRoutedSlots));
+  const int nkc = d.fc.H / kChunkK;
+  // straight-line chunk loops for K ranges of 2 and 14 chunks (H = 1024, 7168)
+  if (nkc == 2 * kRoutedKSplit)
+    launch_kernel(fc1_routed_kernel<VPL, 2>, grid, 64 * kRoutedWaves, 0, stream, e0, e1, d);
+  else if (nkc == 14 * kRoutedKSplit)
+    launch_kernel(fc1_routed_kernel<VPL, 14>, grid, 64 * kRoutedWaves, 0, stream, e0, e1, d);
+  else
+    launch_kernel(fc1_routed_kernel<VPL, 0>, grid, 64 * kRoutedWaves, 0, stream, e0, e1, d);
+  return hipGetLastError();
+}
+
 // out = bf16(acc), 8 values per thread.
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ acc, uint16_t* __restrict__ out,
                                                        int64_t n8) {
@@ -348,5 +625,33 @@ hipError_t launch_fc1(const FcArgs& a, hipStream_t stream, hipEvent_t ev_start, 
   return launch_fc<true>(a, stream, ev_start, ev_stop);
 }
 hipError_t launch_fc2(const FcArgs& a, hipStream_t stream) { return launch_fc<false>(a, stream, nullptr, nullptr); }
+
+bool routed_fc1_fits(int64_t M, int64_t E, int64_t I, int64_t k) {
+  return M >= 1 && M <= kRoutedMaxTokens && M * k <= kRoutedMaxAssign && E <= kRoutedMaxExperts &&
+         (2 * I / kPairRows) % kRoutedSlots == 0;
+}
+
+bool routed_fc1_preferred(int64_t M, int64_t E, int64_t I, int64_t k) {
+  if (!routed_fc1_fits(M, E, I, k)) return false;
+  // Per CU the routed kernel streams ~10-15 % slower than the wide kernel;
+  // it wins while the wide kernel's workgroups (16 pairs of one expert
+  // each, for the expected number of distinct experts) would fill at most
+  // 1.5 rounds of the CUs. On the 384-expert top-8 layer (measured): M = 3
+  // ... 6 by 19-2 %, slower from M = 7.
+  double miss = 1.0;  // probability that an expert is not among M tokens' top-k (uniform routing)
+  for (int64_t t = 0; t < M; ++t) miss *= 1.0 - (double)k / (double)E;
+  const double wide_wgs = (double)E * (1.0 - miss) * (double)(2 * I / kPairRows) / kWideNP;
+  return wide_wgs <= 1.5 * device_cus();
+}
+
+hipError_t launch_fc1_routed(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const int E = d.fc.E;
+  if (E <= 64) return launch_routed_vpl<1>(d, stream, ev_start, ev_stop);
+  if (E <= 128) return launch_routed_vpl<2>(d, stream, ev_start, ev_stop);
+  if (E <= 256) return launch_routed_vpl<4>(d, stream, ev_start, ev_stop);
+  if (E <= 384) return launch_routed_vpl<6>(d, stream, ev_start, ev_stop);
+  if (E <= 512) return launch_routed_vpl<8>(d, stream, ev_start, ev_stop);
+  return launch_routed_vpl<16>(d, stream, ev_start, ev_stop);
+}
 
 }  // namespace moe

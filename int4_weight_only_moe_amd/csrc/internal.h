@@ -152,6 +152,17 @@ inline bool token_fc2_fits(int64_t M, int64_t E, int64_t I, int64_t k) {
   return (double)(M * k) <= 1.2 * (double)E * (1.0 - miss);
 }
 
+// Routing, grouping and FC1 in one kernel for batches of up to 16 tokens
+// (M*k <= 256, E <= 1024, 2I/32 a multiple of 16): fills every output that
+// moe_route_align fills (d.topk_ids ... d.npp_out, in d.block_m-row blocks)
+// and FC1's activation rows in d.fc.act_out; clears d.fc.zero_words16
+// 16-byte words of d.fc.acc (0: none). ev_start / ev_stop as for launch_decode.
+bool routed_fc1_fits(int64_t M, int64_t E, int64_t I, int64_t k);
+// Whether moe_w4a16_layer takes it: fits, and the grouped wide kernel would
+// leave CUs idle (few experts touched). Queries the current device.
+bool routed_fc1_preferred(int64_t M, int64_t E, int64_t I, int64_t k);
+hipError_t launch_fc1_routed(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+
 // Launch with optional kernel-timestamp events.
 template <typename... KArgs, typename... Args>
 inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,

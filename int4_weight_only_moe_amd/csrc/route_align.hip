@@ -65,12 +65,6 @@ __device__ __forceinline__ uint64_t equal_key_lanes(int key, int nbits, uint64_t
   return m;
 }
 
-// Set bits of m in the lanes below this one.
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 __device__ __forceinline__ void align_body(AlignShared& sh, const int32_t* __restrict__ ids, int MK, int E,
                            int block_m, int32_t* __restrict__ sorted_ids,
                            int32_t* __restrict__ block_expert, int32_t* __restrict__ offsets,

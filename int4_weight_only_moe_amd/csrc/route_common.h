@@ -147,6 +147,11 @@ __device__ __forceinline__ int topk_take(uint32_t (&key)[VPL], uint32_t& taken_k
   return we;
 }
 
+// Set bits of m in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Routes token t with one wave: `rounds` takes (k for the full routing), and
 // the expert of take number `slot` is returned. With out_ids non-null the
 // routing is complete (rounds = k) and lanes < k write expert and weight of

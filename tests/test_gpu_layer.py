@@ -1,7 +1,10 @@
-"""moe_w4a16_layer: the one-call layer. For M <= 4 it runs the two-kernel
-decode path (routing inside FC1, output-stationary FC2); above, the four-kernel
-path. Integers must equal moe_route_align's, the output must meet the oracle
-bar, and the decode path's output must be identical on every call."""
+"""moe_w4a16_layer: the one-call layer. M <= 2 runs the two-kernel decode
+path (routing inside FC1, output-stationary FC2); while few experts are
+touched (M <= 16, M*k <= 256; every small shape here, M = 3..6 on the
+384-expert layer) routing and grouping run inside the FC1 kernel; otherwise
+the decode path where it fits, else the four-kernel path. Integers must
+equal moe_route_align's, the output must meet the oracle bar, and the decode
+path's output must be identical on every call."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +23,12 @@ SHAPES = {
     "k16": (wl.LayerShape(E=32, H=256, I=128, k=16), 4),   # M*k up to 64
     "k1": (wl.LayerShape(E=32, H=384, I=640, k=1), 5),
     "e1024": (wl.LayerShape(E=1024, H=256, I=128, k=8), 6),  # 16 logits per lane in the top-k
+    # M = 5..16 take the routed FC1 on every shape (M*k <= 256). "wide": the
+    # straight-line chunk loop (H = 1024), per-token FC2 at M = 5, grouped FC2
+    # and several items per workgroup at 16; "wide_e1024": 16 logits per lane,
+    # k = 16 (grouped FC2), several items per workgroup from M = 9
+    "wide": (wl.LayerShape(E=128, H=1024, I=256, k=8), 7),
+    "wide_e1024": (wl.LayerShape(E=1024, H=256, I=256, k=16), 8),
 }
 
 
@@ -37,7 +46,7 @@ def run_layer_call(layer, logits, x_bits, block_m, reps=1):
 
 @pytest.mark.parametrize("shape_name", list(SHAPES))
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9, 16, 17])
-@pytest.mark.parametrize("block_m", [16, 64])
+@pytest.mark.parametrize("block_m", [16, 32, 64])
 def test_layer_matches_oracle(shape_name, M, block_m):
     shape, seed = SHAPES[shape_name]
     if M * shape.k > 64 and M <= 4:
@@ -50,7 +59,7 @@ def test_layer_matches_oracle(shape_name, M, block_m):
     ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,
                              oracle_experts(shape, seed))
     assert_output_close(outs[0], ref, f"{shape_name} M={M}")
-    if M <= 4:
+    if M <= 2:
         for o in outs[1:]:
             assert np.array_equal(o, outs[0]), "decode path must be deterministic"
 
@@ -70,10 +79,12 @@ def test_layer_k26_decode_sizes():
         print(f"layer k26 M={M}: rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
 
 
-@pytest.mark.parametrize("M", [9, 16, 17, 90])
+@pytest.mark.parametrize("M", [3, 5, 6, 7, 9, 16, 17, 90])
 def test_layer_k26_grouped_sizes(M):
-    """The layer call past the decode sizes, as the benchmark times it: FC2 per
-    token up to 16 tokens, the grouped FC2 and its finalize above."""
+    """The layer call past the decode sizes, as the benchmark times it: the
+    routed FC1 at M = 3..6 (several items per workgroup from M = 5), the
+    grouped FC1 from 7; FC2 per token up to 16 tokens, the grouped FC2 and
+    its finalize above."""
     layer = k26_layer()
     s = layer.shape
     block_m = moe.moe_w4a16_preferred_block_m(M, s.E, s.H, s.I, s.k)
@@ -99,10 +110,10 @@ def test_layer_k26_m1_closed_form():
     assert np.all(outs[0] == 50176.0)
 
 
-def test_layer_graph_replays():
-    shape, seed = SHAPES["mid"]
+@pytest.mark.parametrize("shape_name,M", [("mid", 2), ("wide", 5)])
+def test_layer_graph_replays(shape_name, M):
+    shape, seed = SHAPES[shape_name]
     layer = device_layer(shape, seed)
-    M = 2
     t = wl.tokens(shape, M, 5)
     lg, x = to_dev(t.logits), x_device(t.x_bits)
     rb = moe.alloc_route_buffers(M, shape.E, shape.k, 16)

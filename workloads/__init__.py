@@ -70,12 +70,14 @@ K26 = LayerShape(E=384, H=7168, I=2048, k=8)
 
 # The workloads: a tiny layer the oracle runs in milliseconds, and the
 # 384-expert layer at the token counts the pages measure (1 = one stream
-# decoding, 9 = one stream verifying a tree of budget 8, 90 = ten such
+# decoding, 4 = four streams decoding, 9 = one stream verifying a tree of
+# budget 8, 90 = ten such
 # streams, 256 / 512 / 1024 = multi-stream batches), plus M=1024 with a
 # per-expert routing bias that skews the expert load.
 WORKLOADS = {
     "tiny": Workload("tiny", TINY, 16, 0, 0, note="8 experts, H=256, I=128, top-2, M=16"),
     "k26_m1": Workload("k26_m1", K26, 1, 2026, 1, note="decode, one stream"),
+    "k26_m4": Workload("k26_m4", K26, 4, 2026, 4, note="decode, four streams"),
     "k26_m9": Workload("k26_m9", K26, 9, 2026, 9, note="tree verify, 1 stream x q_len 9"),
     "k26_m90": Workload("k26_m90", K26, 90, 2026, 90, note="tree verify, 10 streams x q_len 9"),
     "k26_m256": Workload("k26_m256", K26, 256, 2026, 256, note="all experts touched on average"),
