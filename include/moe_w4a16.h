@@ -42,6 +42,14 @@
  *
  * Limits (MOE_ERR_UNSUPPORTED otherwise): 1 <= E <= 1024, 1 <= top_k <= min(E, 16),
  * H and I multiples of 128, block_m in {16, 32, 64}, M*top_k*max(H, I) < 2^31.
+ *
+ * MXFP4 expert weights (the moe_mxfp4_* entry points at the end): "From
+ * 1,060 to 4,016 tok/s on one B300, and why it wasn't the kernels" serves a
+ * MoE whose experts are MXFP4 (opening section; its MoE kernels are MXFP4,
+ * section "Finding 2: the MoE autotuner only saw decode shapes"). The same
+ * routing, grouping, layer structure and bf16 activations, with the weights
+ * in the OCP Microscaling (MX) v1.0 MXFP4 format: FP4 e2m1 codes and one E8M0
+ * scale per 32 input channels.
  */
 #ifndef MOE_W4A16_H
 #define MOE_W4A16_H
@@ -225,6 +233,57 @@ int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int
  *                 paths the routing is part of it), for timing that stage.
  */
 int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
+                    int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights,
+                    int32_t* sorted_token_ids, int32_t* block_expert_ids, int32_t* expert_offsets,
+                    int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed, const void* w2_packed,
+                    void* workspace, int64_t workspace_bytes, uint16_t* out_bf16, void* stream,
+                    void* const* stage_events);
+
+/*
+ * ---- MXFP4 weights --------------------------------------------------------
+ * Canonical MXFP4 weight format (input of moe_mxfp4_repack):
+ *   qweight     uint8 [E, N, K/2]: byte i of a row holds input channel 2i in
+ *               its low nibble and 2i+1 in its high nibble; a nibble is an
+ *               FP4 e2m1 code (bit 3 sign, bits 2..1 exponent with bias 1,
+ *               bit 0 mantissa: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ *   scales_e8m0 uint8 [E, N, K/32]: s encodes 2^(s - 127) (255 = NaN).
+ *   W[e, n, c] = fp4(qweight code) * 2^(scales_e8m0[e, n, c/32] - 127).
+ *   W13 / W2 rows and shapes as for the INT4 format. Limits as above.
+ * The device layout is the INT4 one with the codes in canonical byte order
+ * and one scale byte per group: 0.53125 bytes per weight (INT4: 0.5625).
+ * The kernels widen each code to the exact bf16 value code * 2^(s - 127)
+ * (gfx950's FP4 conversion), so scales whose weights leave bf16's range
+ * (s >= 253, or subnormal products) are outside the exact-result contract.
+ */
+
+/* Bytes of one repacked MXFP4 weight tensor (host); -1 for unsupported shapes. */
+int64_t moe_mxfp4_packed_bytes(int32_t E, int32_t N, int32_t K);
+
+/* moe_mxfp4_repack / moe_mxfp4_unpack: as moe_w4a16_repack / _unpack for the
+ * MXFP4 format (kind 0 = W13, 1 = W2; 16-byte aligned buffers). */
+int moe_mxfp4_repack(const uint8_t* qweight, const uint8_t* scales_e8m0, int32_t E, int32_t N, int32_t K,
+                     int32_t kind, void* packed, void* stream);
+int moe_mxfp4_unpack(const void* packed, int32_t E, int32_t N, int32_t K, int32_t kind, uint8_t* qweight,
+                     uint8_t* scales_e8m0, void* stream);
+
+/* moe_mxfp4_fc1, _fc2, _forward, _layer: the moe_w4a16_* entry points of the
+ * same names (same arguments, workspace, routing buffers and semantics) with
+ * moe_mxfp4_repack weights. */
+int moe_mxfp4_fc1(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k,
+                  int32_t block_m, const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
+                  const int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed, void* workspace,
+                  int64_t workspace_bytes, void* stream);
+int moe_mxfp4_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
+                  const float* topk_weights, const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
+                  const int32_t* num_tokens_post_pad, int64_t cap, const void* w2_packed, void* workspace,
+                  int64_t workspace_bytes, uint16_t* out_bf16, void* stream);
+int moe_mxfp4_forward(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k,
+                      int32_t block_m, const float* topk_weights, const int32_t* sorted_token_ids,
+                      const int32_t* block_expert_ids, const int32_t* expert_offsets,
+                      const int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed,
+                      const void* w2_packed, void* workspace, int64_t workspace_bytes, uint16_t* out_bf16,
+                      void* stream);
+int moe_mxfp4_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
                     int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights,
                     int32_t* sorted_token_ids, int32_t* block_expert_ids, int32_t* expert_offsets,
                     int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed, const void* w2_packed,

@@ -18,8 +18,12 @@ from ._binding import (  # noqa: F401
     GROUP, KIND_W13, KIND_W2, MOE_ERR_CAPACITY, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE, MOE_OK, MoeError, lib, library_path, moe_route_align, moe_route_align_capacity,
     moe_w4a16_abi_version, moe_w4a16_fc1, moe_w4a16_fc2, moe_w4a16_forward, moe_w4a16_layer, moe_w4a16_packed_bytes,
-    moe_w4a16_preferred_block_m, moe_w4a16_repack, moe_w4a16_unpack, moe_w4a16_workspace_bytes, status_string,
+    moe_w4a16_preferred_block_m, moe_w4a16_repack, moe_w4a16_unpack, moe_w4a16_workspace_bytes,
+    moe_mxfp4_fc1, moe_mxfp4_fc2, moe_mxfp4_forward, moe_mxfp4_layer, moe_mxfp4_packed_bytes, moe_mxfp4_repack,
+    moe_mxfp4_unpack, status_string,
 )
+
+FORMATS = ("int4", "mxfp4")  # weight formats: INT4 g32 + fp16 scales, MXFP4 (e2m1 + E8M0 per 32)
 
 
 @dataclass
@@ -67,35 +71,56 @@ def repack(qweight: torch.Tensor, scales_f16: torch.Tensor, kind: int, stream=No
     return packed
 
 
+def repack_mxfp4(qweight: torch.Tensor, scales_e8m0: torch.Tensor, kind: int, stream=None) -> torch.Tensor:
+    """Repack canonical [E, N, K/2] FP4 codes + [E, N, K/32] E8M0 scales into a new device blob."""
+    E, N, K2 = qweight.shape
+    nbytes = moe_mxfp4_packed_bytes(E, N, 2 * K2)
+    if nbytes < 0:
+        raise ValueError("unsupported weight shape")
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=qweight.device)
+    moe_mxfp4_repack(qweight, scales_e8m0, kind, packed, stream=stream)
+    return packed
+
+
+def _check_fmt(fmt: str) -> None:
+    if fmt not in FORMATS:
+        raise ValueError(f"fmt must be one of {FORMATS}")
+
+
 def forward(x: torch.Tensor, rb: RouteBuffers, I: int, w13_packed: torch.Tensor, w2_packed: torch.Tensor,
-            workspace: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+            workspace: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None,
+            fmt: str = "int4") -> torch.Tensor:
+    _check_fmt(fmt)
     M, H = x.shape
     if workspace is None:
         workspace = torch.empty(max(moe_w4a16_workspace_bytes(M, rb.E, H, I, rb.top_k), 16),
                                 dtype=torch.uint8, device=x.device)
     if out is None:
         out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
-    moe_w4a16_forward(x, rb.E, I, rb.top_k, rb.block_m, rb.topk_weights, rb.sorted_token_ids,
-                      rb.block_expert_ids, rb.expert_offsets, rb.num_tokens_post_pad, w13_packed, w2_packed,
-                      workspace, out, cap=rb.cap, stream=stream)
+    fwd = moe_mxfp4_forward if fmt == "mxfp4" else moe_w4a16_forward
+    fwd(x, rb.E, I, rb.top_k, rb.block_m, rb.topk_weights, rb.sorted_token_ids, rb.block_expert_ids,
+        rb.expert_offsets, rb.num_tokens_post_pad, w13_packed, w2_packed, workspace, out, cap=rb.cap, stream=stream)
     return out
 
 
 def layer(logits: torch.Tensor, x: torch.Tensor, rb: RouteBuffers, I: int, w13_packed: torch.Tensor,
           w2_packed: torch.Tensor, workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-          stream=None, stage_events=None) -> torch.Tensor:
+          stream=None, stage_events=None, fmt: str = "int4") -> torch.Tensor:
     """Routing + expert MLPs in one call. Two kernels while few experts are
     touched (routing inside FC1, FC2 per token: M <= 2 on the decode path,
     up to 16 tokens on the routed FC1), else three up to 16 tokens (routing,
     grouped FC1, FC2 per token), and routing + grouped FC1 + grouped FC2 +
-    finalize above."""
+    finalize above. fmt: "int4" (moe_w4a16_repack weights) or "mxfp4"
+    (moe_mxfp4_repack weights)."""
+    _check_fmt(fmt)
     M, H = x.shape
     if workspace is None:
         workspace = torch.empty(max(moe_w4a16_workspace_bytes(M, rb.E, H, I, rb.top_k), 16),
                                 dtype=torch.uint8, device=x.device)
     if out is None:
         out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
-    moe_w4a16_layer(logits, x, I, rb.top_k, rb.block_m, rb.topk_ids, rb.topk_weights, rb.sorted_token_ids,
-                    rb.block_expert_ids, rb.expert_offsets, rb.num_tokens_post_pad, w13_packed, w2_packed,
-                    workspace, out, cap=rb.cap, stream=stream, stage_events=stage_events)
+    call = moe_mxfp4_layer if fmt == "mxfp4" else moe_w4a16_layer
+    call(logits, x, I, rb.top_k, rb.block_m, rb.topk_ids, rb.topk_weights, rb.sorted_token_ids,
+         rb.block_expert_ids, rb.expert_offsets, rb.num_tokens_post_pad, w13_packed, w2_packed,
+         workspace, out, cap=rb.cap, stream=stream, stage_events=stage_events)
     return out

@@ -49,7 +49,13 @@ _SIGNATURES = {
                                      _i64, _vp, _vp]),
     "moe_w4a16_layer": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
+    "moe_mxfp4_packed_bytes": (_i64, [_i32, _i32, _i32]),
+    "moe_mxfp4_repack": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "moe_mxfp4_unpack": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
 }
+# the MXFP4 stages take the same arguments as the INT4 ones
+for _stage in ("fc1", "fc2", "forward", "layer"):
+    _SIGNATURES["moe_mxfp4_" + _stage] = _SIGNATURES["moe_w4a16_" + _stage]
 
 
 class MoeError(RuntimeError):
@@ -121,6 +127,10 @@ def moe_w4a16_packed_bytes(E: int, N: int, K: int, group: int = GROUP) -> int:
     return lib().moe_w4a16_packed_bytes(E, N, K, group)
 
 
+def moe_mxfp4_packed_bytes(E: int, N: int, K: int) -> int:
+    return lib().moe_mxfp4_packed_bytes(E, N, K)
+
+
 def moe_w4a16_workspace_bytes(M: int, E: int, H: int, I: int, top_k: int) -> int:
     return lib().moe_w4a16_workspace_bytes(M, E, H, I, top_k)
 
@@ -164,15 +174,33 @@ def moe_w4a16_unpack(packed: torch.Tensor, E: int, N: int, K: int, kind: int, qw
     _check("moe_w4a16_unpack", st)
 
 
+def moe_mxfp4_repack(qweight: torch.Tensor, scales_e8m0: torch.Tensor, kind: int, packed: torch.Tensor,
+                     stream=None) -> None:
+    E, N, K2 = qweight.shape
+    st = lib().moe_mxfp4_repack(
+        _ptr(qweight, torch.uint8, "qweight"), _ptr(scales_e8m0, torch.uint8, "scales_e8m0"),
+        E, N, 2 * K2, kind, _ptr(packed, torch.uint8, "packed"), _stream(stream))
+    _check("moe_mxfp4_repack", st)
+
+
+def moe_mxfp4_unpack(packed: torch.Tensor, E: int, N: int, K: int, kind: int, qweight: torch.Tensor,
+                     scales_e8m0: torch.Tensor, stream=None) -> None:
+    st = lib().moe_mxfp4_unpack(
+        _ptr(packed, torch.uint8, "packed"), E, N, K, kind,
+        _ptr(qweight, torch.uint8, "qweight"), _ptr(scales_e8m0, torch.uint8, "scales_e8m0"), _stream(stream))
+    _check("moe_mxfp4_unpack", st)
+
+
 def moe_w4a16_forward(x: torch.Tensor, E: int, I: int, top_k: int, block_m: int,
                       topk_weights: torch.Tensor, sorted_token_ids: torch.Tensor,
                       block_expert_ids: torch.Tensor, expert_offsets: torch.Tensor,
                       num_tokens_post_pad: torch.Tensor, w13_packed: torch.Tensor, w2_packed: torch.Tensor,
-                      workspace: torch.Tensor, out: torch.Tensor, cap: int | None = None, stream=None) -> None:
+                      workspace: torch.Tensor, out: torch.Tensor, cap: int | None = None, stream=None,
+                      _prefix: str = "moe_w4a16") -> None:
     M, H = x.shape
     if cap is None:
         cap = sorted_token_ids.numel()
-    st = lib().moe_w4a16_forward(
+    st = getattr(lib(), _prefix + "_forward")(
         _ptr(x, torch.bfloat16, "x"), M, E, H, I, top_k, block_m,
         _ptr(topk_weights, torch.float32, "topk_weights"),
         _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
@@ -182,39 +210,39 @@ def moe_w4a16_forward(x: torch.Tensor, E: int, I: int, top_k: int, block_m: int,
         _ptr(w13_packed, torch.uint8, "w13_packed"), _ptr(w2_packed, torch.uint8, "w2_packed"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
         _ptr(out, torch.bfloat16, "out"), _stream(stream))
-    _check("moe_w4a16_forward", st)
+    _check(_prefix + "_forward", st)
 
 
 def moe_w4a16_fc1(x: torch.Tensor, E: int, I: int, top_k: int, block_m: int, sorted_token_ids: torch.Tensor,
                   block_expert_ids: torch.Tensor, num_tokens_post_pad: torch.Tensor, w13_packed: torch.Tensor,
-                  workspace: torch.Tensor, cap: int | None = None, stream=None) -> None:
+                  workspace: torch.Tensor, cap: int | None = None, stream=None, _prefix: str = "moe_w4a16") -> None:
     M, H = x.shape
     if cap is None:
         cap = sorted_token_ids.numel()
-    st = lib().moe_w4a16_fc1(
+    st = getattr(lib(), _prefix + "_fc1")(
         _ptr(x, torch.bfloat16, "x"), M, E, H, I, top_k, block_m,
         _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
         _ptr(block_expert_ids, torch.int32, "block_expert_ids"),
         _ptr(num_tokens_post_pad, torch.int32, "num_tokens_post_pad"), cap,
         _ptr(w13_packed, torch.uint8, "w13_packed"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream))
-    _check("moe_w4a16_fc1", st)
+    _check(_prefix + "_fc1", st)
 
 
 def moe_w4a16_fc2(M: int, E: int, H: int, I: int, top_k: int, block_m: int, topk_weights: torch.Tensor,
                   sorted_token_ids: torch.Tensor, block_expert_ids: torch.Tensor,
                   num_tokens_post_pad: torch.Tensor, w2_packed: torch.Tensor, workspace: torch.Tensor,
-                  out: torch.Tensor, cap: int | None = None, stream=None) -> None:
+                  out: torch.Tensor, cap: int | None = None, stream=None, _prefix: str = "moe_w4a16") -> None:
     if cap is None:
         cap = sorted_token_ids.numel()
-    st = lib().moe_w4a16_fc2(
+    st = getattr(lib(), _prefix + "_fc2")(
         M, E, H, I, top_k, block_m, _ptr(topk_weights, torch.float32, "topk_weights"),
         _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
         _ptr(block_expert_ids, torch.int32, "block_expert_ids"),
         _ptr(num_tokens_post_pad, torch.int32, "num_tokens_post_pad"), cap,
         _ptr(w2_packed, torch.uint8, "w2_packed"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), _ptr(out, torch.bfloat16, "out"), _stream(stream))
-    _check("moe_w4a16_fc2", st)
+    _check(_prefix + "_fc2", st)
 
 
 def moe_w4a16_layer(logits: torch.Tensor, x: torch.Tensor, I: int, top_k: int, block_m: int,
@@ -222,7 +250,7 @@ def moe_w4a16_layer(logits: torch.Tensor, x: torch.Tensor, I: int, top_k: int, b
                     block_expert_ids: torch.Tensor, expert_offsets: torch.Tensor,
                     num_tokens_post_pad: torch.Tensor, w13_packed: torch.Tensor, w2_packed: torch.Tensor,
                     workspace: torch.Tensor, out: torch.Tensor, cap: int | None = None, stream=None,
-                    stage_events=None) -> None:
+                    stage_events=None, _prefix: str = "moe_w4a16") -> None:
     """stage_events: None or a pair of raw hipEvent_t handles (ints)."""
     M, E = logits.shape
     H = x.shape[1]
@@ -233,7 +261,7 @@ def moe_w4a16_layer(logits: torch.Tensor, x: torch.Tensor, I: int, top_k: int, b
     ev = None
     if stage_events is not None:
         ev = (ctypes.c_void_p * 2)(int(stage_events[0]), int(stage_events[1]))
-    st = lib().moe_w4a16_layer(
+    st = getattr(lib(), _prefix + "_layer")(
         _ptr(logits, torch.float32, "logits"), _ptr(x, torch.bfloat16, "x"), M, E, H, I, top_k, block_m,
         _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_weights, torch.float32, "topk_weights"),
         _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
@@ -243,4 +271,24 @@ def moe_w4a16_layer(logits: torch.Tensor, x: torch.Tensor, I: int, top_k: int, b
         _ptr(w13_packed, torch.uint8, "w13_packed"), _ptr(w2_packed, torch.uint8, "w2_packed"),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _ptr(out, torch.bfloat16, "out"),
         _stream(stream), ev)
-    _check("moe_w4a16_layer", st)
+    _check(_prefix + "_layer", st)
+
+
+def moe_mxfp4_forward(*args, **kw) -> None:
+    """moe_w4a16_forward with moe_mxfp4_repack weights."""
+    moe_w4a16_forward(*args, _prefix="moe_mxfp4", **kw)
+
+
+def moe_mxfp4_fc1(*args, **kw) -> None:
+    """moe_w4a16_fc1 with moe_mxfp4_repack weights."""
+    moe_w4a16_fc1(*args, _prefix="moe_mxfp4", **kw)
+
+
+def moe_mxfp4_fc2(*args, **kw) -> None:
+    """moe_w4a16_fc2 with moe_mxfp4_repack weights."""
+    moe_w4a16_fc2(*args, _prefix="moe_mxfp4", **kw)
+
+
+def moe_mxfp4_layer(*args, **kw) -> None:
+    """moe_w4a16_layer with moe_mxfp4_repack weights."""
+    moe_w4a16_layer(*args, _prefix="moe_mxfp4", **kw)

@@ -10,7 +10,7 @@ using moe::kChunkK;
 using moe::kGroup;
 using moe::kPairRows;
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr int32_t kMaxExperts = 1024;
 using moe::kMaxTopK;
 
@@ -39,6 +39,11 @@ int64_t capacity(int32_t M, int32_t E, int32_t k, int32_t block_m) {
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 }  // namespace
+
+// A launcher of the kernels for weight format `fmt` (moe::kFmtInt4 or
+// moe::kFmtMxfp4).
+#define FMT_CALL(fmt, fn, ...) \
+  ((fmt) == moe::kFmtMxfp4 ? moe::fmt_mxfp4::fn(__VA_ARGS__) : moe::fmt_int4::fn(__VA_ARGS__))
 
 extern "C" {
 
@@ -85,7 +90,12 @@ int moe_route_align(const float* logits, int32_t M, int32_t E, int32_t top_k, in
 
 int64_t moe_w4a16_packed_bytes(int32_t E, int32_t N, int32_t K, int32_t group) {
   if (E <= 0 || N <= 0 || K <= 0 || group != kGroup || N % kPairRows != 0 || K % kChunkK != 0) return -1;
-  return (int64_t)E * moe::packed_bytes_per_expert(N, K);
+  return (int64_t)E * moe::packed_bytes_fmt(moe::kFmtInt4, N, K);
+}
+
+int64_t moe_mxfp4_packed_bytes(int32_t E, int32_t N, int32_t K) {
+  if (E <= 0 || N <= 0 || K <= 0 || N % kPairRows != 0 || K % kChunkK != 0) return -1;
+  return (int64_t)E * moe::packed_bytes_fmt(moe::kFmtMxfp4, N, K);
 }
 
 static int check_repack(const void* a, const void* b, const void* c, int32_t E, int32_t N, int32_t K,
@@ -103,7 +113,15 @@ int moe_w4a16_repack(const uint8_t* qweight, const uint16_t* scales_f16, int32_t
                      int32_t group, int32_t kind, void* packed, void* stream) {
   const int st = check_repack(qweight, scales_f16, packed, E, N, K, group, kind);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_repack(qweight, scales_f16, E, N, K, kind, (uint8_t*)packed,
+  return hip_status(moe::launch_repack(moe::kFmtInt4, qweight, scales_f16, E, N, K, kind, (uint8_t*)packed,
+                                       (hipStream_t)stream));
+}
+
+int moe_mxfp4_repack(const uint8_t* qweight, const uint8_t* scales_e8m0, int32_t E, int32_t N, int32_t K,
+                     int32_t kind, void* packed, void* stream) {
+  const int st = check_repack(qweight, scales_e8m0, packed, E, N, K, kGroup, kind);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_repack(moe::kFmtMxfp4, qweight, scales_e8m0, E, N, K, kind, (uint8_t*)packed,
                                        (hipStream_t)stream));
 }
 
@@ -111,8 +129,16 @@ int moe_w4a16_unpack(const void* packed, int32_t E, int32_t N, int32_t K, int32_
                      uint8_t* qweight, uint16_t* scales_f16, void* stream) {
   const int st = check_repack(packed, qweight, scales_f16, E, N, K, group, kind);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_unpack((const uint8_t*)packed, E, N, K, kind, qweight, scales_f16,
+  return hip_status(moe::launch_unpack(moe::kFmtInt4, (const uint8_t*)packed, E, N, K, kind, qweight, scales_f16,
                                        (hipStream_t)stream));
+}
+
+int moe_mxfp4_unpack(const void* packed, int32_t E, int32_t N, int32_t K, int32_t kind, uint8_t* qweight,
+                     uint8_t* scales_e8m0, void* stream) {
+  const int st = check_repack(packed, qweight, scales_e8m0, E, N, K, kGroup, kind);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_unpack(moe::kFmtMxfp4, (const uint8_t*)packed, E, N, K, kind, qweight,
+                                       scales_e8m0, (hipStream_t)stream));
 }
 
 int64_t moe_w4a16_workspace_bytes(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
@@ -149,11 +175,11 @@ static int check_fc(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, i
 #ifndef MOE_TILED_MIN_PER_EXPERT
 #define MOE_TILED_MIN_PER_EXPERT 16.0
 #endif
-static bool use_tiled(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
-  return moe::tile_path_supported(H, I) && (double)M * top_k / E >= MOE_TILED_MIN_PER_EXPERT;
+static bool use_tiled(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
+  return FMT_CALL(fmt, tile_path_supported, H, I) && (double)M * top_k / E >= MOE_TILED_MIN_PER_EXPERT;
 }
 
-static moe::FcArgs fc_args(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
+static moe::FcArgs fc_args(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
                            int64_t cap, const int32_t* sorted_ids, const int32_t* block_expert,
                            const int32_t* npp, void* workspace) {
   moe::FcArgs a{};
@@ -167,15 +193,15 @@ static moe::FcArgs fc_args(int32_t M, int32_t E, int32_t H, int32_t I, int32_t t
   a.M = M; a.E = E; a.H = H; a.I = I; a.k = top_k; a.block_m = block_m;
   a.cap = cap;
   a.zero_words16 = (int64_t)M * H * 4 / 16;
-  if (use_tiled(M, E, H, I, top_k)) {
+  if (use_tiled(fmt, M, E, H, I, top_k)) {
     a.tiles = (int2*)(ws + L.tiles_off);
     a.ntiles = (int32_t*)(ws + L.ntiles_off);
-    a.max_tiles = (int)moe::tile_grid_tiles(M, E, top_k, block_m, cap);
+    a.max_tiles = (int)FMT_CALL(fmt, tile_grid_tiles, M, E, top_k, block_m, cap);
   }
   return a;
 }
 
-int moe_w4a16_fc1(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k,
+static int fc1_impl(int fmt, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k,
                   int32_t block_m, const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
                   const int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed, void* workspace,
                   int64_t workspace_bytes, void* stream) {
@@ -186,14 +212,14 @@ int moe_w4a16_fc1(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32
   if (!aligned16(x_bf16) || !aligned16(w13_packed) || !aligned16(workspace) || !aligned4(sorted_token_ids) ||
       !aligned4(block_expert_ids) || !aligned4(num_tokens_post_pad))
     return MOE_ERR_INVALID_ARG;
-  moe::FcArgs a = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
+  moe::FcArgs a = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
                           num_tokens_post_pad, workspace);
   a.act_in = x_bf16;
   a.wpacked = (const uint8_t*)w13_packed;
-  return hip_status(moe::launch_fc1(a, (hipStream_t)stream));
+  return hip_status(FMT_CALL(fmt, launch_fc1, a, (hipStream_t)stream));
 }
 
-int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
+static int fc2_impl(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
                   const float* topk_weights, const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
                   const int32_t* num_tokens_post_pad, int64_t cap, const void* w2_packed, void* workspace,
                   int64_t workspace_bytes, uint16_t* out_bf16, void* stream) {
@@ -205,17 +231,17 @@ int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int
   if (!aligned16(w2_packed) || !aligned16(workspace) || !aligned16(out_bf16) || !aligned4(topk_weights) ||
       !aligned4(sorted_token_ids) || !aligned4(block_expert_ids) || !aligned4(num_tokens_post_pad))
     return MOE_ERR_INVALID_ARG;
-  moe::FcArgs a = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
+  moe::FcArgs a = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
                           num_tokens_post_pad, workspace);
   a.act_in = a.act_out;  // FC2 reads the FC1 activations
   a.act_out = nullptr;
   a.wpacked = (const uint8_t*)w2_packed;
   a.topk_weights = topk_weights;
   a.out = out_bf16;
-  return hip_status(moe::launch_fc2(a, (hipStream_t)stream));
+  return hip_status(FMT_CALL(fmt, launch_fc2, a, (hipStream_t)stream));
 }
 
-int moe_w4a16_forward(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k,
+static int forward_impl(int fmt, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k,
                       int32_t block_m, const float* topk_weights, const int32_t* sorted_token_ids,
                       const int32_t* block_expert_ids, const int32_t* expert_offsets,
                       const int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed,
@@ -230,14 +256,14 @@ int moe_w4a16_forward(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, i
       !aligned16(out_bf16) || !aligned4(topk_weights) || !aligned4(sorted_token_ids) ||
       !aligned4(block_expert_ids) || !aligned4(expert_offsets) || !aligned4(num_tokens_post_pad))
     return MOE_ERR_INVALID_ARG;
-  st = moe_w4a16_fc1(x_bf16, M, E, H, I, top_k, block_m, sorted_token_ids, block_expert_ids,
-                     num_tokens_post_pad, cap, w13_packed, workspace, workspace_bytes, stream);
+  st = fc1_impl(fmt, x_bf16, M, E, H, I, top_k, block_m, sorted_token_ids, block_expert_ids,
+                num_tokens_post_pad, cap, w13_packed, workspace, workspace_bytes, stream);
   if (st != MOE_OK) return st;
-  return moe_w4a16_fc2(M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
-                       num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
+  return fc2_impl(fmt, M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
+                  num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
 }
 
-int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
+static int layer_impl(int fmt, const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
                     int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights,
                     int32_t* sorted_token_ids, int32_t* block_expert_ids, int32_t* expert_offsets,
                     int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed, const void* w2_packed,
@@ -258,10 +284,10 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
   hipEvent_t ev1 = stage_events ? (hipEvent_t)stage_events[1] : nullptr;
   // decode path for one or two tokens; then the routed FC1 while few experts
   // are touched; the decode path where it fits; else the four kernels
-  const bool routed = moe::routed_fc1_preferred(M, E, I, top_k);
+  const bool routed = FMT_CALL(fmt, routed_fc1_preferred, M, E, I, top_k);
   if (moe::decode_path_fits(M, H, I, top_k) && (M <= 2 || !routed)) {
     moe::DecodeArgs d{};
-    d.fc = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
+    d.fc = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
                    workspace);
     d.fc.act_in = x_bf16;
     d.fc.wpacked = (const uint8_t*)w13_packed;
@@ -276,12 +302,12 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
     d.expert_offsets = expert_offsets;
     d.npp_out = num_tokens_post_pad;
     d.block_m = block_m;
-    return hip_status(moe::launch_decode(d, s, ev0, ev1));
+    return hip_status(FMT_CALL(fmt, launch_decode, d, s, ev0, ev1));
   }
   const bool token_fc2 = moe::token_fc2_fits(M, E, I, top_k);
   if (routed) {  // routing and grouping inside FC1's workgroups
     moe::DecodeArgs d{};
-    d.fc = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
+    d.fc = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
                    workspace);
     d.fc.act_in = x_bf16;
     d.fc.wpacked = (const uint8_t*)w13_packed;
@@ -294,21 +320,21 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
     d.expert_offsets = expert_offsets;
     d.npp_out = num_tokens_post_pad;
     d.block_m = block_m;
-    st = hip_status(moe::launch_fc1_routed(d, s, ev0, ev1));
+    st = hip_status(FMT_CALL(fmt, launch_fc1_routed, d, s, ev0, ev1));
   } else {
     st = moe_route_align(logits, M, E, top_k, block_m, topk_ids, topk_weights, sorted_token_ids, block_expert_ids,
                          expert_offsets, num_tokens_post_pad, cap, stream);
     if (st != MOE_OK) return st;
-    moe::FcArgs a = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
+    moe::FcArgs a = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
                             num_tokens_post_pad, workspace);
     a.act_in = x_bf16;
     a.wpacked = (const uint8_t*)w13_packed;
-    st = hip_status(moe::launch_fc1(a, s, ev0, ev1));
+    st = hip_status(FMT_CALL(fmt, launch_fc1, a, s, ev0, ev1));
   }
   if (st != MOE_OK) return st;
   if (token_fc2) {  // small batches: FC2 per token, no accumulator
     moe::DecodeArgs d2{};
-    d2.fc = fc_args(M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
+    d2.fc = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
                     workspace);
     d2.fc.act_in = d2.fc.act_out;  // FC1's activations
     d2.fc.act_out = nullptr;
@@ -316,10 +342,80 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
     d2.fc.out = out_bf16;
     d2.topk_ids = topk_ids;
     d2.topk_weights = topk_weights;
-    return hip_status(moe::launch_fc2_tokens(d2, s));
+    return hip_status(FMT_CALL(fmt, launch_fc2_tokens, d2, s));
   }
-  return moe_w4a16_fc2(M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
-                       num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
+  return fc2_impl(fmt, M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
+                  num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
+}
+
+int moe_w4a16_fc1(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
+              const int32_t* sorted_token_ids, const int32_t* block_expert_ids, const int32_t* num_tokens_post_pad,
+              int64_t cap, const void* w13_packed, void* workspace, int64_t workspace_bytes, void* stream) {
+  return fc1_impl(moe::kFmtInt4, x_bf16, M, E, H, I, top_k, block_m, sorted_token_ids, block_expert_ids,
+                  num_tokens_post_pad, cap, w13_packed, workspace, workspace_bytes, stream);
+}
+
+int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m, const float* topk_weights,
+              const int32_t* sorted_token_ids, const int32_t* block_expert_ids, const int32_t* num_tokens_post_pad,
+              int64_t cap, const void* w2_packed, void* workspace, int64_t workspace_bytes, uint16_t* out_bf16,
+              void* stream) {
+  return fc2_impl(moe::kFmtInt4, M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
+                  num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
+}
+
+int moe_w4a16_forward(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
+                  const float* topk_weights, const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
+                  const int32_t* expert_offsets, const int32_t* num_tokens_post_pad, int64_t cap,
+                  const void* w13_packed, const void* w2_packed, void* workspace, int64_t workspace_bytes,
+                  uint16_t* out_bf16, void* stream) {
+  return forward_impl(moe::kFmtInt4, x_bf16, M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
+                      expert_offsets, num_tokens_post_pad, cap, w13_packed, w2_packed, workspace, workspace_bytes,
+                      out_bf16, stream);
+}
+
+int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
+                int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights, int32_t* sorted_token_ids,
+                int32_t* block_expert_ids, int32_t* expert_offsets, int32_t* num_tokens_post_pad, int64_t cap,
+                const void* w13_packed, const void* w2_packed, void* workspace, int64_t workspace_bytes,
+                uint16_t* out_bf16, void* stream, void* const* stage_events) {
+  return layer_impl(moe::kFmtInt4, logits, x_bf16, M, E, H, I, top_k, block_m, topk_ids, topk_weights, sorted_token_ids,
+                    block_expert_ids, expert_offsets, num_tokens_post_pad, cap, w13_packed, w2_packed, workspace,
+                    workspace_bytes, out_bf16, stream, stage_events);
+}
+
+int moe_mxfp4_fc1(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
+              const int32_t* sorted_token_ids, const int32_t* block_expert_ids, const int32_t* num_tokens_post_pad,
+              int64_t cap, const void* w13_packed, void* workspace, int64_t workspace_bytes, void* stream) {
+  return fc1_impl(moe::kFmtMxfp4, x_bf16, M, E, H, I, top_k, block_m, sorted_token_ids, block_expert_ids,
+                  num_tokens_post_pad, cap, w13_packed, workspace, workspace_bytes, stream);
+}
+
+int moe_mxfp4_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m, const float* topk_weights,
+              const int32_t* sorted_token_ids, const int32_t* block_expert_ids, const int32_t* num_tokens_post_pad,
+              int64_t cap, const void* w2_packed, void* workspace, int64_t workspace_bytes, uint16_t* out_bf16,
+              void* stream) {
+  return fc2_impl(moe::kFmtMxfp4, M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
+                  num_tokens_post_pad, cap, w2_packed, workspace, workspace_bytes, out_bf16, stream);
+}
+
+int moe_mxfp4_forward(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
+                  const float* topk_weights, const int32_t* sorted_token_ids, const int32_t* block_expert_ids,
+                  const int32_t* expert_offsets, const int32_t* num_tokens_post_pad, int64_t cap,
+                  const void* w13_packed, const void* w2_packed, void* workspace, int64_t workspace_bytes,
+                  uint16_t* out_bf16, void* stream) {
+  return forward_impl(moe::kFmtMxfp4, x_bf16, M, E, H, I, top_k, block_m, topk_weights, sorted_token_ids, block_expert_ids,
+                      expert_offsets, num_tokens_post_pad, cap, w13_packed, w2_packed, workspace, workspace_bytes,
+                      out_bf16, stream);
+}
+
+int moe_mxfp4_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
+                int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights, int32_t* sorted_token_ids,
+                int32_t* block_expert_ids, int32_t* expert_offsets, int32_t* num_tokens_post_pad, int64_t cap,
+                const void* w13_packed, const void* w2_packed, void* workspace, int64_t workspace_bytes,
+                uint16_t* out_bf16, void* stream, void* const* stage_events) {
+  return layer_impl(moe::kFmtMxfp4, logits, x_bf16, M, E, H, I, top_k, block_m, topk_ids, topk_weights, sorted_token_ids,
+                    block_expert_ids, expert_offsets, num_tokens_post_pad, cap, w13_packed, w2_packed, workspace,
+                    workspace_bytes, out_bf16, stream, stage_events);
 }
 
 }  // extern "C"

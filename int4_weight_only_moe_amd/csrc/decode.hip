@@ -38,6 +38,7 @@
 #include "route_common.h"
 
 namespace moe {
+namespace MOE_FMT_NS {
 namespace {
 
 constexpr int kDecKSplit = 4;   // FC1 waves per workgroup (split K)
@@ -81,9 +82,12 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
   const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(2 * I, H) +
                          ((int64_t)pair * nkc + wave) * kPairChunkBytes;
   const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
-  // lanes 16..63 read their scales out of range: zeros, no memory access
-  const uint32_t os0 = lane < 16 ? kTileNibbleBytes + 8u * lane : kOutOfRange;
-  const uint32_t os1 = lane < 16 ? kTileBytes + kTileNibbleBytes + 8u * lane : kOutOfRange;
+  // INT4: lanes 16..63 read their scales out of range (zeros, no memory
+  // access): the scale multiplies D rows, which lanes 0..15 hold. FP4: the
+  // scale enters the B operand, whose column lane % 16 every lane supplies.
+  const bool own_scales = kFmt == kFmtMxfp4 || lane < 16;
+  const uint32_t os0 = own_scales ? kTileNibbleBytes + kScaleRowBytes * (lane & 15) : kOutOfRange;
+  const uint32_t os1 = own_scales ? kTileBytes + kTileNibbleBytes + kScaleRowBytes * (lane & 15) : kOutOfRange;
 
   // x of this lane's row, at this wave's first chunk and this lane's K offset
   const int xrow = (lane & 15) < MR ? (lane & 15) : 0;
@@ -99,8 +103,8 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
     WChunk w;
     w.q0 = bload16<kPolicyWeights>(wr, oq0);
     w.q1 = bload16<kPolicyWeights>(wr, oq1);
-    w.s0 = bload8<kPolicyWeights>(wr, os0);
-    w.s1 = bload8<kPolicyWeights>(wr, os1);
+    w.s0 = load_scales<kPolicyWeights>(wr, os0);
+    w.s1 = load_scales<kPolicyWeights>(wr, os1);
     return w;
   };
 
@@ -112,22 +116,20 @@ __device__ __forceinline__ void fc1_decode_body(const DecodeArgs& d, const uint4
   auto chunk = [&](const WChunk& w, int c) {
     const uint32_t q0[4] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w};
     const uint32_t q1[4] = {w.q1.x, w.q1.y, w.q1.z, w.q1.w};
-    const uint32_t s0w[2] = {w.s0.x, w.s0.y};
-    const uint32_t s1w[2] = {w.s1.x, w.s1.y};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bf16x8_t xv = as_bf16x8(xl[c * kDecKSplit * (kChunkK / 8) + 4 * j]);
-      const bf16x8_t b0 = dequant_u4_plus128(q0[j]);
-      const bf16x8_t b1 = dequant_u4_plus128(q1[j]);
-      const float g0 = f16_bits_to_f32((s0w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-      const float g1 = f16_bits_to_f32((s1w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-      const f32x4_t off = cr[c * kDecKSplit * (kChunkK / kGroup) + j];
+      const float g0 = group_scale(w.s0, j);
+      const float g1 = group_scale(w.s1, j);
+      const bf16x8_t b0 = dequant_group(q0[j], g0);
+      const bf16x8_t b1 = dequant_group(q1[j], g1);
+      const f32x4_t off = group_c(cr[c * kDecKSplit * (kChunkK / kGroup) + j]);
       const f32x4_t t0 = mfma16x16x32(xv, b0, off);
       const f32x4_t t1 = mfma16x16x32(xv, b1, off);
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
-        acc0[i] = __builtin_fmaf(t0[i], g0, acc0[i]);
-        acc1[i] = __builtin_fmaf(t1[i], g1, acc1[i]);
+        acc0[i] = group_add(acc0[i], t0[i], g0);
+        acc1[i] = group_add(acc1[i], t1[i], g1);
       }
     }
   };
@@ -344,23 +346,28 @@ void fc1_decode_kernel(DecodeArgs d) {
 }
 
 // One 16-row tile of a pair, for one activation row (D row 0, lanes 0..15):
-// per group, one MFMA of the row with the codes (q + 136), all four issued
-// back to back; then each group's -136 * (group sum) correction (cr, one
-// float per group, the same for every lane) is added and the sum scaled
-// into that group's own running sum (no dependence between the groups).
+// per group, one MFMA of the row with the codes (INT4: q + 136; FP4: the
+// scaled values), all four issued back to back; then, for INT4, each group's
+// -136 * (group sum) correction (cr, one float per group, the same for every
+// lane) is added and the sum scaled; each group keeps its own running sum
+// (no dependence between the groups).
 __device__ __forceinline__ void mma_chunk_tile(uint4 q, uint2 sc, const uint4 (&xa)[4], const float4 cr,
                                                float (&accj)[4]) {
   const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
-  const uint32_t sw[2] = {sc.x, sc.y};
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  float g[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) g[j] = group_scale(sc, j);
   f32x4_t t[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) t[j] = mfma16x16x32(as_bf16x8(xa[j]), dequant_u4_plus128(qq[j]), zero4);
+  for (int j = 0; j < 4; ++j) t[j] = mfma16x16x32(as_bf16x8(xa[j]), dequant_group(qq[j], g[j]), zero4);
   const float crj[4] = {cr.x, cr.y, cr.z, cr.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float g = f16_bits_to_f32((sw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-    accj[j] = __builtin_fmaf(t[j][0] + crj[j], g, accj[j]);
+    if constexpr (kFmt == kFmtMxfp4)
+      accj[j] += t[j][0];  // the scale is in the B operand; FP4 needs no correction
+    else
+      accj[j] = __builtin_fmaf(t[j][0] + crj[j], g[j], accj[j]);
   }
 }
 
@@ -408,9 +415,11 @@ void fc2_decode_kernel(DecodeArgs d) {
   const int n = I / kChunkK;
   const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(H, I) +
                          (int64_t)pair * n * kPairChunkBytes + h * kTileBytes;
-  // Only D row 0 (lanes 0..15) is used: lanes 16..63 read their scales out of
-  // range (zeros, no memory access).
-  const uint32_t oq = 16u * lane, os = lane < 16 ? kTileNibbleBytes + 8u * lane : kOutOfRange;
+  // Only D row 0 (lanes 0..15) is used: for INT4 lanes 16..63 read their
+  // scales out of range (zeros, no memory access); FP4 scales enter the B
+  // operand, whose column lane % 16 every lane supplies.
+  const uint32_t oq = 16u * lane;
+  const uint32_t os = (kFmt == kFmtMxfp4 || lane < 16) ? kTileNibbleBytes + kScaleRowBytes * (lane & 15) : kOutOfRange;
   uint4* dst = xrows + j * row16;
   float* corr = reinterpret_cast<float*>(xrows + k * row16) + j * ng;
 
@@ -421,7 +430,7 @@ void fc2_decode_kernel(DecodeArgs d) {
     const __amdgpu_buffer_rsrc_t wr =
         make_rsrc(wbase + (int64_t)c * kPairChunkBytes, c < n ? (uint32_t)kTileBytes : 0u);
     qb[slot] = bload16<kPolicyWeights>(wr, oq);
-    sb[slot] = bload8<kPolicyWeights>(wr, os);
+    sb[slot] = load_scales<kPolicyWeights>(wr, os);
   };
   // Issue order: the activation row, then the first P2 weight chunks, so that
   // staging the row waits only for its own loads.
@@ -567,4 +576,5 @@ hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t e0,
   return launch_decode_vpl<16>(d, stream, e0, e1);
 }
 
+}  // namespace MOE_FMT_NS
 }  // namespace moe

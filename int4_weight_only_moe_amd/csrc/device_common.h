@@ -40,6 +40,21 @@ __device__ __forceinline__ bf16x8_t dequant_u4_plus128(uint32_t w) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(p0, p1, p2, p3));
 }
 
+// Eight FP4 e2m1 codes (byte b holds codes 2b, 2b+1, low nibble first)
+// become eight bf16 values code * 2^e, where e is the exponent field of
+// `scale` (gfx950's conversion uses only the scale's exponent bits; an E8M0
+// byte shifted into them gives exactly 2^(byte - 127), byte 0 included).
+// Exact whenever the product is a bf16 value.
+__device__ __forceinline__ bf16x8_t dequant_fp4(uint32_t w, float scale) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)));
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // D(16x16, fp32) = A(16x32) * B(32x16) + C on the bf16 matrix cores.

@@ -36,6 +36,7 @@
 #include "route_common.h"
 
 namespace moe {
+namespace MOE_FMT_NS {
 namespace {
 
 template <int S, int KSPLIT, int P, int NCH, bool kFc1>
@@ -119,14 +120,15 @@ __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const
   const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(N, K) + (int64_t)pair * n * kPairChunkBytes;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)n * kPairChunkBytes);
   const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
-  const uint32_t os0 = kTileNibbleBytes + 8u * (lane & 15), os1 = kTileBytes + kTileNibbleBytes + 8u * (lane & 15);
+  const uint32_t os0 = kTileNibbleBytes + kScaleRowBytes * (lane & 15);
+  const uint32_t os1 = kTileBytes + kTileNibbleBytes + kScaleRowBytes * (lane & 15);
   auto load_w = [&](int c) {
     const uint32_t base = (uint32_t)c * kPairChunkBytes;  // past the K range: zeros
     WChunk w;
     w.q0 = bload16<kPolicy>(wr, base + oq0);
     w.q1 = bload16<kPolicy>(wr, base + oq1);
-    w.s0 = bload8<kPolicy>(wr, base + os0);
-    w.s1 = bload8<kPolicy>(wr, base + os1);
+    w.s0 = load_scales<kPolicy>(wr, base + os0);
+    w.s1 = load_scales<kPolicy>(wr, base + os1);
     return w;
   };
   // The weight stream goes out first: it does not wait for the row ids that
@@ -187,25 +189,23 @@ __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const
         const WChunk w = wb[j];
         const uint32_t q0[4] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w};
         const uint32_t q1[4] = {w.q1.x, w.q1.y, w.q1.z, w.q1.w};
-        const uint32_t s0w[2] = {w.s0.x, w.s0.y};
-        const uint32_t s1w[2] = {w.s1.x, w.s1.y};
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const bf16x8_t b0 = dequant_u4_plus128(q0[g]);
-          const bf16x8_t b1 = dequant_u4_plus128(q1[g]);
-          const float g0 = f16_bits_to_f32((s0w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
-          const float g1 = f16_bits_to_f32((s1w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
+          const float g0 = group_scale(w.s0, g);
+          const float g1 = group_scale(w.s1, g);
+          const bf16x8_t b0 = dequant_group(q0[g], g0);
+          const bf16x8_t b1 = dequant_group(q1[g], g1);
 #pragma unroll
           for (int s = 0; s < S; ++s) {
             if (s > 0 && !sact[s]) continue;
             const bf16x8_t xv = as_bf16x8(xt[slot][16 * s + mrow][4 * g + kv]);
-            const f32x4_t off = xs4[slot][g][4 * s + kv];
+            const f32x4_t off = group_c(xs4[slot][g][4 * s + kv]);
             const f32x4_t t0 = mfma16x16x32(xv, b0, off);
             const f32x4_t t1 = mfma16x16x32(xv, b1, off);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              acc0[s][i] = __builtin_fmaf(t0[i], g0, acc0[s][i]);
-              acc1[s][i] = __builtin_fmaf(t1[i], g1, acc1[s][i]);
+              acc0[s][i] = group_add(acc0[s][i], t0[i], g0);
+              acc1[s][i] = group_add(acc1[s][i], t1[i], g1);
             }
           }
           // keep the LDS reads of later groups from being hoisted (register pressure)
@@ -396,7 +396,8 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
   const int64_t wexp = packed_bytes_per_expert(2 * a.I, H);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.act_in, (uint32_t)M * (uint32_t)H * 2u);
   const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
-  const uint32_t os0 = kTileNibbleBytes + 8u * (lane & 15), os1 = kTileBytes + kTileNibbleBytes + 8u * (lane & 15);
+  const uint32_t os0 = kTileNibbleBytes + kScaleRowBytes * (lane & 15);
+  const uint32_t os1 = kTileBytes + kTileNibbleBytes + kScaleRowBytes * (lane & 15);
 
   auto work_of = [&](int item) {
     const int blk = item / ipb;
@@ -418,8 +419,8 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
     WChunk w;
     w.q0 = bload16<kPolicyWeights>(wr, oq0);
     w.q1 = bload16<kPolicyWeights>(wr, oq1);
-    w.s0 = bload8<kPolicyWeights>(wr, os0);
-    w.s1 = bload8<kPolicyWeights>(wr, os1);
+    w.s0 = load_scales<kPolicyWeights>(wr, os0);
+    w.s1 = load_scales<kPolicyWeights>(wr, os1);
     return w;
   };
   auto load_x = [&](uint4 (&xa)[1][4], const RoutedWork& r, int c) {
@@ -654,4 +655,5 @@ hipError_t launch_fc1_routed(const DecodeArgs& d, hipStream_t stream, hipEvent_t
   return launch_routed_vpl<16>(d, stream, ev_start, ev_stop);
 }
 
+}  // namespace MOE_FMT_NS
 }  // namespace moe

@@ -7,6 +7,7 @@
 #include "device_common.h"
 
 namespace moe {
+namespace MOE_FMT_NS {
 
 constexpr uint32_t kNeg136Pair = 0xC308C308u;  // two bf16 -136.0
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset that reads zeros
@@ -55,9 +56,57 @@ __device__ __forceinline__ float group_corr_quad(uint4 v) {
   return -136.0f * sum;
 }
 
+template <int kPolicy = kPolicyDefault>
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kPolicy);
+}
+
+// Format-dependent pieces of a group's product. A tile row's 4 group scales
+// take kScaleRowBytes (fp16: 8, E8M0: 4) at kTileNibbleBytes + row * that.
+constexpr uint32_t kScaleRowBytes = kTileScaleBytes / kTileRows;
+template <int kPolicy = kPolicyDefault>
+__device__ __forceinline__ uint2 load_scales(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (kFmt == kFmtMxfp4)
+    return make_uint2(bload4<kPolicy>(r, off), 0u);
+  else
+    return bload8<kPolicy>(r, off);
+}
+// Scale of group j (0..3) from a row's loaded scales: the fp16 value, or the
+// E8M0 byte placed in an fp32 exponent field (the form dequant_fp4 takes).
+__device__ __forceinline__ float group_scale(uint2 sw, int j) {
+  if constexpr (kFmt == kFmtMxfp4)
+    return __uint_as_float(((sw.x >> (8 * j)) & 0xFFu) << 23);
+  else
+    return f16_bits_to_f32(((j < 2 ? sw.x : sw.y) >> (16 * (j & 1))) & 0xFFFFu);
+}
+// The B operand of one group (8 codes of one dword): INT4 as q + 136 (the
+// scale is applied to the MFMA result), FP4 already scaled (exact).
+__device__ __forceinline__ bf16x8_t dequant_group(uint32_t q, float scale) {
+  if constexpr (kFmt == kFmtMxfp4)
+    return dequant_fp4(q, scale);
+  else
+    return dequant_u4_plus128(q);
+}
+// The MFMA accumulator input of a group: INT4 needs -136 * sum(x); FP4 codes
+// carry no offset.
+__device__ __forceinline__ f32x4_t group_c(f32x4_t corr) {
+  if constexpr (kFmt == kFmtMxfp4)
+    return f32x4_t{0.f, 0.f, 0.f, 0.f};
+  else
+    return corr;
+}
+// A running sum plus one group's MFMA result t: scaled by the group scale
+// (INT4) or as is (FP4: the scale is in the B operand).
+__device__ __forceinline__ float group_add(float acc, float t, float g) {
+  if constexpr (kFmt == kFmtMxfp4)
+    return acc + t;
+  else
+    return __builtin_fmaf(t, g, acc);
+}
+
 struct WChunk {
-  uint4 q0, q1;  // nibbles of the two tiles of a pair, 16 B per lane each
-  uint2 s0, s1;  // the 4 group scales of row (lane % 16) of each tile
+  uint4 q0, q1;  // codes of the two tiles of a pair, 16 B per lane each
+  uint2 s0, s1;  // the 4 group scales of row (lane % 16) of each tile (E8M0: in s.x)
 };
 
 // One chunk = 4 groups: per group, widen both tiles' codes, then per active
@@ -68,25 +117,23 @@ __device__ __forceinline__ void mma_chunk(const WChunk& w, const uint4 (&xa)[S][
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t q0[4] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w};
   const uint32_t q1[4] = {w.q1.x, w.q1.y, w.q1.z, w.q1.w};
-  const uint32_t s0w[2] = {w.s0.x, w.s0.y};
-  const uint32_t s1w[2] = {w.s1.x, w.s1.y};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const bf16x8_t b0 = dequant_u4_plus128(q0[j]);
-    const bf16x8_t b1 = dequant_u4_plus128(q1[j]);
-    const float g0 = f16_bits_to_f32((s0w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-    const float g1 = f16_bits_to_f32((s1w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+    const float g0 = group_scale(w.s0, j);
+    const float g1 = group_scale(w.s1, j);
+    const bf16x8_t b0 = dequant_group(q0[j], g0);
+    const bf16x8_t b1 = dequant_group(q1[j], g1);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       if (s > 0 && !sact[s]) continue;  // sub-tile 0 always holds a row
       const bf16x8_t xv = as_bf16x8(xa[s][j]);
-      const f32x4_t off = mfma16x16x32(xv, neg136, zero4);
+      const f32x4_t off = group_c(mfma16x16x32(xv, neg136, zero4));
       const f32x4_t t0 = mfma16x16x32(xv, b0, off);
       const f32x4_t t1 = mfma16x16x32(xv, b1, off);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc0[s][i] = __builtin_fmaf(t0[i], g0, acc0[s][i]);
-        acc1[s][i] = __builtin_fmaf(t1[i], g1, acc1[s][i]);
+        acc0[s][i] = group_add(acc0[s][i], t0[i], g0);
+        acc1[s][i] = group_add(acc1[s][i], t1[i], g1);
       }
     }
   }
@@ -169,7 +216,8 @@ __device__ __forceinline__ void fc_block(const FcArgs& a, const int e, const int
   const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(N, K) +
                          ((int64_t)pair * nkc + kc0) * kPairChunkBytes;
   const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
-  const uint32_t os0 = kTileNibbleBytes + 8u * (lane & 15), os1 = kTileBytes + kTileNibbleBytes + 8u * (lane & 15);
+  const uint32_t os0 = kTileNibbleBytes + kScaleRowBytes * (lane & 15);
+  const uint32_t os1 = kTileBytes + kTileNibbleBytes + kScaleRowBytes * (lane & 15);
 
   // One buffer descriptor per chunk (scalar arithmetic), so the per-lane
   // offsets stay four constant registers; a chunk at or past n has no bytes
@@ -180,8 +228,8 @@ __device__ __forceinline__ void fc_block(const FcArgs& a, const int e, const int
     WChunk w;
     w.q0 = bload16<kPolicyWeights>(wr, oq0);
     w.q1 = bload16<kPolicyWeights>(wr, oq1);
-    w.s0 = bload8<kPolicyWeights>(wr, os0);
-    w.s1 = bload8<kPolicyWeights>(wr, os1);
+    w.s0 = load_scales<kPolicyWeights>(wr, os0);
+    w.s1 = load_scales<kPolicyWeights>(wr, os1);
     return w;
   };
   auto load_x = [&](uint4 (&xa)[S][4], int c) {
@@ -260,4 +308,5 @@ __device__ __forceinline__ void fc_block(const FcArgs& a, const int e, const int
 }
 
 
+}  // namespace MOE_FMT_NS
 }  // namespace moe

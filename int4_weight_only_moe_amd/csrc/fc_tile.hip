@@ -41,6 +41,7 @@
 #include "fc_common.h"
 
 namespace moe {
+namespace MOE_FMT_NS {
 namespace {
 
 constexpr int kTW = 8;                     // waves (= tile pairs) per workgroup
@@ -119,14 +120,15 @@ __device__ __forceinline__ void fc_tile_body(const FcArgs& a, const int e, const
   const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(N, K) + (int64_t)pair * n * kPairChunkBytes;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)n * kPairChunkBytes);
   const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
-  const uint32_t os0 = kTileNibbleBytes + 8u * (lane & 15), os1 = kTileBytes + kTileNibbleBytes + 8u * (lane & 15);
+  const uint32_t os0 = kTileNibbleBytes + kScaleRowBytes * (lane & 15);
+  const uint32_t os1 = kTileBytes + kTileNibbleBytes + kScaleRowBytes * (lane & 15);
   auto load_w = [&](int c) {
     const uint32_t base = (uint32_t)c * kPairChunkBytes;  // past the K range: zeros
     WChunk w;
     w.q0 = bload16<kPolicy>(wr, base + oq0);
     w.q1 = bload16<kPolicy>(wr, base + oq1);
-    w.s0 = bload8<kPolicy>(wr, base + os0);
-    w.s1 = bload8<kPolicy>(wr, base + os1);
+    w.s0 = load_scales<kPolicy>(wr, base + os0);
+    w.s1 = load_scales<kPolicy>(wr, base + os1);
     return w;
   };
 
@@ -196,14 +198,23 @@ __device__ __forceinline__ void fc_tile_body(const FcArgs& a, const int e, const
         const WChunk w = wb[j];
         const uint32_t q0[4] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w};
         const uint32_t q1[4] = {w.q1.x, w.q1.y, w.q1.z, w.q1.w};
-        const uint32_t s0w[2] = {w.s0.x, w.s0.y};
-        const uint32_t s1w[2] = {w.s1.x, w.s1.y};
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const bf16x8_t b0 = dequant_u4_plus128(q0[g]);
-          const bf16x8_t b1 = dequant_u4_plus128(q1[g]);
-          const float g0 = f16_bits_to_f32((s0w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
-          const float g1 = f16_bits_to_f32((s1w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
+          const float g0 = group_scale(w.s0, g);
+          const float g1 = group_scale(w.s1, g);
+          const bf16x8_t b0 = dequant_group(q0[g], g0);
+          const bf16x8_t b1 = dequant_group(q1[g], g1);
+          if constexpr (kFmt == kFmtMxfp4) {
+            // FP4: the scale is in the B operand, so each MFMA accumulates
+            // straight into its sub-tile's sums (no vector work per output)
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+              const bf16x8_t xv = as_bf16x8(xt[slot][16 * s + mrow][4 * g + kv]);
+              acc0[s] = mfma16x16x32(xv, b0, acc0[s]);
+              acc1[s] = mfma16x16x32(xv, b1, acc1[s]);
+            }
+            continue;
+          }
           // Sub-tiles one after another, software-pipelined: step s issues
           // the MFMAs of sub-tile s (and the correction of s + 1), then the
           // scale FMAs of sub-tile s - 1, which run on the vector unit while
@@ -339,4 +350,5 @@ hipError_t launch_fc_tiled(const FcArgs& a, hipStream_t stream, hipEvent_t e0, h
 template hipError_t launch_fc_tiled<true>(const FcArgs&, hipStream_t, hipEvent_t, hipEvent_t);
 template hipError_t launch_fc_tiled<false>(const FcArgs&, hipStream_t, hipEvent_t, hipEvent_t);
 
+}  // namespace MOE_FMT_NS
 }  // namespace moe

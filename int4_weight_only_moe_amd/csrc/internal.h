@@ -8,9 +8,27 @@
 
 namespace moe {
 
-// Device layout of the repacked INT4 weights.
-//   A "tile" is 16 rows x 128 input channels: 1024 bytes of nibbles followed
-//   by 128 bytes of fp16 scales (16 rows x 4 groups of 32).
+// Weight formats. kFmtInt4: INT4 codes (offset binary, q = u - 8), one fp16
+// scale per 32 channels. kFmtMxfp4: FP4 e2m1 codes, one E8M0 scale
+// (2^(s - 127)) per 32 channels. The grouped-GEMM sources (fc.hip,
+// fc_tile.hip, decode.hip) are compiled once per format: MOE_WEIGHT_FORMAT
+// selects it (the *_mxfp4.hip wrappers set 1), and their format-dependent
+// code lives in the namespace MOE_FMT_NS.
+constexpr int kFmtInt4 = 0;
+constexpr int kFmtMxfp4 = 1;
+#ifndef MOE_WEIGHT_FORMAT
+#define MOE_WEIGHT_FORMAT 0
+#endif
+#if MOE_WEIGHT_FORMAT == 1
+#define MOE_FMT_NS fmt_mxfp4
+#else
+#define MOE_FMT_NS fmt_int4
+#endif
+constexpr int kFmt = MOE_WEIGHT_FORMAT;  // the format this translation unit's kernels read
+
+// Device layout of the repacked weights.
+//   A "tile" is 16 rows x 128 input channels: 1024 bytes of codes followed
+//   by the scales of 16 rows x 4 groups of 32 (fp16: 128 bytes, E8M0: 64).
 //   A "pair" is two tiles read together by one wave: for W13 the gate rows
 //   [16r, 16r+16) and the up rows I + [16r, 16r+16); for W2 the rows
 //   [32r, 32r+16) and [32r+16, 32r+32).
@@ -20,13 +38,18 @@ constexpr int kGroup = 32;
 constexpr int kTileRows = 16;
 constexpr int kChunkK = 128;                 // input channels per tile
 constexpr int kTileNibbleBytes = 1024;       // 16 x 128 / 2
-constexpr int kTileScaleBytes = 128;         // 16 x 4 x 2
-constexpr int kTileBytes = kTileNibbleBytes + kTileScaleBytes;
+__host__ __device__ constexpr int tile_scale_bytes(int fmt) { return fmt == kFmtMxfp4 ? 64 : 128; }
 constexpr int kPairRows = 32;
+// format-dependent sizes, of this translation unit's format (internal linkage)
+constexpr int kTileScaleBytes = tile_scale_bytes(kFmt);
+constexpr int kTileBytes = kTileNibbleBytes + kTileScaleBytes;
 constexpr int kPairChunkBytes = 2 * kTileBytes;
 
-__host__ __device__ inline int64_t packed_bytes_per_expert(int64_t N, int64_t K) {
-  return (N / kPairRows) * (K / kChunkK) * kPairChunkBytes;
+__host__ __device__ constexpr int64_t packed_bytes_fmt(int fmt, int64_t N, int64_t K) {
+  return (N / kPairRows) * (K / kChunkK) * 2 * (kTileNibbleBytes + tile_scale_bytes(fmt));
+}
+static __host__ __device__ inline int64_t packed_bytes_per_expert(int64_t N, int64_t K) {
+  return packed_bytes_fmt(kFmt, N, K);
 }
 
 // Tiles of the tiled grouped GEMM (fc_tile.hip): up to 128 rows of one
@@ -62,10 +85,11 @@ hipError_t launch_route_align(const float* logits, int M, int E, int k, int bloc
                               int32_t* block_expert, int32_t* offsets, int32_t* npp,
                               int64_t cap, hipStream_t stream);
 
-hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int E, int N, int K, int kind,
+// s: fp16 scales (kFmtInt4) or E8M0 bytes (kFmtMxfp4), [E, N, K/32].
+hipError_t launch_repack(int fmt, const uint8_t* q, const void* s, int E, int N, int K, int kind,
                          uint8_t* packed, hipStream_t stream);
-hipError_t launch_unpack(const uint8_t* packed, int E, int N, int K, int kind, uint8_t* q,
-                         uint16_t* s, hipStream_t stream);
+hipError_t launch_unpack(int fmt, const uint8_t* packed, int E, int N, int K, int kind, uint8_t* q,
+                         void* s, hipStream_t stream);
 
 struct FcArgs {
   const uint16_t* act_in;      // FC1: x [M, H]; FC2: act [M*k, I]
@@ -85,19 +109,6 @@ struct FcArgs {
   int32_t* ntiles;              // [1]
   int max_tiles;                // grid tiles (a multiple of 8)
 };
-
-// ev_start / ev_stop (may be null) take the FC1 kernel's own start and end
-// timestamps (hipExtLaunchKernel), for timing the stage without extra packets.
-hipError_t launch_fc1(const FcArgs& a, hipStream_t stream, hipEvent_t ev_start = nullptr,
-                      hipEvent_t ev_stop = nullptr);
-hipError_t launch_fc2(const FcArgs& a, hipStream_t stream);
-
-// Tiled path (fc_tile.hip).
-bool tile_path_supported(int64_t H, int64_t I);
-int64_t tile_grid_tiles(int64_t M, int64_t E, int64_t k, int64_t block_m, int64_t cap);
-hipError_t launch_tile_plan(const FcArgs& a, hipStream_t stream);
-template <bool kFc1>
-hipError_t launch_fc_tiled(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1);
 
 // Decode path (tiny batches): routing fused into FC1, output-stationary FC2.
 constexpr int kMaxTopK = 16;
@@ -128,11 +139,6 @@ struct DecodeArgs {
   int32_t* npp_out;        // [1]
   int block_m;
 };
-// ev_start / ev_stop (may be null) take the routing+FC1 kernel's own timestamps.
-hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
-// FC2 + combine per token (output-stationary, no accumulator): act rows in
-// d.fc.act_in, ids / weights in d.topk_ids / d.topk_weights, output d.fc.out.
-hipError_t launch_fc2_tokens(const DecodeArgs& d, hipStream_t stream);
 // Small batches take launch_fc2_tokens in moe_w4a16_layer: it reads each
 // (token, slot)'s expert once, so an expert that several tokens share is
 // read again, but it needs no accumulator, atomics or finalize kernel and
@@ -152,16 +158,48 @@ inline bool token_fc2_fits(int64_t M, int64_t E, int64_t I, int64_t k) {
   return (double)(M * k) <= 1.2 * (double)E * (1.0 - miss);
 }
 
-// Routing, grouping and FC1 in one kernel for batches of up to 16 tokens
-// (M*k <= 256, E <= 1024, 2I/32 a multiple of 16): fills every output that
-// moe_route_align fills (d.topk_ids ... d.npp_out, in d.block_m-row blocks)
-// and FC1's activation rows in d.fc.act_out; clears d.fc.zero_words16
-// 16-byte words of d.fc.acc (0: none). ev_start / ev_stop as for launch_decode.
-bool routed_fc1_fits(int64_t M, int64_t E, int64_t I, int64_t k);
-// Whether moe_w4a16_layer takes it: fits, and the grouped wide kernel would
-// leave CUs idle (few experts touched). Queries the current device.
-bool routed_fc1_preferred(int64_t M, int64_t E, int64_t I, int64_t k);
-hipError_t launch_fc1_routed(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+// Launchers of the format-dependent kernels, declared for both formats
+// (namespaces fmt_int4 and fmt_mxfp4); each is defined by that format's
+// build of fc.hip, fc_tile.hip or decode.hip.
+//   launch_fc1 / launch_fc2   grouped GEMM stages; ev_start / ev_stop (may be
+//                             null) take FC1's own start and end timestamps
+//                             (hipExtLaunchKernel), for timing the stage
+//                             without extra packets
+//   tile_path_supported, tile_grid_tiles, launch_tile_plan, launch_fc_tiled
+//                             the tiled grouped GEMM (fc_tile.hip)
+//   launch_decode             routing fused into FC1 + output-stationary FC2
+//                             for tiny batches; events as for launch_fc1
+//   launch_fc2_tokens         FC2 + combine per token (output-stationary, no
+//                             accumulator): act rows in d.fc.act_in, ids and
+//                             weights in d.topk_ids / d.topk_weights, output
+//                             d.fc.out
+//   routed_fc1_fits, routed_fc1_preferred, launch_fc1_routed
+//                             routing, grouping and FC1 in one kernel for up
+//                             to 16 tokens (M*k <= 256, E <= 1024): fills every
+//                             output moe_route_align fills (d.topk_ids ...
+//                             d.npp_out, in d.block_m-row blocks) and FC1's
+//                             activation rows, clears d.fc.zero_words16
+//                             16-byte words of d.fc.acc (0: none);
+//                             "preferred" = fits and the grouped wide kernel
+//                             would leave CUs idle (queries the device)
+#define MOE_FORMAT_LAUNCHERS \
+  hipError_t launch_fc1(const FcArgs& a, hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr); \
+  hipError_t launch_fc2(const FcArgs& a, hipStream_t stream); \
+  bool tile_path_supported(int64_t H, int64_t I); \
+  int64_t tile_grid_tiles(int64_t M, int64_t E, int64_t k, int64_t block_m, int64_t cap); \
+  hipError_t launch_tile_plan(const FcArgs& a, hipStream_t stream); \
+  template <bool kFc1> hipError_t launch_fc_tiled(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1); \
+  hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop); \
+  hipError_t launch_fc2_tokens(const DecodeArgs& d, hipStream_t stream); \
+  bool routed_fc1_fits(int64_t M, int64_t E, int64_t I, int64_t k); \
+  bool routed_fc1_preferred(int64_t M, int64_t E, int64_t I, int64_t k); \
+  hipError_t launch_fc1_routed(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+namespace fmt_int4 {
+MOE_FORMAT_LAUNCHERS
+}  // namespace fmt_int4
+namespace fmt_mxfp4 {
+MOE_FORMAT_LAUNCHERS
+}  // namespace fmt_mxfp4
 
 // Launch with optional kernel-timestamp events.
 template <typename... KArgs, typename... Args>

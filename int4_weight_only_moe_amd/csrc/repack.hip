@@ -1,4 +1,5 @@
-// Canonical INT4 weights <-> the gfx950 tile layout the GEMM kernels stream.
+// Canonical INT4 or MXFP4 weights <-> the gfx950 tile layout the GEMM
+// kernels stream.
 //
 // "The Throughput Lever: Quantifying the MoE GEMM and Mapping the Road to
 // B300", section "Building the Benchmark", converts GPTQ-format INT4 weights
@@ -9,6 +10,9 @@
 // [4p, 4p+4) and code 2p+1 in bits [16+4p, 20+4p) so that one AND/OR per pair
 // turns two codes into two bf16 values. The 128 bytes of scales that follow
 // hold row r's 4 group scales at offset 8*r.
+// MXFP4 (FP4 e2m1 codes, E8M0 scales): the same tiles with the codes in
+// canonical byte order (gfx950's FP4 conversion takes a byte's low nibble
+// first) and 64 bytes of scales, row r's 4 bytes at offset 4*r.
 #include "internal.h"
 
 namespace moe {
@@ -48,7 +52,7 @@ struct TileIndex {
 };
 
 // Thread -> (expert, tile, lane): one thread per 16 device bytes of nibbles.
-__device__ __forceinline__ bool tile_index(int64_t gid, int E, int N, int K, int kind, TileIndex& ti,
+__device__ __forceinline__ bool tile_index(int fmt, int64_t gid, int E, int N, int K, int kind, TileIndex& ti,
                                            int64_t& canon_byte_row) {
   const int64_t nkc = K / kChunkK, npair = N / kPairRows;
   const int64_t per_expert = npair * nkc * 2 * 64;
@@ -63,50 +67,58 @@ __device__ __forceinline__ bool tile_index(int64_t gid, int E, int N, int K, int
   const int r = ti.L % 16, sb = ti.L / 16;
   ti.n = canon_row(kind, N, p, h, r);
   ti.c0 = kc * kChunkK + 8 * sb;  // channel of group j is c0 + 32*j
-  ti.dev_off = ti.e * packed_bytes_per_expert(N, K) + tile * kTileBytes;
+  ti.dev_off = ti.e * packed_bytes_fmt(fmt, N, K) + tile * (kTileNibbleBytes + tile_scale_bytes(fmt));
   canon_byte_row = (ti.e * N + ti.n) * (K / 2);
   return true;
 }
 
-__global__ __launch_bounds__(kThreads) void repack_kernel(const uint8_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ s, int E,
-                                                          int N, int K, int kind,
-                                                          uint8_t* __restrict__ packed) {
+__global__ __launch_bounds__(kThreads) void repack_kernel(int fmt, const uint8_t* __restrict__ q,
+                                                          const void* __restrict__ s, int E, int N, int K,
+                                                          int kind, uint8_t* __restrict__ packed) {
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   TileIndex ti;
   int64_t row;
-  if (!tile_index(gid, E, N, K, kind, ti, row)) return;
+  if (!tile_index(fmt, gid, E, N, K, kind, ti, row)) return;
   uint32_t d[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t x = *reinterpret_cast<const uint32_t*>(q + row + (ti.c0 + 32 * j) / 2);
-    d[j] = to_device_dword(x);
+    d[j] = fmt == kFmtMxfp4 ? x : to_device_dword(x);
   }
   *reinterpret_cast<uint4*>(packed + ti.dev_off + 16 * ti.L) = make_uint4(d[0], d[1], d[2], d[3]);
   if (ti.L < 16) {  // this lane also moves the 4 group scales of row ti.n
     const int64_t g0 = (ti.c0 - 8 * (ti.L / 16)) / kGroup;
-    const uint2 sc = *reinterpret_cast<const uint2*>(s + (ti.e * N + ti.n) * (K / kGroup) + g0);
-    *reinterpret_cast<uint2*>(packed + ti.dev_off + kTileNibbleBytes + 8 * (ti.L % 16)) = sc;
+    const int64_t srow = (ti.e * N + ti.n) * (K / kGroup) + g0;
+    if (fmt == kFmtMxfp4)
+      *reinterpret_cast<uint32_t*>(packed + ti.dev_off + kTileNibbleBytes + 4 * (ti.L % 16)) =
+          *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(s) + srow);
+    else
+      *reinterpret_cast<uint2*>(packed + ti.dev_off + kTileNibbleBytes + 8 * (ti.L % 16)) =
+          *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(s) + srow);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void unpack_kernel(const uint8_t* __restrict__ packed, int E,
-                                                          int N, int K, int kind,
-                                                          uint8_t* __restrict__ q,
-                                                          uint16_t* __restrict__ s) {
+__global__ __launch_bounds__(kThreads) void unpack_kernel(int fmt, const uint8_t* __restrict__ packed, int E,
+                                                          int N, int K, int kind, uint8_t* __restrict__ q,
+                                                          void* __restrict__ s) {
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   TileIndex ti;
   int64_t row;
-  if (!tile_index(gid, E, N, K, kind, ti, row)) return;
+  if (!tile_index(fmt, gid, E, N, K, kind, ti, row)) return;
   const uint4 v = *reinterpret_cast<const uint4*>(packed + ti.dev_off + 16 * ti.L);
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    *reinterpret_cast<uint32_t*>(q + row + (ti.c0 + 32 * j) / 2) = to_canonical_dword(d[j]);
+    *reinterpret_cast<uint32_t*>(q + row + (ti.c0 + 32 * j) / 2) = fmt == kFmtMxfp4 ? d[j] : to_canonical_dword(d[j]);
   if (ti.L < 16) {
     const int64_t g0 = (ti.c0 - 8 * (ti.L / 16)) / kGroup;
-    const uint2 sc = *reinterpret_cast<const uint2*>(packed + ti.dev_off + kTileNibbleBytes + 8 * (ti.L % 16));
-    *reinterpret_cast<uint2*>(s + (ti.e * N + ti.n) * (K / kGroup) + g0) = sc;
+    const int64_t srow = (ti.e * N + ti.n) * (K / kGroup) + g0;
+    if (fmt == kFmtMxfp4)
+      *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(s) + srow) =
+          *reinterpret_cast<const uint32_t*>(packed + ti.dev_off + kTileNibbleBytes + 4 * (ti.L % 16));
+    else
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(s) + srow) =
+          *reinterpret_cast<const uint2*>(packed + ti.dev_off + kTileNibbleBytes + 8 * (ti.L % 16));
   }
 }
 
@@ -117,19 +129,19 @@ int64_t grid_for(int E, int N, int K) {
 
 }  // namespace
 
-hipError_t launch_repack(const uint8_t* q, const uint16_t* s, int E, int N, int K, int kind,
+hipError_t launch_repack(int fmt, const uint8_t* q, const void* s, int E, int N, int K, int kind,
                          uint8_t* packed, hipStream_t stream) {
   const int64_t blocks = grid_for(E, N, K);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  repack_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(q, s, E, N, K, kind, packed);
+  repack_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(fmt, q, s, E, N, K, kind, packed);
   return hipGetLastError();
 }
 
-hipError_t launch_unpack(const uint8_t* packed, int E, int N, int K, int kind, uint8_t* q, uint16_t* s,
+hipError_t launch_unpack(int fmt, const uint8_t* packed, int E, int N, int K, int kind, uint8_t* q, void* s,
                          hipStream_t stream) {
   const int64_t blocks = grid_for(E, N, K);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  unpack_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(packed, E, N, K, kind, q, s);
+  unpack_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(fmt, packed, E, N, K, kind, q, s);
   return hipGetLastError();
 }
 

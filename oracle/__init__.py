@@ -23,6 +23,9 @@ is taken; each reading is named in the function that uses it.
 Everything floating-point here is float64. The dequantised weight q*s is exact
 in float64 (a 4-bit integer times an 11-bit fp16 significand).
 
+MXFP4 expert weights (``dequantize_mxfp4``) are the same layer with FP4
+e2m1 weights and E8M0 scales.
+
 Pins (what checks this oracle against something other than itself) live in
 ``tests/test_oracle_*.py``: hand-packed nibbles, brute-force routing,
 argsort-based alignment, closed forms, a dense masked formulation, a textbook
@@ -183,20 +186,67 @@ def expert_mlp(x: np.ndarray, W13: np.ndarray, W2: np.ndarray) -> np.ndarray:
     return W2 @ act
 
 
+# --------------------------------------------------------------------------
+# O1', O2': MXFP4 expert weights (FP4 e2m1 codes, E8M0 scale per 32)
+# --------------------------------------------------------------------------
+# "From 1,060 to 4,016 tok/s on one B300, and why it wasn't the kernels"
+# (opening section) serves a MoE whose experts are MXFP4. The pages do not
+# define the format; the reading taken is the OCP Microscaling (MX) v1.0
+# MXFP4: blocks of 32 elements along K sharing one E8M0 scale, elements in
+# FP4 E2M1. The codes are packed like the INT4 ones (channel 2i in the low
+# nibble of byte i).
+def decode_fp4_e2m1(codes: np.ndarray) -> np.ndarray:
+    """Value of 4-bit E2M1 codes: bit 3 sign, bits 2..1 exponent (bias 1),
+    bit 0 mantissa; exponent 0 is subnormal (mantissa * 0.5), otherwise
+    2^(exponent - 1) * (1 + mantissa / 2). float64, same shape."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = (c >> 3) & 1
+    exp = (c >> 1) & 3
+    man = c & 1
+    mag = np.where(exp == 0, 0.5 * man, np.ldexp(1.0 + 0.5 * man, exp - 1))
+    return np.where(sign == 1, -mag, mag)
+
+
+def decode_e8m0(scales: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes s -> 2^(s - 127) in float64; s = 255 is NaN."""
+    s = np.asarray(scales, dtype=np.int64)
+    return np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+
+
+def dequantize_mxfp4(qweight: np.ndarray, scales_e8m0: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """W[n, c] = e2m1(code[n, c]) * 2^(s[n, c // 32] - 127) in float64 (exact:
+    a 2-bit significand times a power of two)."""
+    qb = np.asarray(qweight, dtype=np.uint8)
+    s = decode_e8m0(scales_e8m0)
+    K = 2 * qb.shape[-1]
+    if K != s.shape[-1] * GROUP:
+        raise ValueError(f"K={K} does not match {s.shape[-1]} groups of {GROUP}")
+    W = np.empty(qb.shape[:-1] + (K,), dtype=np.float64) if out is None else out
+    pairs = W.reshape(qb.shape + (2,))
+    pairs[..., 0] = decode_fp4_e2m1(qb & 0x0F)  # channel 2i: low nibble
+    pairs[..., 1] = decode_fp4_e2m1(qb >> 4)    # channel 2i+1: high nibble
+    groups = W.reshape(qb.shape[:-1] + (K // GROUP, GROUP))
+    groups *= s[..., None]
+    return W
+
+
 ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]]
+DEQUANT = {"int4": dequantize, "mxfp4": dequantize_mxfp4}
 
 
 class DequantCache:
-    """Dequantised experts on demand.
+    """Dequantised experts on demand, for weight format ``fmt`` ("int4":
+    ``dequantize``, "mxfp4": ``dequantize_mxfp4``).
 
     Keeps up to ``max_items`` experts; with ``max_items == 0`` it keeps none
     and rewrites one pair of scratch buffers on every call (the caller uses
     an expert's matrices before asking for the next one).
     """
 
-    def __init__(self, get_expert: ExpertFn, max_items: int = 64):
+    def __init__(self, get_expert: ExpertFn, max_items: int = 64, fmt: str = "int4"):
         self.get_expert = get_expert
         self.max_items = max_items
+        self.dequant = DEQUANT[fmt]
         self.items: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
         self.scratch = None
 
@@ -204,14 +254,15 @@ class DequantCache:
         if e in self.items:
             return self.items[e]
         w13, s13, w2, s2 = self.get_expert(e)
+        dq = self.dequant
         if self.max_items == 0:
             if self.scratch is None or self.scratch[0].shape != (w13.shape[0], 2 * w13.shape[1]):
                 self.scratch = (np.empty((w13.shape[0], 2 * w13.shape[1])),
                                 np.empty((w2.shape[0], 2 * w2.shape[1])))
-            return dequantize(w13, s13, self.scratch[0]), dequantize(w2, s2, self.scratch[1])
+            return dq(w13, s13, self.scratch[0]), dq(w2, s2, self.scratch[1])
         if len(self.items) >= self.max_items:
             self.items.pop(next(iter(self.items)))
-        self.items[e] = (dequantize(w13, s13), dequantize(w2, s2))
+        self.items[e] = (dq(w13, s13), dq(w2, s2))
         return self.items[e]
 
 

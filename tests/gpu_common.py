@@ -26,27 +26,34 @@ def x_device(x_bits: np.ndarray) -> torch.Tensor:
 
 
 class DeviceLayer:
-    """Repacked weights of one layer on the device."""
+    """Repacked weights of one layer on the device (fmt "int4" or "mxfp4")."""
 
-    def __init__(self, shape: wl.LayerShape, w13, s13, w2, s2):
+    def __init__(self, shape: wl.LayerShape, w13, s13, w2, s2, fmt: str = "int4"):
         self.shape = shape
+        self.fmt = fmt
         q13, q2 = to_dev(w13), to_dev(w2)
-        sc13, sc2 = to_dev(s13.view(np.uint16)).view(torch.float16), to_dev(s2.view(np.uint16)).view(torch.float16)
-        self.w13 = moe.repack(q13, sc13, moe.KIND_W13)
-        self.w2 = moe.repack(q2, sc2, moe.KIND_W2)
+        if fmt == "mxfp4":
+            sc13, sc2 = to_dev(s13), to_dev(s2)
+            self.w13 = moe.repack_mxfp4(q13, sc13, moe.KIND_W13)
+            self.w2 = moe.repack_mxfp4(q2, sc2, moe.KIND_W2)
+        else:
+            sc13 = to_dev(s13.view(np.uint16)).view(torch.float16)
+            sc2 = to_dev(s2.view(np.uint16)).view(torch.float16)
+            self.w13 = moe.repack(q13, sc13, moe.KIND_W13)
+            self.w2 = moe.repack(q2, sc2, moe.KIND_W2)
         torch.cuda.synchronize()
         del q13, q2, sc13, sc2
 
 
-def device_layer(shape: wl.LayerShape, seed: int) -> DeviceLayer:
-    return DeviceLayer(shape, *wl.layer_weights(shape, seed))
+def device_layer(shape: wl.LayerShape, seed: int, fmt: str = "int4") -> DeviceLayer:
+    return DeviceLayer(shape, *wl.layer_weights(shape, seed, fmt=fmt), fmt=fmt)
 
 
-def oracle_experts(shape: wl.LayerShape, seed: int, keep: int = 64):
+def oracle_experts(shape: wl.LayerShape, seed: int, keep: int = 64, fmt: str = "int4"):
     def get(e):
-        ew = wl.expert_weights(shape, seed, e)
+        ew = wl.expert_weights(shape, seed, e, fmt)
         return ew.w13, ew.s13, ew.w2, ew.s2
-    return oracle.DequantCache(get, max_items=keep)
+    return oracle.DequantCache(get, max_items=keep, fmt=fmt)
 
 
 def run_layer(layer: DeviceLayer, logits: np.ndarray, x_bits: np.ndarray, block_m: int):
@@ -55,7 +62,7 @@ def run_layer(layer: DeviceLayer, logits: np.ndarray, x_bits: np.ndarray, block_
     M = logits.shape[0]
     rb = moe.alloc_route_buffers(M, s.E, s.k, block_m)
     moe.route_align(to_dev(logits), rb)
-    out = moe.forward(x_device(x_bits), rb, s.I, layer.w13, layer.w2)
+    out = moe.forward(x_device(x_bits), rb, s.I, layer.w13, layer.w2, fmt=layer.fmt)
     torch.cuda.synchronize()
     return rb, out.float().cpu().numpy()
 
@@ -109,3 +116,9 @@ def assert_output_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
 def k26_layer() -> DeviceLayer:
     """The 384-expert layer (9.5 GB of weights), generated and repacked once per session."""
     return device_layer(wl.K26, 2026)
+
+
+@functools.lru_cache(maxsize=None)
+def k26_mxfp4_layer() -> DeviceLayer:
+    """The 384-expert layer with MXFP4 weights (9.0 GB), generated and repacked once per session."""
+    return device_layer(wl.K26, 2026, fmt="mxfp4")

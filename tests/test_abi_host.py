@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) >= 12
     for name in names:
         assert hasattr(lib, name), name
-    assert moe.moe_w4a16_abi_version() == 1
+    assert moe.moe_w4a16_abi_version() == 2
 
 
 def test_status_strings():
@@ -61,6 +61,16 @@ def test_packed_bytes():
     assert moe.moe_w4a16_packed_bytes(1, 48, 128) == -1     # N not a multiple of 32
     assert moe.moe_w4a16_packed_bytes(1, 32, 96) == -1      # K not a multiple of 128
     assert moe.moe_w4a16_packed_bytes(1, 32, 128, 64) == -1  # only group 32
+
+
+def test_mxfp4_packed_bytes():
+    # FP4 codes (half a byte) + one E8M0 byte per 32 weights = 17/32 byte per weight
+    assert moe.moe_mxfp4_packed_bytes(384, 4096, 7168) == 384 * 4096 * 7168 * 17 // 32
+    total = moe.moe_mxfp4_packed_bytes(384, 4096, 7168) + moe.moe_mxfp4_packed_bytes(384, 7168, 2048)
+    assert total == 8_984_199_168
+    assert moe.moe_mxfp4_packed_bytes(1, 48, 128) == -1
+    assert moe.moe_mxfp4_packed_bytes(1, 32, 96) == -1
+    assert moe.moe_mxfp4_packed_bytes(0, 32, 128) == -1
 
 
 def test_workspace_bytes():
@@ -112,6 +122,13 @@ def test_repack_validation():
     assert lib.moe_w4a16_repack(None, FAKE, 2, 64, 128, 32, 1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_w4a16_repack(FAKE + 8, FAKE, 2, 64, 128, 32, 1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_w4a16_unpack(FAKE, 2, 64, 128, 32, 0, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # MXFP4: same rules (no group argument)
+    assert lib.moe_mxfp4_repack(FAKE, FAKE, 2, 64, 128, 2, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_repack(FAKE, FAKE, 2, 48, 128, 1, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_mxfp4_repack(FAKE, FAKE, 2, 64, 96, 1, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_mxfp4_repack(FAKE, None, 2, 64, 128, 1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_repack(FAKE, FAKE + 4, 2, 64, 128, 1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_unpack(FAKE, 2, 64, 128, 0, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def _fwd(lib, M=4, E=384, H=7168, I=2048, k=8, B=16, cap=None, ws=None, x=FAKE, out=FAKE):
@@ -166,3 +183,25 @@ def test_layer_validation():
     assert call(logits=None) == moe.MOE_ERR_INVALID_ARG
     assert call(x=p + 2) == moe.MOE_ERR_INVALID_ARG
     assert call(E=1025) == moe.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("prefix", ["moe_w4a16", "moe_mxfp4"])
+def test_both_formats_validate_alike(prefix):
+    """The MXFP4 stages share the INT4 stages' argument checks."""
+    lib = moe.lib()
+    p = FAKE
+    cap = moe.moe_route_align_capacity(4, 384, 8, 16)
+    ws = moe.moe_w4a16_workspace_bytes(4, 384, 7168, 2048, 8)
+    fwd, layer = getattr(lib, prefix + "_forward"), getattr(lib, prefix + "_layer")
+    fc1, fc2 = getattr(lib, prefix + "_fc1"), getattr(lib, prefix + "_fc2")
+    assert fwd(None, 0, 384, 7168, 2048, 8, 16, None, None, None, None, None, 0, None, None, None, 0, None,
+               None) == moe.MOE_OK
+    assert fwd(p, 4, 384, 7000, 2048, 8, 16, p, p, p, p, p, cap, p, p, p, ws, p, None) == moe.MOE_ERR_UNSUPPORTED
+    assert fwd(p, 4, 384, 7168, 2048, 8, 16, p, p, p, p, p, cap - 16, p, p, p, ws, p, None) == moe.MOE_ERR_CAPACITY
+    assert fwd(p, 4, 384, 7168, 2048, 8, 16, p, p, p, p, p, cap, p, p, p, ws - 1, p, None) == moe.MOE_ERR_WORKSPACE
+    assert layer(None, p, 4, 384, 7168, 2048, 8, 16, p, p, p, p, p, p, cap, p, p, p, ws, p, None,
+                 None) == moe.MOE_ERR_INVALID_ARG
+    assert layer(p, p, 4, 1025, 7168, 2048, 8, 16, p, p, p, p, p, p, cap, p, p, p, ws, p, None,
+                 None) == moe.MOE_ERR_UNSUPPORTED
+    assert fc1(p, 4, 384, 7168, 2048, 8, 16, p, p, p, cap, p, p, ws - 16, None) == moe.MOE_ERR_WORKSPACE
+    assert fc2(4, 384, 7168, 2048, 8, 16, p, p, p, p, cap, p, p, ws, None, None) == moe.MOE_ERR_INVALID_ARG

@@ -50,6 +50,7 @@ def const_layer(shape, byte=0x99, scale_bits=0x2000):
     s2 = torch.full((E, H, I // 32), scale_bits, dtype=torch.int16, device="cuda").view(torch.float16)
     layer = DeviceLayer.__new__(DeviceLayer)
     layer.shape = shape
+    layer.fmt = "int4"
     layer.w13 = moe.repack(q13, s13, moe.KIND_W13)
     layer.w2 = moe.repack(q2, s2, moe.KIND_W2)
     torch.cuda.synchronize()

@@ -113,14 +113,29 @@ def f32_from_f16_bits(bits: np.ndarray) -> np.ndarray:
 @dataclass
 class ExpertWeights:
     w13: np.ndarray  # uint8 [2I, H/2]
-    s13: np.ndarray  # float16 [2I, H/32]
+    s13: np.ndarray  # float16 (INT4) or uint8 E8M0 (MXFP4) [2I, H/32]
     w2: np.ndarray   # uint8 [H, I/2]
-    s2: np.ndarray   # float16 [H, I/32]
+    s2: np.ndarray   # float16 or uint8 [H, I/32]
 
 
-def expert_weights(shape: LayerShape, seed: int, e: int) -> ExpertWeights:
-    """Draw the canonical INT4 weights and fp16 scales of expert ``e``."""
+# MXFP4 scales: 2^-6, 2^-5 or 2^-4 with equal probability (E8M0 bytes 121..123),
+# so that e2m1 codes (magnitudes up to 6) give weights of the INT4 draws' size.
+MXFP4_SCALE_EXP = (-6, -3)
+
+
+def expert_weights(shape: LayerShape, seed: int, e: int, fmt: str = "int4") -> ExpertWeights:
+    """Draw the canonical weights and scales of expert ``e``: INT4 codes and
+    fp16 scales, or (fmt "mxfp4", a stream of its own) FP4 e2m1 codes and
+    E8M0 scales."""
     H, I = shape.H, shape.I
+    if fmt == "mxfp4":
+        rng = np.random.default_rng([seed, e, 4])
+        lo, hi = MXFP4_SCALE_EXP
+        w13 = rng.integers(0, 256, (2 * I, H // 2), dtype=np.uint8)
+        s13 = (127 + rng.integers(lo, hi, (2 * I, H // GROUP))).astype(np.uint8)
+        w2 = rng.integers(0, 256, (H, I // 2), dtype=np.uint8)
+        s2 = (127 + rng.integers(lo, hi, (H, I // GROUP))).astype(np.uint8)
+        return ExpertWeights(w13, s13, w2, s2)
     rng = np.random.default_rng([seed, e])
     w13 = rng.integers(0, 256, (2 * I, H // 2), dtype=np.uint8)
     s13 = rng.uniform(SCALE_LO, SCALE_HI, (2 * I, H // GROUP)).astype(np.float16)
@@ -129,20 +144,21 @@ def expert_weights(shape: LayerShape, seed: int, e: int) -> ExpertWeights:
     return ExpertWeights(w13, s13, w2, s2)
 
 
-def layer_weights(shape: LayerShape, seed: int, threads: int | None = None):
+def layer_weights(shape: LayerShape, seed: int, threads: int | None = None, fmt: str = "int4"):
     """Draw all experts of a layer as stacked arrays (w13, s13, w2, s2).
 
     Experts are drawn in parallel threads (numpy releases the GIL while
     filling arrays); the result does not depend on the thread count.
     """
     E, H, I = shape.E, shape.H, shape.I
+    sdt = np.uint8 if fmt == "mxfp4" else np.float16
     w13 = np.empty((E, 2 * I, H // 2), np.uint8)
-    s13 = np.empty((E, 2 * I, H // GROUP), np.float16)
+    s13 = np.empty((E, 2 * I, H // GROUP), sdt)
     w2 = np.empty((E, H, I // 2), np.uint8)
-    s2 = np.empty((E, H, I // GROUP), np.float16)
+    s2 = np.empty((E, H, I // GROUP), sdt)
 
     def fill(e):
-        ew = expert_weights(shape, seed, e)
+        ew = expert_weights(shape, seed, e, fmt)
         w13[e], s13[e], w2[e], s2[e] = ew.w13, ew.s13, ew.w2, ew.s2
 
     if threads is None:
