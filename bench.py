@@ -2,12 +2,14 @@
 
 One step = one layer call over one batch through moe_w4a16_layer: routing,
 FC1 (gate/up, SiLU*mul) and FC2 with the weighted combine (two kernels for
-M <= 4, four above). The headline workload is the
+small batches, up to four above). The headline workload is the
 384-expert layer (hidden 7168, intermediate 2048, top-8) at M = 1 token
 (one decoding stream), the shape of "The Throughput Lever: Quantifying the MoE
 GEMM and Mapping the Road to B300", section "The Result: Two Regimes", table
-row M = 1. A sweep over M = 9, 90, 256, 512, 1024 and the skewed M = 1024
-batch is reported in the same JSON line.
+row M = 1. A sweep over M = 4, 9, 90, 256, 512, 1024, the skewed M = 1024
+batch and prefill chunks of 2048-8192 tokens is reported in the same JSON
+line, and (mxfp4_sweep) the same layer with MXFP4 expert weights through
+moe_mxfp4_layer at M = 1, 4, 9, 256, 1024 (context: the headline is INT4).
 
 Weights are synthetic (random INT4 codes, fp16 scales in [0.005, 0.02]) and
 resident in HBM before timing starts. To keep the 256 MB last-level cache from
@@ -23,7 +25,7 @@ figure). The same K steps
 replayed from one captured HIP graph are reported as context. The CPU oracle is timed on a bounded sample of
 the same workload (cpu_baseline).
 
-    python bench.py [--steps K] [--warmup W] [--replicas R] [--no-sweep] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--replicas R] [--no-sweep] [--no-mxfp4] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -56,6 +58,9 @@ def parse():
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--sweep-steps", type=int, default=200)
     p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4-weight sweep")
+    p.add_argument("--weights", choices=("int4", "mxfp4"), default="int4",
+                   help="expert weight format of the headline and the sweep (mxfp4: for profiling that path)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (to scale HBM counters)")
@@ -72,23 +77,34 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def layer_bytes(D, M, s):
-    """Algorithmic bytes of one layer call: touched experts' nibbles + scales,
+# weight bytes per weight: INT4 codes + an fp16 scale per 32 (9/16), MXFP4
+# codes + an E8M0 byte per 32 (17/32)
+WEIGHT_BYTES = {"int4": (9, 16), "mxfp4": (17, 32)}
+MXFP4_SWEEP = ["k26_m1", "k26_m4", "k26_m9", "k26_m256", "k26_m1024"]
+
+
+def _wbytes(n, fmt):
+    num, den = WEIGHT_BYTES[fmt]
+    return n * num // den
+
+
+def layer_bytes(D, M, s, fmt="int4"):
+    """Algorithmic bytes of one layer call: touched experts' codes + scales,
     x in and out (bf16), logits (fp32), ids and weights."""
-    per_expert = (2 * s.I * s.H + s.H * s.I) * 9 // 16
+    per_expert = _wbytes(2 * s.I * s.H + s.H * s.I, fmt)
     return D * per_expert + 4 * M * s.H + 4 * M * s.E + 8 * M * s.k
 
 
-def fc1_bytes(D, M, s):
-    """Algorithmic bytes of one FC1 launch: touched experts' W13 nibbles + scales,
+def fc1_bytes(D, M, s, fmt="int4"):
+    """Algorithmic bytes of one FC1 launch: touched experts' W13 codes + scales,
     the x rows, and the bf16 activations it writes."""
-    return D * (2 * s.I * s.H * 9 // 16) + 2 * M * s.H + 2 * M * s.k * s.I
+    return D * _wbytes(2 * s.I * s.H, fmt) + 2 * M * s.H + 2 * M * s.k * s.I
 
 
-def fc2_bytes(D, M, s):
-    """Algorithmic bytes of one FC2 stage: touched experts' W2 nibbles + scales, the
+def fc2_bytes(D, M, s, fmt="int4"):
+    """Algorithmic bytes of one FC2 stage: touched experts' W2 codes + scales, the
     bf16 activations it reads and the bf16 output."""
-    return D * (s.H * s.I * 9 // 16) + 2 * M * s.k * s.I + 2 * M * s.H
+    return D * _wbytes(s.H * s.I, fmt) + 2 * M * s.k * s.I + 2 * M * s.H
 
 
 def flops(M, s):
@@ -152,9 +168,26 @@ class Bench:
         # repack time on its own (one more repack of W13 + W2 from device copies)
         self.repack_ms = self._time_repack(w13, s13, w2, s2)
         self.layers = [(p13, p2)] + [(p13.clone(), p2.clone()) for _ in range(replicas - 1)]
+        self.fmt_layers = {"int4": self.layers}
+        self.replicas = replicas
         torch.cuda.synchronize()
         print(f"# weights: generated + repacked in {t1 - t0:.1f} s, {replicas} copies "
               f"({replicas * (p13.numel() + p2.numel()) / 1e9:.1f} GB)", file=sys.stderr, flush=True)
+
+    def mxfp4_layers(self):
+        """The same layer with seeded MXFP4 weights (built on first use), as many copies."""
+        if "mxfp4" not in self.fmt_layers:
+            torch, moe, wl = self.torch, self.moe, self.wl
+            t0 = time.time()
+            w13, s13, w2, s2 = wl.layer_weights(self.s, 2026, fmt="mxfp4")
+            p13 = moe.repack_mxfp4(torch.from_numpy(w13).cuda(), torch.from_numpy(s13).cuda(), moe.KIND_W13)
+            p2 = moe.repack_mxfp4(torch.from_numpy(w2).cuda(), torch.from_numpy(s2).cuda(), moe.KIND_W2)
+            del w13, s13, w2, s2
+            self.fmt_layers["mxfp4"] = [(p13, p2)] + [(p13.clone(), p2.clone()) for _ in range(self.replicas - 1)]
+            torch.cuda.synchronize()
+            print(f"# MXFP4 weights: generated + repacked in {time.time() - t0:.1f} s, {self.replicas} copies "
+                  f"({self.replicas * (p13.numel() + p2.numel()) / 1e9:.1f} GB)", file=sys.stderr, flush=True)
+        return self.fmt_layers["mxfp4"]
 
     def _time_repack(self, w13, s13, w2, s2):
         torch, moe = self.torch, self.moe
@@ -191,12 +224,12 @@ class Bench:
         # touched experts for the byte count: the k largest logits per row
         return np.argsort(-logits, axis=1, kind="stable")[:, :k]
 
-    def step(self, c, layer, ev=None):
-        """One layer call: moe_w4a16_layer (routing + FC1 + FC2); ev = optional
-        pair of HIP events recorded around its FC1 stage."""
+    def step(self, c, layer, ev=None, fmt="int4"):
+        """One layer call: moe_w4a16_layer or moe_mxfp4_layer (routing + FC1 +
+        FC2); ev = optional pair of HIP events recorded around its FC1 stage."""
         s = self.s
         self.moe.layer(c["logits"], c["x"], c["rb"], s.I, layer[0], layer[1], workspace=c["ws"], out=c["out"],
-                       stage_events=None if ev is None else (ev[0].handle, ev[1].handle))
+                       stage_events=None if ev is None else (ev[0].handle, ev[1].handle), fmt=fmt)
 
     def spin(self, seconds):
         """Keep the GPU busy for about `seconds` ahead of the host: device
@@ -217,7 +250,7 @@ class Bench:
         for _ in range(max(1, int(seconds / self._spin_copy_s))):
             self._spin_bufs[1].copy_(self._spin_bufs[0])
 
-    def run(self, name, steps, warmup, replicas):
+    def run(self, name, steps, warmup, replicas, fmt="int4"):
         """W eager warm-up steps, then K timed steps launched back to back, then
         K more steps with HIP events on the FC1 stage.
 
@@ -235,11 +268,12 @@ class Bench:
         """
         torch = self.torch
         c = self.prepare(name)
-        R = min(replicas, len(self.layers))
+        layers = self.mxfp4_layers() if fmt == "mxfp4" else self.layers
+        R = min(replicas, len(layers))
         torch.cuda.synchronize()
         h0 = time.perf_counter()
         for i in range(warmup):
-            self.step(c, self.layers[i % R])
+            self.step(c, layers[i % R], fmt=fmt)
         host_per_step = (time.perf_counter() - h0) / max(warmup, 1)
         torch.cuda.synchronize()
         # Untimed steps queued between the spin and the start event: the
@@ -253,10 +287,10 @@ class Bench:
         t0 = time.perf_counter()
         self.spin(spin_s)
         for i in range(ramp):
-            self.step(c, self.layers[i % R])
+            self.step(c, layers[i % R], fmt=fmt)
         start.record()
         for i in range(steps):
-            self.step(c, self.layers[i % R])
+            self.step(c, layers[i % R], fmt=fmt)
         stop.record()
         enqueue_s = time.perf_counter() - t0
         torch.cuda.synchronize()
@@ -268,24 +302,25 @@ class Bench:
         evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
         self.spin(spin_s)
         for i in range(ramp):
-            self.step(c, self.layers[i % R])
+            self.step(c, layers[i % R], fmt=fmt)
         for i in range(steps):
-            self.step(c, self.layers[i % R], evs[i])
+            self.step(c, layers[i % R], evs[i], fmt=fmt)
         torch.cuda.synchronize()
         fc1_us = float(np.mean([a.elapsed_ms(b) for a, b in evs])) * 1e3
         return c, total_ms / steps, fc1_us, wall
 
-    def run_graph(self, name, steps, replicas):
+    def run_graph(self, name, steps, replicas, fmt="int4"):
         """The same K steps captured in one HIP graph and replayed (context)."""
         torch = self.torch
         c = self.prepare(name)
-        R = min(replicas, len(self.layers))
-        self.step(c, self.layers[0])
+        layers = self.mxfp4_layers() if fmt == "mxfp4" else self.layers
+        R = min(replicas, len(layers))
+        self.step(c, layers[0], fmt=fmt)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(steps):
-                self.step(c, self.layers[i % R])
+                self.step(c, layers[i % R], fmt=fmt)
         g.replay()
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -296,18 +331,22 @@ class Bench:
         del g
         return start.elapsed_time(stop) / steps
 
-    def record(self, name, steps, warmup, replicas):
-        c, ms, fc1_us, wall = self.run(name, steps, warmup, replicas)
+    def record(self, name, steps, warmup, replicas, fmt="int4"):
+        c, ms, fc1_us, wall = self.run(name, steps, warmup, replicas, fmt)
         w, s, D = c["w"], self.s, c["D"]
         us = ms * 1e3
-        return dict(
+        lb = layer_bytes(D, w.M, s, fmt)
+        r = dict(
             workload=name, M=w.M, block_m=c["B"], experts_touched=D, us_per_call=round(us, 2),
-            us_per_token=round(us / w.M, 3), hbm_TBps=round(layer_bytes(D, w.M, s) / (us * 1e-6) / 1e12, 3),
+            us_per_token=round(us / w.M, 3), hbm_TBps=round(lb / (us * 1e-6) / 1e12, 3),
             mfma_pct=round(100 * flops(w.M, s) / (us * 1e-6) / (MFMA_BF16_PEAK_TFS * 1e12), 2),
-            roofline_frac=round(max(layer_bytes(D, w.M, s) / (HBM_PEAK_GBS * 1e9),
+            roofline_frac=round(max(lb / (HBM_PEAK_GBS * 1e9),
                                     flops(w.M, s) / (MFMA_BF16_PEAK_TFS * 1e12)) / (us * 1e-6), 4),
-            fc1_us=round(fc1_us, 2), fc1_GBps=round(fc1_bytes(D, w.M, s) / (fc1_us * 1e-6) / 1e9, 1),
-            replicas=min(replicas, len(self.layers)), wall_s=round(wall, 3)), c
+            fc1_us=round(fc1_us, 2), fc1_GBps=round(fc1_bytes(D, w.M, s, fmt) / (fc1_us * 1e-6) / 1e9, 1),
+            replicas=min(replicas, len(self.layers)), wall_s=round(wall, 3))
+        if fmt != "int4":
+            r["weights"] = fmt
+        return r, c
 
     def cpu_baseline(self, c, budget_s=12.0):
         """The oracle (as it stands) on the headline batch, repeated for about budget_s seconds."""
@@ -365,19 +404,26 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    head, c = b.record(a.workload, a.steps, a.warmup, a.replicas)
+    fmt = a.weights
+    head, c = b.record(a.workload, a.steps, a.warmup, a.replicas, fmt)
     s, D, M = b.s, c["D"], c["w"].M
-    fc1_alg = fc1_bytes(D, M, s)
+    fc1_alg = fc1_bytes(D, M, s, fmt)
     fc1_s = head["fc1_us"] * 1e-6
     sweep = []
     if not a.no_sweep:
         for name in SWEEP:
-            r, _ = b.record(name, a.sweep_steps, 5, a.replicas)
+            r, _ = b.record(name, a.sweep_steps, 5, a.replicas, fmt)
             sweep.append(r)
             print(f"# {json.dumps(r)}", file=sys.stderr, flush=True)
-        warm, _ = b.record(a.workload, a.sweep_steps, 5, 1)
+        warm, _ = b.record(a.workload, a.sweep_steps, 5, 1, fmt)
         warm["note"] = "one weight copy: consecutive steps may hit the last-level cache (context only)"
         sweep.append(warm)
+    mxfp4 = []
+    if not a.no_mxfp4 and fmt == "int4":
+        for name in ([a.workload] if a.no_sweep else MXFP4_SWEEP):
+            r, _ = b.record(name, a.sweep_steps, 5, a.replicas, fmt="mxfp4")
+            mxfp4.append(r)
+            print(f"# {json.dumps(r)}", file=sys.stderr, flush=True)
     cpu = None if a.no_cpu_baseline else b.cpu_baseline(c)
     line = {
         "metric": "MoE layer us/token (+ achieved HBM TB/s, MFMA %) on the 384-expert INT4 g32 layer",
@@ -392,18 +438,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded random INT4 weights and router logits, bf16 N(0,1) activations)",
-        "config": {"workload": f"{a.workload}: E=384, H=7168, I=2048, top-8, INT4 g32, M={M} tokens",
+        "config": {"workload": f"{a.workload}: E=384, H=7168, I=2048, top-8, "
+                               f"{'INT4 g32' if fmt == 'int4' else 'MXFP4'}, M={M} tokens",
                    "global_batch": M, "block_m": head["block_m"], "experts_touched": D,
                    "weight_copies_cycled": head["replicas"],
                    "launch": "eager, queued ahead of the GPU"},
-        "graph_us_per_call": round(b.run_graph(a.workload, a.steps, a.replicas) * 1e3, 2),
+        "graph_us_per_call": round(b.run_graph(a.workload, a.steps, a.replicas, fmt) * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(fc1_alg / fc1_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(fc1_alg / fc1_s / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for(fc1_alg), "kernel": "FC1 stage (fc1_decode_kernel for M <= 4, else fc_kernel FC1)",
+                     "traffic": traffic_for(fc1_alg) if fmt == "int4" else None,
+                     "kernel": "FC1 stage (fc1_decode_kernel at M <= 2, fc1_routed_kernel for few touched experts, "
+                               "else the grouped FC1 kernel)",
                      "kernel_avg_us": head["fc1_us"], "algorithmic_bytes": fc1_alg},
         "layer": {k: head[k] for k in ("us_per_call", "hbm_TBps", "mfma_pct", "roofline_frac")},
         "repack_ms": round(b.repack_ms, 2),
         "sweep": sweep,
+        "mxfp4_sweep": mxfp4,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
