@@ -281,11 +281,8 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
 // Flips": at small batches the fixed per-step costs, a separate routing
 // launch among them, weigh most).
 //
-// Prologue, once per workgroup: waves 0..M-1 route one token each; a bitmap
-// of the touched experts in LDS ranks them. Top-k experts are distinct, so
-// no expert gets more than M <= 16 rows: every touched expert is exactly one
-// block (of any block_m), the blocks are the touched experts in ascending
-// order, and a block's rows are that expert's assignments in ascending f.
+// Prologue, once per workgroup: small_route (routing, ranks of the touched
+// experts, block tables).
 //
 // Work: items (block, group of kRoutedSlots tile pairs), dealt round-robin
 // to resident workgroups (one per CU). A workgroup's 16 waves are
@@ -302,9 +299,6 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
 // Workgroup 0 writes the routing and grouping outputs after its items,
 // exactly as moe_route_align lays them out for block_m (FC2, their consumer,
 // is the next kernel).
-constexpr int kRoutedMaxTokens = 16;
-constexpr int kRoutedMaxAssign = 256;
-constexpr int kRoutedMaxExperts = 1024;
 constexpr int kRoutedWaves = 16;
 constexpr int kRoutedKSplit = 4;                            // waves per tile pair
 constexpr int kRoutedSlots = kRoutedWaves / kRoutedKSplit;  // tile pairs per item
@@ -323,20 +317,14 @@ template <int VPL, int NCH>
 __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArgs d) {
   constexpr int P = kRoutedP, KS = kRoutedKSplit;
   constexpr int kThreads = 64 * kRoutedWaves;
-  __shared__ int32_t ids[kRoutedMaxAssign];
-  __shared__ float wts[kRoutedMaxAssign];
-  __shared__ uint32_t bits[kRoutedMaxExperts / 32];      // touched experts
-  __shared__ int32_t before[kRoutedMaxExperts / 32 + 1];  // touched experts in the words below
+  __shared__ SmallRoute sh;
   __shared__ f32x4_t red[2][KS - 1][kRoutedSlots][2][64];  // K-range partial sums, by item parity
-  __shared__ int32_t blk_e[kRoutedMaxAssign];               // expert of each block
-  __shared__ int32_t blk_rows[kRoutedMaxAssign][16];        // rows of each block, padded with M*k
 
   const FcArgs& a = d.fc;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kq = wave % KS, slot = wave / KS;
   const int M = a.M, E = a.E, k = a.k, MK = M * k, H = a.H;
-  const int nwords = (E + 31) / 32;
 
   if (a.zero_words16 > 0) {  // clear FC2's accumulator when the grouped FC2 follows
     uint4* z = reinterpret_cast<uint4*>(a.acc);
@@ -345,48 +333,7 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
       z[i] = make_uint4(0, 0, 0, 0);
   }
 
-  if (tid < nwords) bits[tid] = 0u;
-  if (wave < M) topk_token<VPL>(d.logits, wave, E, k, ids, wts);
-  __syncthreads();
-  for (int f = tid; f < MK; f += kThreads) atomicOr(&bits[ids[f] >> 5], 1u << (ids[f] & 31));
-  __syncthreads();
-  if (wave == 0) {  // exclusive prefix of the words' popcounts (nwords <= 32)
-    const int c = lane < nwords ? __builtin_popcount(bits[lane]) : 0;
-    int incl = c;
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      const int t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
-    if (lane < nwords) before[lane] = incl - c;
-    if (lane == nwords - 1) before[nwords] = incl;
-  }
-  __syncthreads();
-  // LDS values read here are the same in every lane: readfirstlane keeps
-  // the loop counts and the weight addresses in scalar registers.
-  const int nd = __builtin_amdgcn_readfirstlane(before[nwords]);  // touched experts = blocks
-  auto rank = [&](int x) {  // touched experts below x
-    const int wx = x >> 5, b = x & 31;
-    return before[wx] + __builtin_popcount(bits[wx] & ((1u << b) - 1u));
-  };
-  // block tables: the expert of rank r is block r; its rows are its
-  // assignments in ascending f (one ballot per 64 assignments), then padding
-  for (int x = tid; x < E; x += kThreads)
-    if ((bits[x >> 5] >> (x & 31)) & 1u) blk_e[rank(x)] = x;
-  __syncthreads();
-  for (int b = wave; b < nd; b += kRoutedWaves) {
-    const int e = blk_e[b];
-    int base = 0;
-    for (int f0 = 0; f0 < MK; f0 += 64) {
-      const int f = f0 + lane;
-      const bool hit = f < MK && ids[f] == e;
-      const uint64_t hm = __ballot(hit);
-      if (hit) blk_rows[b][base + lanes_below(hm)] = f;
-      base += __builtin_popcountll(hm);
-    }
-    if (lane >= base && lane < 16) blk_rows[b][lane] = MK;
-  }
-  __syncthreads();
+  const int nd = small_route<VPL, kThreads>(sh, d.logits, M, E, k);  // touched experts = blocks
 
   const int nkc = H / kChunkK;
   const int kc0 = kq * nkc / KS;
@@ -403,8 +350,8 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
     const int blk = item / ipb;
     RoutedWork r;
     r.pair = (item % ipb) * kRoutedSlots + slot;
-    const int e = __builtin_amdgcn_readfirstlane(blk_e[blk]);
-    r.frow = blk_rows[blk][lane & 15];
+    const int e = __builtin_amdgcn_readfirstlane(sh.blk_e[blk]);
+    r.frow = sh.blk_rows[blk][lane & 15];
     r.w = a.wpacked + (int64_t)e * wexp + ((int64_t)r.pair * nkc + kc0) * kPairChunkBytes;
     r.wbytes = kPairChunkBytes;
     r.xoff = r.frow < MK ? ((uint32_t)(r.frow / k) * (uint32_t)H + 8u * (lane >> 4) + (uint32_t)kc0 * kChunkK) * 2u
@@ -506,20 +453,9 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
     par ^= 1;
   }
 
-  if (blockIdx.x == 0) {  // routing + grouping outputs, in block_m-row blocks
-    const int bm = d.block_m;
-    for (int f = tid; f < MK; f += kThreads) {
-      d.topk_ids[f] = ids[f];
-      d.topk_weights[f] = wts[f];
-    }
-    for (int i = tid; i < nd * bm; i += kThreads) {
-      const int b = i / bm, p = i % bm;
-      d.sorted_ids[i] = p < 16 ? blk_rows[b][p] : MK;
-    }
-    for (int b = tid; b < nd; b += kThreads) d.block_expert[b] = blk_e[b];
-    for (int x = tid; x <= E; x += kThreads) d.expert_offsets[x] = bm * (x < E ? rank(x) : nd);
-    if (tid == 0) *d.npp_out = bm * nd;
-  }
+  if (blockIdx.x == 0)  // routing + grouping outputs, in block_m-row blocks
+    small_route_write<kThreads>(sh, nd, M, E, k, d.block_m, d.topk_ids, d.topk_weights, d.sorted_ids,
+                                d.block_expert, d.expert_offsets, d.npp_out);
 }
 
 // Workgroups of the routed FC1: one per compute unit (its register use
@@ -628,7 +564,7 @@ hipError_t launch_fc1(const FcArgs& a, hipStream_t stream, hipEvent_t ev_start, 
 hipError_t launch_fc2(const FcArgs& a, hipStream_t stream) { return launch_fc<false>(a, stream, nullptr, nullptr); }
 
 bool routed_fc1_fits(int64_t M, int64_t E, int64_t I, int64_t k) {
-  return M >= 1 && M <= kRoutedMaxTokens && M * k <= kRoutedMaxAssign && E <= kRoutedMaxExperts &&
+  return M >= 1 && M <= kSmallMaxTokens && M * k <= kSmallMaxAssign && E <= kSmallMaxExperts &&
          (2 * I / kPairRows) % kRoutedSlots == 0;
 }
 

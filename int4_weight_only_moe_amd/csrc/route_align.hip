@@ -9,10 +9,10 @@
 // to the tile size, a stable permutation of the assignments and the padding.
 //
 // Two launch shapes produce identical integers:
-//   M <= kFusedMaxTokens: one workgroup does the top-k (one wave per token)
-//                         and then the grouping;
-//   otherwise:            a top-k kernel with one wave per token over many
-//                         workgroups, then a one-workgroup grouping kernel.
+//   M <= 16:    one workgroup does the top-k (one wave per token) and ranks
+//               the touched experts (small_route: one block per expert);
+//   otherwise:  a top-k kernel with one wave per token over many
+//               workgroups, then a one-workgroup grouping kernel.
 #include "internal.h"
 #include "device_common.h"
 #include "route_common.h"
@@ -23,7 +23,6 @@ namespace {
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
 constexpr int kMaxExperts = 1024;
-constexpr int kFusedMaxTokens = 16;
 constexpr int kIdsPerLane = 8;  // expert ids a lane loads at once in the grouping passes
 constexpr int kTopkWavesPerBlock = 4;
 
@@ -200,27 +199,27 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   align_body(sh, ids, MK, E, block_m, sorted_ids, block_expert, offsets, npp);
 }
 
-// Small batches: waves 0..M-1 route one token each, then the whole
-// workgroup groups the assignments (the ids are read back after a barrier).
+// Small batches (M <= 16): small_route in one workgroup (routing, ranks of
+// the touched experts by an LDS bitmap, one block per touched expert), then
+// the outputs from its tables. Measured at M = 9 on the 384-expert layer:
+// 10.4 us with the general grouping (histogram, scan, ballot placement).
 template <int VPL>
-__global__ __launch_bounds__(kAlignThreads) void route_align_fused_kernel(
-    const float* __restrict__ logits, int M, int E, int k, int block_m, int32_t* topk_ids,
+__global__ __launch_bounds__(kAlignThreads) void route_align_small_kernel(
+    const float* __restrict__ logits, int M, int E, int k, int block_m, int32_t* __restrict__ topk_ids,
     float* __restrict__ topk_w, int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ offsets, int32_t* __restrict__ npp) {
-  __shared__ AlignShared sh;
-  __shared__ int32_t ids_lds[kFusedMaxTokens * 16];
-  const int wave = threadIdx.x >> 6;
-  if (wave < M) topk_token<VPL>(logits, wave, E, k, topk_ids, topk_w, ids_lds);
-  __syncthreads();
-  align_body(sh, ids_lds, M * k, E, block_m, sorted_ids, block_expert, offsets, npp);
+  __shared__ SmallRoute sh;
+  const int nd = small_route<VPL, kAlignThreads>(sh, logits, M, E, k);
+  small_route_write<kAlignThreads>(sh, nd, M, E, k, block_m, topk_ids, topk_w, sorted_ids, block_expert, offsets,
+                                   npp);
 }
 
 template <int VPL>
 hipError_t launch_vpl(const float* logits, int M, int E, int k, int block_m, int32_t* topk_ids,
                       float* topk_w, int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets,
                       int32_t* npp, hipStream_t stream) {
-  if (M <= kFusedMaxTokens) {
-    route_align_fused_kernel<VPL><<<1, kAlignThreads, 0, stream>>>(
+  if (M <= kSmallMaxTokens && M * k <= kSmallMaxAssign) {
+    route_align_small_kernel<VPL><<<1, kAlignThreads, 0, stream>>>(
         logits, M, E, k, block_m, topk_ids, topk_w, sorted_ids, block_expert, offsets, npp);
     return hipGetLastError();
   }

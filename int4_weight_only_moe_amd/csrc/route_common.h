@@ -196,4 +196,101 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
   topk_route<VPL>(logits, t, E, k, k, 0, topk_ids, topk_w, ids_copy);
 }
 
+// ---------------------------------------------------------------------------
+// Routing and grouping of a small batch inside one workgroup (M <= 16,
+// M*k <= 256, E <= 1024). Waves 0..M-1 route one token each; a bitmap of the
+// touched experts in LDS ranks them. Top-k experts are distinct within a
+// token, so no expert gets more than M <= 16 rows: every touched expert is
+// exactly one block of any block_m >= 16, the blocks are the touched experts
+// in ascending order, and a block's rows are that expert's assignments in
+// ascending f (the stable per-expert order of the grouping).
+constexpr int kSmallMaxTokens = 16;
+constexpr int kSmallMaxAssign = 256;
+constexpr int kSmallMaxExperts = 1024;
+
+struct SmallRoute {
+  int32_t ids[kSmallMaxAssign];                   // topk ids, f = t*k + j
+  float wts[kSmallMaxAssign];                     // topk weights
+  uint32_t bits[kSmallMaxExperts / 32];           // touched experts
+  int32_t before[kSmallMaxExperts / 32 + 1];      // touched experts in the words below
+  int32_t blk_e[kSmallMaxAssign];                 // expert of block r (rank r)
+  int32_t blk_rows[kSmallMaxAssign][kSmallMaxTokens];  // rows of block r, then M*k
+};
+
+// Touched experts below x.
+__device__ __forceinline__ int small_rank(const SmallRoute& sh, int x) {
+  const int w = x >> 5, b = x & 31;
+  return sh.before[w] + __builtin_popcount(sh.bits[w] & ((1u << b) - 1u));
+}
+
+// Fills sh for the batch; returns the number of touched experts (= blocks).
+// Every thread of the workgroup (kThreads, at least 64 * M) must call it:
+// it contains barriers.
+template <int VPL, int kThreads>
+__device__ int small_route(SmallRoute& sh, const float* __restrict__ logits, int M, int E, int k) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int MK = M * k, nwords = (E + 31) / 32;
+  if (tid < nwords) sh.bits[tid] = 0u;
+  if (wave < M) topk_token<VPL>(logits, wave, E, k, sh.ids, sh.wts);
+  __syncthreads();
+  for (int f = tid; f < MK; f += kThreads) atomicOr(&sh.bits[sh.ids[f] >> 5], 1u << (sh.ids[f] & 31));
+  __syncthreads();
+  if (wave == 0) {  // exclusive prefix of the words' popcounts (nwords <= 32)
+    const int c = lane < nwords ? __builtin_popcount(sh.bits[lane]) : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (lane < nwords) sh.before[lane] = incl - c;
+    if (lane == nwords - 1) sh.before[nwords] = incl;
+  }
+  __syncthreads();
+  // (the same value in every lane: readfirstlane keeps loop counts scalar)
+  const int nd = __builtin_amdgcn_readfirstlane(sh.before[nwords]);
+  for (int x = tid; x < E; x += kThreads)
+    if ((sh.bits[x >> 5] >> (x & 31)) & 1u) sh.blk_e[small_rank(sh, x)] = x;
+  __syncthreads();
+  // rows of each block: one ballot per 64 assignments, positions by lane rank
+  for (int b = wave; b < nd; b += kThreads / 64) {
+    const int e = sh.blk_e[b];
+    int base = 0;
+    for (int f0 = 0; f0 < MK; f0 += 64) {
+      const int f = f0 + lane;
+      const bool hit = f < MK && sh.ids[f] == e;
+      const uint64_t hm = __ballot(hit);
+      if (hit) sh.blk_rows[b][base + lanes_below(hm)] = f;
+      base += __builtin_popcountll(hm);
+    }
+    if (lane >= base && lane < kSmallMaxTokens) sh.blk_rows[b][lane] = MK;
+  }
+  __syncthreads();
+  return nd;
+}
+
+// The routing and grouping outputs exactly as moe_route_align lays them out
+// for block_m = bm >= 16 (any threads of one workgroup, no barrier):
+// topk_ids / topk_weights [M*k], sorted_ids [nd*bm], block_expert [nd],
+// offsets [E+1], npp [1].
+template <int kThreads>
+__device__ void small_route_write(const SmallRoute& sh, int nd, int M, int E, int k, int bm,
+                                  int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                                  int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+                                  int32_t* __restrict__ offsets, int32_t* __restrict__ npp) {
+  const int tid = threadIdx.x, MK = M * k;
+  for (int f = tid; f < MK; f += kThreads) {
+    topk_ids[f] = sh.ids[f];
+    topk_w[f] = sh.wts[f];
+  }
+  for (int i = tid; i < nd * bm; i += kThreads) {
+    const int b = i / bm, p = i % bm;
+    sorted_ids[i] = p < kSmallMaxTokens ? sh.blk_rows[b][p] : MK;
+  }
+  for (int b = tid; b < nd; b += kThreads) block_expert[b] = sh.blk_e[b];
+  for (int x = tid; x <= E; x += kThreads) offsets[x] = bm * (x < E ? small_rank(sh, x) : nd);
+  if (tid == 0) *npp = bm * nd;
+}
+
 }  // namespace moe
