@@ -9,7 +9,7 @@ GEMM and Mapping the Road to B300", section "The Result: Two Regimes", table
 row M = 1. A sweep over M = 4, 9, 90, 256, 512, 1024, the skewed M = 1024
 batch and prefill chunks of 2048-8192 tokens is reported in the same JSON
 line, and (mxfp4_sweep) the same layer with MXFP4 expert weights through
-moe_mxfp4_layer at M = 1, 4, 9, 256, 1024 (context: the headline is INT4).
+moe_mxfp4_layer at M = 1, 4, 9, 256, 1024, 4096 (context: the headline is INT4).
 
 Weights are synthetic (random INT4 codes, fp16 scales in [0.005, 0.02]) and
 resident in HBM before timing starts. To keep the 256 MB last-level cache from
@@ -80,7 +80,7 @@ def kernel_source_sha() -> str:
 # weight bytes per weight: INT4 codes + an fp16 scale per 32 (9/16), MXFP4
 # codes + an E8M0 byte per 32 (17/32)
 WEIGHT_BYTES = {"int4": (9, 16), "mxfp4": (17, 32)}
-MXFP4_SWEEP = ["k26_m1", "k26_m4", "k26_m9", "k26_m256", "k26_m1024"]
+MXFP4_SWEEP = ["k26_m1", "k26_m4", "k26_m9", "k26_m256", "k26_m1024", "k26_m4096"]
 
 
 def _wbytes(n, fmt):

@@ -24,6 +24,10 @@
 //     and the group scale is applied to the fp32 MFMA result (scale after
 //     the product, so the weights are never rounded);
 //   * partial sums of the waves meet in LDS; wave 0 runs the epilogue.
+// With MXFP4 weights (this file compiled with MOE_WEIGHT_FORMAT = 1) the
+// codes are widened to exact bf16 values already carrying the group's E8M0
+// scale, so there is neither the -136 correction nor a scale after the
+// product (fc_common.h: group_scale, dequant_group, group_c, group_add).
 // FC1 epilogue: act_f = bf16(SiLU(gate) * up); gate and up of one output
 // column land in the same lane because a pair is (gate tile r, up tile r).
 // FC2 epilogue: acc[t] += w_f * y_f with fp32 atomics into a workspace
