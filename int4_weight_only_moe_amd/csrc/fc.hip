@@ -34,6 +34,8 @@
 // accumulator that FC1 clears; a last small kernel rounds acc to bf16 once.
 // (A "last arriving workgroup converts" scheme needs agent-scope fences, and
 // on gfx950 each of those writes back and invalidates the L2.)
+#include <atomic>
+
 #include "internal.h"
 #include "device_common.h"
 #include "fc_common.h"
@@ -464,11 +466,20 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
 
 // Workgroups of the routed FC1: one per compute unit (its register use
 // allows one 16-wave workgroup per CU), at most one per work item.
+// CU count of the current device, queried once per device (a benign race:
+// every thread stores the same value).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
 inline int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  if (dev < kMaxDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 inline int64_t routed_grid(int64_t max_items) {

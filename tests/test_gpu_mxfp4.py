@@ -133,3 +133,31 @@ def test_mxfp4_k26_sampled(name):
     ref = oracle.moe_forward(_x(t), ids, wts, oracle_experts(s, 2026, keep=0, fmt="mxfp4"), tokens_subset=rows)
     rel, mx = assert_output_close(out[rows], ref[rows], f"mxfp4 {name}")
     print(f"mxfp4 {name}: rows {rows} rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("M", [2, 5])
+def test_mxfp4_layer_graph_replays(M):
+    """The MXFP4 layer call captured in a HIP graph: every replay equals the
+    eager call (decode path at M = 2, routed FC1 + per-token FC2 at M = 5)."""
+    shape, seed = SHAPES[1]
+    layer = device_layer(shape, seed, fmt="mxfp4")
+    t = wl.tokens(shape, M, 400 + M)
+    lg, x = to_dev(t.logits), x_device(t.x_bits)
+    rb = moe.alloc_route_buffers(M, shape.E, shape.k, 16)
+    ws = torch.empty(moe.moe_w4a16_workspace_bytes(M, shape.E, shape.H, shape.I, shape.k), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((M, shape.H), dtype=torch.bfloat16, device="cuda")
+    moe.layer(lg, x, rb, shape.I, layer.w13, layer.w2, workspace=ws, out=out, fmt="mxfp4")
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.layer(lg, x, rb, shape.I, layer.w13, layer.w2, workspace=ws, out=out, fmt="mxfp4")
+    y = torch.randn(512, 512, device="cuda")
+    for _ in range(4):
+        out.fill_(0)
+        rb.topk_ids.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        (y @ y).sum().item()
