@@ -45,7 +45,8 @@ constexpr int kDecKSplit = 4;   // FC1 waves per workgroup (split K)
 // FC1 chunks in flight per wave (fewer for 3-4 rows: their sums need the registers)
 constexpr int dec_p1(int rows) { return rows <= 2 ? 4 : 3; }
 
-struct SmallRoute {
+// The decode batch's routing in LDS (M <= 4 tokens, M*k <= 64 assignments).
+struct DecodeRoute {
   int32_t ids[kDecodeMaxAssign];
   float w[kDecodeMaxAssign];
   int32_t list[kDecodeMaxAssign];                    // distinct experts, ascending
@@ -193,7 +194,7 @@ constexpr int kXEarlyRows = 2;
 template <int VPL, int NCH, int MR>
 __global__ __launch_bounds__(64 * kDecKSplit) __attribute__((amdgpu_waves_per_eu(4)))
 void fc1_decode_kernel(DecodeArgs d) {
-  __shared__ SmallRoute sh;
+  __shared__ DecodeRoute sh;
   extern __shared__ uint4 xs[];  // [M][row16]: the batch's x rows, then xcorr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -53,10 +53,8 @@ void fc_kernel(FcArgs a) {
   // wave index, blocks, experts and chunk ranges are wave-uniform: keep them
   // in scalar registers so the buffer descriptors built from them are too
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int K = kFc1 ? a.H : a.I;
   const int N = kFc1 ? 2 * a.I : a.H;
   const int npairs = N / kPairRows;
-  const int MK = a.M * a.k;
 
   if constexpr (kFc1) {
     // Clear FC2's fp32 accumulator (the start of the workspace), spread over
@@ -205,6 +203,11 @@ __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const
           for (int s = 0; s < S; ++s) {
             if (s > 0 && !sact[s]) continue;
             const bf16x8_t xv = as_bf16x8(xt[slot][16 * s + mrow][4 * g + kv]);
+            if constexpr (kFmt == kFmtMxfp4) {  // scaled operand: accumulate in the MFMA
+              acc0[s] = mfma16x16x32(xv, b0, acc0[s]);
+              acc1[s] = mfma16x16x32(xv, b1, acc1[s]);
+              continue;
+            }
             const f32x4_t off = group_c(xs4[slot][g][4 * s + kv]);
             const f32x4_t t0 = mfma16x16x32(xv, b0, off);
             const f32x4_t t1 = mfma16x16x32(xv, b1, off);

@@ -127,6 +127,11 @@ __device__ __forceinline__ void mma_chunk(const WChunk& w, const uint4 (&xa)[S][
     for (int s = 0; s < S; ++s) {
       if (s > 0 && !sact[s]) continue;  // sub-tile 0 always holds a row
       const bf16x8_t xv = as_bf16x8(xa[s][j]);
+      if constexpr (kFmt == kFmtMxfp4) {  // scaled operand: accumulate in the MFMA
+        acc0[s] = mfma16x16x32(xv, b0, acc0[s]);
+        acc1[s] = mfma16x16x32(xv, b1, acc1[s]);
+        continue;
+      }
       const f32x4_t off = group_c(mfma16x16x32(xv, neg136, zero4));
       const f32x4_t t0 = mfma16x16x32(xv, b0, off);
       const f32x4_t t1 = mfma16x16x32(xv, b1, off);
