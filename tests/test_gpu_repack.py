@@ -5,7 +5,6 @@ import pytest
 import torch
 
 import int4_weight_only_moe_amd as moe
-import workloads as wl
 from gpu_common import to_dev
 
 pytestmark = pytest.mark.gpu
