@@ -219,10 +219,11 @@ int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int
  *     batch, and FC2 is output-stationary (each output tile sums its token's
  *     top_k expert results in slot order in one workgroup: no atomics, and
  *     the bf16 output is then identical on every call);
- *   - M <= 16 and M*top_k <= 256 while few experts are touched (the grouped
- *     FC1 would fill at most 1.5 rounds of the device's CUs; on the
- *     384-expert top-8 layer M = 3..6): a persistent FC1 kernel that routes
- *     once per workgroup and splits the work into small items;
+ *   - M <= 16 and M*top_k <= 256 while few experts are touched and the
+ *     batch's x rows fit in 128 KB of LDS (the grouped FC1 would fill at
+ *     most 1.75 rounds of the device's CUs; on the 384-expert top-8 layer
+ *     M = 3..7): a persistent FC1 kernel that routes once per workgroup and
+ *     splits the work into small items;
  *   - else M <= 4 with M*top_k <= 64: the decode path.
  * Up to 16 tokens the output-stationary FC2 follows the FC1 while the
  * M*top_k expert reads stay within 1.2x the expected number of distinct

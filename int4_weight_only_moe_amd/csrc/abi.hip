@@ -284,7 +284,7 @@ static int layer_impl(int fmt, const float* logits, const uint16_t* x_bf16, int3
   hipEvent_t ev1 = stage_events ? (hipEvent_t)stage_events[1] : nullptr;
   // decode path for one or two tokens; then the routed FC1 while few experts
   // are touched; the decode path where it fits; else the four kernels
-  const bool routed = FMT_CALL(fmt, routed_fc1_preferred, M, E, I, top_k);
+  const bool routed = FMT_CALL(fmt, routed_fc1_preferred, M, E, H, I, top_k);
   if (moe::decode_path_fits(M, H, I, top_k) && (M <= 2 || !routed)) {
     moe::DecodeArgs d{};
     d.fc = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,

@@ -295,10 +295,11 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
 //
 // Work: items (block, group of kRoutedSlots tile pairs), dealt round-robin
 // to resident workgroups (one per CU). A workgroup's 16 waves are
-// kRoutedSlots pairs x kRoutedKSplit K ranges; the activations come straight
-// from L2 into registers (as in fc_block: a 16-row tile holds one or two
-// real rows here; staging them in LDS with a barrier per chunk measured
-// slower). The small items (the pairs of one block are split 32 ways) keep
+// kRoutedSlots pairs x kRoutedKSplit K ranges. The batch's x rows (M <= 9 at
+// H = 7168) are staged in LDS once, before the items: every block's rows are
+// tokens of the batch, so each wave reads its A operand from there and keeps
+// only weights in its register ring. The small items (the pairs of one
+// block are split 32 ways) keep
 // the last round short: with a few dozen experts touched, the wide kernel's
 // 8 workgroups of 16 pairs per expert leave most CUs idle in a second round.
 // A wave's last P chunk loads already fetch its next item's first chunks, so
@@ -311,15 +312,17 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
 constexpr int kRoutedWaves = 16;
 constexpr int kRoutedKSplit = 4;                            // waves per tile pair
 constexpr int kRoutedSlots = kRoutedWaves / kRoutedKSplit;  // tile pairs per item
-constexpr int kRoutedP = 2;                                 // chunks in flight per wave
+constexpr int kRoutedP = 2;                                 // weight chunks in flight per wave (divides NCH)
+constexpr int kRoutedXPer = 9;               // x vectors staged per thread: M * H / 8 <= 9 * 1024
+constexpr int kRoutedMaxXBytes = 128 * 1024;  // staged x rows (with the routing tables and partial sums: < 160 KB)
 
 // One wave's share of an item: expert, tile pair, the row of lane % 16 and
-// its activation offset (kOutOfRange for padding).
+// where its A operand starts in the staged rows.
 struct RoutedWork {
   const uint8_t* w;  // this wave's first chunk of the pair
   uint32_t wbytes;   // bytes of a chunk to read: kPairChunkBytes, 0 for no item (reads zeros)
   int pair, frow;
-  uint32_t xoff;
+  int xrow;          // LDS index of this lane's first 16 bytes (padding rows read token 0: never stored)
 };
 
 template <int VPL, int NCH>
@@ -327,7 +330,8 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
   constexpr int P = kRoutedP, KS = kRoutedKSplit;
   constexpr int kThreads = 64 * kRoutedWaves;
   __shared__ SmallRoute sh;
-  __shared__ f32x4_t red[2][KS - 1][kRoutedSlots][2][64];  // K-range partial sums, by item parity
+  __shared__ f32x4_t red[kRoutedSlots][2][64];          // one K range's partial sums
+  extern __shared__ uint4 xs[];                          // [M][H / 8 + 1]: the batch's x rows
 
   const FcArgs& a = d.fc;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -342,7 +346,23 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
       z[i] = make_uint4(0, 0, 0, 0);
   }
 
+  // The x rows: loads issued before the routing, stored to LDS after it
+  // (rows padded by 16 bytes, so that rows start on different banks).
+  const int hv = H / 8, row16 = hv + 1;
+  const uint4* xg = reinterpret_cast<const uint4*>(a.act_in);
+  uint4 xv[kRoutedXPer];
+#pragma unroll
+  for (int v = 0; v < kRoutedXPer; ++v) {
+    const int i = tid + v * kThreads;
+    xv[v] = i < M * hv ? xg[i] : make_uint4(0, 0, 0, 0);
+  }
   const int nd = small_route<VPL, kThreads>(sh, d.logits, M, E, k);  // touched experts = blocks
+#pragma unroll
+  for (int v = 0; v < kRoutedXPer; ++v) {
+    const int i = tid + v * kThreads;
+    if (i < M * hv) xs[(i / hv) * row16 + i % hv] = xv[v];
+  }
+  __syncthreads();
 
   const int nkc = H / kChunkK;
   const int kc0 = kq * nkc / KS;
@@ -350,7 +370,6 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
   const int ipb = 2 * a.I / kPairRows / kRoutedSlots;        // items per block
   const int nitems = nd * ipb;
   const int64_t wexp = packed_bytes_per_expert(2 * a.I, H);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.act_in, (uint32_t)M * (uint32_t)H * 2u);
   const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
   const uint32_t os0 = kTileNibbleBytes + kScaleRowBytes * (lane & 15);
   const uint32_t os1 = kTileBytes + kTileNibbleBytes + kScaleRowBytes * (lane & 15);
@@ -363,8 +382,7 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
     r.frow = sh.blk_rows[blk][lane & 15];
     r.w = a.wpacked + (int64_t)e * wexp + ((int64_t)r.pair * nkc + kc0) * kPairChunkBytes;
     r.wbytes = kPairChunkBytes;
-    r.xoff = r.frow < MK ? ((uint32_t)(r.frow / k) * (uint32_t)H + 8u * (lane >> 4) + (uint32_t)kc0 * kChunkK) * 2u
-                         : kOutOfRange;
+    r.xrow = (r.frow < MK ? r.frow / k : 0) * row16 + kc0 * (kChunkK / 8) + (lane >> 4);
     return r;
   };
   // one buffer descriptor per chunk (scalar arithmetic); a chunk at or past
@@ -379,27 +397,25 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
     w.s1 = load_scales<kPolicyWeights>(wr, os1);
     return w;
   };
-  auto load_x = [&](uint4 (&xa)[1][4], const RoutedWork& r, int c) {
-    const uint32_t o = (c < n) ? r.xoff + (uint32_t)c * kChunkXBytes : kOutOfRange;
+  // A operand of chunk c from the staged rows (a chunk past this wave's
+  // range, whose weights read as zeros, re-reads chunk 0: any finite value)
+  auto lds_x = [&](uint4 (&xa)[1][4], const RoutedWork& r, int c) {
+    const int cc = c < n ? c : 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xa[0][j] = bload16(xr, o + 64u * j);
+    for (int j = 0; j < 4; ++j) xa[0][j] = xs[r.xrow + cc * (kChunkK / 8) + 4 * j];
   };
 
   const bf16x8_t neg136 = as_bf16x8(make_uint4(kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair));
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const bool sact[1] = {true};  // a touched expert has at least one row
   WChunk wb[P];
-  uint4 xb[P][1][4];
-  int item = blockIdx.x, par = 0;
+  int item = blockIdx.x;
   RoutedWork cur;
   if (item < nitems) {
     cur = work_of(item);
     if constexpr (NCH > 0) {
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
-        wb[j] = load_w(cur, j);
-        load_x(xb[j], cur, j);
-      }
+      for (int j = 0; j < P; ++j) wb[j] = load_w(cur, j);
     }
   }
   while (item < nitems) {
@@ -407,7 +423,6 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
     const bool has_next = next < nitems;
     RoutedWork nx = cur;  // past the last item: loads of no bytes
     nx.wbytes = 0u;
-    nx.xoff = kOutOfRange;
     if (has_next) nx = work_of(next);
     f32x4_t acc0[1] = {zero4}, acc1[1] = {zero4};
     if constexpr (NCH > 0) {
@@ -415,51 +430,49 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void fc1_routed_kernel(DecodeArg
       // item's first chunks
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        mma_chunk<1>(wb[c % P], xb[c % P], sact, neg136, acc0, acc1);
-        if (c + P < NCH) {
-          wb[c % P] = load_w(cur, c + P);
-          load_x(xb[c % P], cur, c + P);
-        } else {
-          wb[c % P] = load_w(nx, c + P - NCH);
-          load_x(xb[c % P], nx, c + P - NCH);
-        }
+        uint4 xa[1][4];
+        lds_x(xa, cur, c);
+        mma_chunk<1>(wb[c % P], xa, sact, neg136, acc0, acc1);
+        wb[c % P] = c + P < NCH ? load_w(cur, c + P) : load_w(nx, c + P - NCH);
         __builtin_amdgcn_sched_barrier(0);  // bound live ranges to one chunk
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
-        wb[j] = load_w(cur, j);
-        load_x(xb[j], cur, j);
-      }
+      for (int j = 0; j < P; ++j) wb[j] = load_w(cur, j);
       for (int c = 0; c < n; c += P) {
 #pragma unroll
         for (int j = 0; j < P; ++j) {
-          if (c + j < n) mma_chunk<1>(wb[j], xb[j], sact, neg136, acc0, acc1);
+          if (c + j < n) {
+            uint4 xa[1][4];
+            lds_x(xa, cur, c + j);
+            mma_chunk<1>(wb[j], xa, sact, neg136, acc0, acc1);
+          }
           wb[j] = load_w(cur, c + j + P);
-          load_x(xb[j], cur, c + j + P);
         }
       }
     }
-    // sum the K ranges' partials; the K-range-0 wave of each pair runs the
-    // epilogue (the buffer alternates by item, so the next item's writes
-    // cannot overtake these reads: they come after the next barrier)
-    if (kq > 0) {
-      red[par][kq - 1][slot][0][lane] = acc0[0];
-      red[par][kq - 1][slot][1][lane] = acc1[0];
-    }
-    __syncthreads();
-    if (kq == 0) {
+    // The K-range-0 wave of each pair adds the other ranges' partials in
+    // range order, one range at a time through one LDS buffer (the LDS goes
+    // to the staged rows), then runs the epilogue.
 #pragma unroll
-      for (int q = 0; q < KS - 1; ++q) {
-        acc0[0] += red[par][q][slot][0][lane];
-        acc1[0] += red[par][q][slot][1][lane];
+    for (int q = 1; q < KS; ++q) {
+      if (kq == q) {
+        red[slot][0][lane] = acc0[0];
+        red[slot][1][lane] = acc1[0];
       }
+      __syncthreads();
+      if (kq == 0) {
+        acc0[0] += red[slot][0][lane];
+        acc1[0] += red[slot][1][lane];
+      }
+      __syncthreads();
+    }
+    if (kq == 0) {
       const int frow[1] = {cur.frow};
       fc_epilogue<1, true>(a, cur.pair, frow, sact, acc0, acc1, lane);
     }
     item = next;
     cur = nx;
-    par ^= 1;
   }
 
   if (blockIdx.x == 0)  // routing + grouping outputs, in block_m-row blocks
@@ -490,6 +503,30 @@ inline int64_t routed_grid(int64_t max_items) {
   return max_items < cus ? max_items : cus;
 }
 
+// Dynamic LDS of the routed FC1: the batch's x rows, padded.
+inline uint32_t routed_x_bytes(int64_t M, int64_t H) { return (uint32_t)(M * (H / 8 + 1) * 16); }
+
+// Raises the kernel's dynamic LDS limit (64 KB by default) once.
+template <typename Kernel>
+hipError_t allow_lds(Kernel kernel, uint32_t bytes) {
+  static std::atomic<uint32_t> allowed{0};
+  if (bytes <= 64 * 1024 || bytes <= allowed.load(std::memory_order_relaxed)) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)kRoutedMaxXBytes);
+  if (e == hipSuccess) allowed.store(kRoutedMaxXBytes, std::memory_order_relaxed);
+  return e;
+}
+
+template <int VPL, int NCH>
+hipError_t launch_routed(const DecodeArgs& d, unsigned grid, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  const uint32_t xbytes = routed_x_bytes(d.fc.M, d.fc.H);
+  const hipError_t e = allow_lds(fc1_routed_kernel<VPL, NCH>, xbytes);
+  if (e != hipSuccess) return e;
+  launch_kernel(fc1_routed_kernel<VPL, NCH>, grid, 64 * kRoutedWaves, xbytes, stream, e0, e1, d);
+  return hipGetLastError();
+}
+
 template <int VPL>
 hipError_t launch_routed_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int64_t MK = (int64_t)d.fc.M * d.fc.k;
@@ -497,13 +534,9 @@ hipError_t launch_routed_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t
   const unsigned grid = (unsigned)routed_grid(nblk * (2 * d.fc.I / kPairRows / kRoutedSlots));
   const int nkc = d.fc.H / kChunkK;
   // straight-line chunk loops for K ranges of 2 and 14 chunks (H = 1024, 7168)
-  if (nkc == 2 * kRoutedKSplit)
-    launch_kernel(fc1_routed_kernel<VPL, 2>, grid, 64 * kRoutedWaves, 0, stream, e0, e1, d);
-  else if (nkc == 14 * kRoutedKSplit)
-    launch_kernel(fc1_routed_kernel<VPL, 14>, grid, 64 * kRoutedWaves, 0, stream, e0, e1, d);
-  else
-    launch_kernel(fc1_routed_kernel<VPL, 0>, grid, 64 * kRoutedWaves, 0, stream, e0, e1, d);
-  return hipGetLastError();
+  if (nkc == 2 * kRoutedKSplit) return launch_routed<VPL, 2>(d, grid, stream, e0, e1);
+  if (nkc == 14 * kRoutedKSplit) return launch_routed<VPL, 14>(d, grid, stream, e0, e1);
+  return launch_routed<VPL, 0>(d, grid, stream, e0, e1);
 }
 
 // out = bf16(acc), 8 values per thread.
@@ -581,22 +614,23 @@ hipError_t launch_fc1(const FcArgs& a, hipStream_t stream, hipEvent_t ev_start, 
 }
 hipError_t launch_fc2(const FcArgs& a, hipStream_t stream) { return launch_fc<false>(a, stream, nullptr, nullptr); }
 
-bool routed_fc1_fits(int64_t M, int64_t E, int64_t I, int64_t k) {
+bool routed_fc1_fits(int64_t M, int64_t E, int64_t H, int64_t I, int64_t k) {
   return M >= 1 && M <= kSmallMaxTokens && M * k <= kSmallMaxAssign && E <= kSmallMaxExperts &&
-         (2 * I / kPairRows) % kRoutedSlots == 0;
+         (2 * I / kPairRows) % kRoutedSlots == 0 && M * (H / 8) <= (int64_t)kRoutedXPer * 64 * kRoutedWaves &&
+         routed_x_bytes(M, H) <= (uint32_t)kRoutedMaxXBytes;
 }
 
-bool routed_fc1_preferred(int64_t M, int64_t E, int64_t I, int64_t k) {
-  if (!routed_fc1_fits(M, E, I, k)) return false;
-  // Per CU the routed kernel streams ~10-15 % slower than the wide kernel;
+bool routed_fc1_preferred(int64_t M, int64_t E, int64_t H, int64_t I, int64_t k) {
+  if (!routed_fc1_fits(M, E, H, I, k)) return false;
+  // Per CU the routed kernel streams somewhat slower than the wide kernel;
   // it wins while the wide kernel's workgroups (16 pairs of one expert
   // each, for the expected number of distinct experts) would fill at most
-  // 1.5 rounds of the CUs. On the 384-expert top-8 layer (measured): M = 3
-  // ... 6 by 19-2 %, slower from M = 7.
+  // 1.75 rounds of the CUs. On the 384-expert top-8 layer (measured, layer
+  // call): M = 3 ... 7 by 4-8 %, M = 8 and 9 even (1.9 and 2.1 rounds).
   double miss = 1.0;  // probability that an expert is not among M tokens' top-k (uniform routing)
   for (int64_t t = 0; t < M; ++t) miss *= 1.0 - (double)k / (double)E;
   const double wide_wgs = (double)E * (1.0 - miss) * (double)(2 * I / kPairRows) / kWideNP;
-  return wide_wgs <= 1.5 * device_cus();
+  return wide_wgs <= 1.75 * device_cus();
 }
 
 hipError_t launch_fc1_routed(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {

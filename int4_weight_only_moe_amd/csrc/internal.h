@@ -175,7 +175,8 @@ inline bool token_fc2_fits(int64_t M, int64_t E, int64_t I, int64_t k) {
 //                             d.fc.out
 //   routed_fc1_fits, routed_fc1_preferred, launch_fc1_routed
 //                             routing, grouping and FC1 in one kernel for up
-//                             to 16 tokens (M*k <= 256, E <= 1024): fills every
+//                             to 16 tokens (M*k <= 256, E <= 1024, the x rows
+//                             within 128 KB of LDS: M <= 9 at H = 7168): fills every
 //                             output moe_route_align fills (d.topk_ids ...
 //                             d.npp_out, in d.block_m-row blocks) and FC1's
 //                             activation rows, clears d.fc.zero_words16
@@ -191,8 +192,8 @@ inline bool token_fc2_fits(int64_t M, int64_t E, int64_t I, int64_t k) {
   template <bool kFc1> hipError_t launch_fc_tiled(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1); \
   hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop); \
   hipError_t launch_fc2_tokens(const DecodeArgs& d, hipStream_t stream); \
-  bool routed_fc1_fits(int64_t M, int64_t E, int64_t I, int64_t k); \
-  bool routed_fc1_preferred(int64_t M, int64_t E, int64_t I, int64_t k); \
+  bool routed_fc1_fits(int64_t M, int64_t E, int64_t H, int64_t I, int64_t k); \
+  bool routed_fc1_preferred(int64_t M, int64_t E, int64_t H, int64_t I, int64_t k); \
   hipError_t launch_fc1_routed(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 namespace fmt_int4 {
 MOE_FORMAT_LAUNCHERS

@@ -1,6 +1,6 @@
 """moe_w4a16_layer: the one-call layer. M <= 2 runs the two-kernel decode
 path (routing inside FC1, output-stationary FC2); while few experts are
-touched (M <= 16, M*k <= 256; every small shape here, M = 3..6 on the
+touched (M <= 16, M*k <= 256; every small shape here, M = 3..7 on the
 384-expert layer) routing and grouping run inside the FC1 kernel; otherwise
 the decode path where it fits, else the four-kernel path. Integers must
 equal moe_route_align's, the output must meet the oracle bar, and the decode
@@ -82,8 +82,8 @@ def test_layer_k26_decode_sizes():
 @pytest.mark.parametrize("M", [3, 5, 6, 7, 9, 16, 17, 90])
 def test_layer_k26_grouped_sizes(M):
     """The layer call past the decode sizes, as the benchmark times it: the
-    routed FC1 at M = 3..6 (several items per workgroup from M = 5), the
-    grouped FC1 from 7; FC2 per token up to 16 tokens, the grouped FC2 and
+    routed FC1 at M = 3..7 (several items per workgroup from M = 5), the
+    grouped FC1 from 9; FC2 per token up to 16 tokens, the grouped FC2 and
     its finalize above."""
     layer = k26_layer()
     s = layer.shape
