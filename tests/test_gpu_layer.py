@@ -29,6 +29,9 @@ SHAPES = {
     # k = 16 (grouped FC2), several items per workgroup from M = 9
     "wide": (wl.LayerShape(E=128, H=1024, I=256, k=8), 7),
     "wide_e1024": (wl.LayerShape(E=1024, H=256, I=256, k=16), 8),
+    # E not a multiple of 32 or 64: a partial last word in the routing bitmap,
+    # masked lanes in the top-k
+    "odd_e": (wl.LayerShape(E=100, H=512, I=256, k=5), 9),
 }
 
 
