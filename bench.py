@@ -447,7 +447,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(fc1_alg / fc1_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(fc1_alg / fc1_s / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for(fc1_alg) if fmt == "int4" else None,
-                     "kernel": "FC1 stage (fc1_decode_kernel at M <= 2, fc1_routed_kernel for few touched experts, "
+                     "kernel": "FC1 stage (fc1_decode_kernel at M = 1, fc1_routed_kernel for few touched experts, "
                                "else the grouped FC1 kernel)",
                      "kernel_avg_us": head["fc1_us"], "algorithmic_bytes": fc1_alg},
         "layer": {k: head[k] for k in ("us_per_call", "hbm_TBps", "mfma_pct", "roofline_frac")},

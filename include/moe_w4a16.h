@@ -215,7 +215,7 @@ int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int
  * runs at HBM speed. Small batches therefore run two kernels instead of
  * four, with the routing and grouping inside the FC1 kernel (one of its
  * workgroups also writes the routing/grouping outputs):
- *   - M <= 2 (M*top_k <= 64): the decode path; every FC1 workgroup routes the
+ *   - M = 1: the decode path; every FC1 workgroup routes the
  *     batch, and FC2 is output-stationary (each output tile sums its token's
  *     top_k expert results in slot order in one workgroup: no atomics, and
  *     the bf16 output is then identical on every call);

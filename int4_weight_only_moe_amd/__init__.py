@@ -107,7 +107,7 @@ def layer(logits: torch.Tensor, x: torch.Tensor, rb: RouteBuffers, I: int, w13_p
           w2_packed: torch.Tensor, workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
           stream=None, stage_events=None, fmt: str = "int4") -> torch.Tensor:
     """Routing + expert MLPs in one call. Two kernels while few experts are
-    touched (routing inside FC1, FC2 per token: M <= 2 on the decode path,
+    touched (routing inside FC1, FC2 per token: M = 1 on the decode path,
     up to 16 tokens on the routed FC1), else three up to 16 tokens (routing,
     grouped FC1, FC2 per token), and routing + grouped FC1 + grouped FC2 +
     finalize above. fmt: "int4" (moe_w4a16_repack weights) or "mxfp4"

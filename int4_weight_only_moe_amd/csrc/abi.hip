@@ -282,10 +282,12 @@ static int layer_impl(int fmt, const float* logits, const uint16_t* x_bf16, int3
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t ev0 = stage_events ? (hipEvent_t)stage_events[0] : nullptr;
   hipEvent_t ev1 = stage_events ? (hipEvent_t)stage_events[1] : nullptr;
-  // decode path for one or two tokens; then the routed FC1 while few experts
-  // are touched; the decode path where it fits; else the four kernels
+  // decode path for one token; then the routed FC1 while few experts are
+  // touched (measured on the 384-expert layer: decode 42.9 vs routed 46.4 us
+  // at M = 1, 82.7 vs 80.4 at M = 2); the decode path where it fits; else
+  // the four kernels
   const bool routed = FMT_CALL(fmt, routed_fc1_preferred, M, E, H, I, top_k);
-  if (moe::decode_path_fits(M, H, I, top_k) && (M <= 2 || !routed)) {
+  if (moe::decode_path_fits(M, H, I, top_k) && (M == 1 || !routed)) {
     moe::DecodeArgs d{};
     d.fc = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
                    workspace);
