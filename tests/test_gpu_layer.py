@@ -82,6 +82,28 @@ def test_layer_k26_decode_sizes():
         print(f"layer k26 M={M}: rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
 
 
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_layer_decode_four_tokens_wide_fc1(fmt):
+    """Four tokens, 384 experts, top-8, I = 3840: the routed FC1 would need
+    about 31 distinct experts x 15 groups of 16 pairs = 470 workgroups, more
+    than 1.75 rounds of 256 CUs, while the k activation rows of FC2 still fit
+    64 KB of LDS, so the layer call takes the four-token decode kernels (the
+    only shapes that reach them), in both weight formats."""
+    shape, seed = wl.LayerShape(E=384, H=128, I=3840, k=8), 12
+    print(f"layer decode M=4 {fmt} {shape}", flush=True)
+    layer = device_layer(shape, seed, fmt=fmt)
+    t = wl.tokens(shape, 4, 77)
+    rb = moe.alloc_route_buffers(4, shape.E, shape.k, 16)
+    lg, x = to_dev(t.logits), x_device(t.x_bits)
+    outs = [moe.layer(lg, x, rb, shape.I, layer.w13, layer.w2, fmt=fmt).float().cpu().numpy() for _ in range(2)]
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1]), "decode path must be deterministic"
+    ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, 16)
+    ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,
+                             oracle_experts(shape, seed, fmt=fmt))
+    assert_output_close(outs[0], ref, f"decode M=4 {fmt}")
+
+
 @pytest.mark.parametrize("M", [3, 5, 6, 7, 9, 16, 17, 90])
 def test_layer_k26_grouped_sizes(M):
     """The layer call past the decode sizes, as the benchmark times it: the
