@@ -202,7 +202,11 @@ void fc1_decode_kernel(DecodeArgs d) {
   const int MK = M * k;
   const int npairs = d.fc.I / 16;
   const int blk = blockIdx.x / npairs;
-  const int pair = blockIdx.x % npairs;
+  // Pair index rotated per slot (a bijection within each slot): a CU's
+  // resident workgroups, blockIdx.x apart by the CU count, would otherwise all
+  // read the same offset of different experts, whose bases are 64 KB
+  // multiples; rotated, they read unrelated offsets (measured ~1 % faster).
+  const int pair = (int)((blockIdx.x % npairs + (unsigned)blk * 37u) % (unsigned)npairs);
   const int hv = H / 8;        // 16-byte vectors per x row
   const int row16 = hv + 1;    // padded LDS row stride: rows start on different banks
   const int ng = H / kGroup;   // quantisation groups per row
