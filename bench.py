@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--sweep-steps", type=int, default=200)
     p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--sweep-list", default=None,
+                   help="comma-separated workloads to sweep instead of the default list (for profiling runs)")
+    p.add_argument("--no-graph", action="store_true", help="skip the graph-replay context figure")
     p.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4-weight sweep")
     p.add_argument("--weights", choices=("int4", "mxfp4"), default="int4",
                    help="expert weight format of the headline and the sweep (mxfp4: for profiling that path)")
@@ -306,8 +309,8 @@ class Bench:
         for i in range(steps):
             self.step(c, layers[i % R], evs[i], fmt=fmt)
         torch.cuda.synchronize()
-        fc1_us = float(np.mean([a.elapsed_ms(b) for a, b in evs])) * 1e3
-        return c, total_ms / steps, fc1_us, wall
+        fc1 = np.array([a.elapsed_ms(b) for a, b in evs]) * 1e3
+        return c, total_ms / steps, fc1, wall
 
     def run_graph(self, name, steps, replicas, fmt="int4"):
         """The same K steps captured in one HIP graph and replayed (context)."""
@@ -332,7 +335,8 @@ class Bench:
         return start.elapsed_time(stop) / steps
 
     def record(self, name, steps, warmup, replicas, fmt="int4"):
-        c, ms, fc1_us, wall = self.run(name, steps, warmup, replicas, fmt)
+        c, ms, fc1, wall = self.run(name, steps, warmup, replicas, fmt)
+        fc1_us = float(np.mean(fc1))
         w, s, D = c["w"], self.s, c["D"]
         us = ms * 1e3
         lb = layer_bytes(D, w.M, s, fmt)
@@ -343,6 +347,7 @@ class Bench:
             roofline_frac=round(max(lb / (HBM_PEAK_GBS * 1e9),
                                     flops(w.M, s) / (MFMA_BF16_PEAK_TFS * 1e12)) / (us * 1e-6), 4),
             fc1_us=round(fc1_us, 2), fc1_GBps=round(fc1_bytes(D, w.M, s, fmt) / (fc1_us * 1e-6) / 1e9, 1),
+            fc1_us_p10_p50_p90=[round(float(v), 2) for v in np.percentile(fc1, [10, 50, 90])],
             replicas=min(replicas, len(self.layers)), wall_s=round(wall, 3))
         if fmt != "int4":
             r["weights"] = fmt
@@ -411,7 +416,7 @@ def main():
     fc1_s = head["fc1_us"] * 1e-6
     sweep = []
     if not a.no_sweep:
-        for name in SWEEP:
+        for name in (a.sweep_list.split(",") if a.sweep_list else SWEEP):
             r, _ = b.record(name, a.sweep_steps, 5, a.replicas, fmt)
             sweep.append(r)
             print(f"# {json.dumps(r)}", file=sys.stderr, flush=True)
@@ -443,7 +448,7 @@ def main():
                    "global_batch": M, "block_m": head["block_m"], "experts_touched": D,
                    "weight_copies_cycled": head["replicas"],
                    "launch": "eager, queued ahead of the GPU"},
-        "graph_us_per_call": round(b.run_graph(a.workload, a.steps, a.replicas, fmt) * 1e3, 2),
+        "graph_us_per_call": None if a.no_graph else round(b.run_graph(a.workload, a.steps, a.replicas, fmt) * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(fc1_alg / fc1_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(fc1_alg / fc1_s / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for(fc1_alg) if fmt == "int4" else None,

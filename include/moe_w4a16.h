@@ -159,6 +159,12 @@ int32_t moe_w4a16_preferred_block_m(int32_t M, int32_t E, int32_t H, int32_t I, 
 
 /*
  * moe_w4a16_forward: the expert MLPs and the weighted combine for one batch.
+ * "The Throughput Lever: Quantifying the MoE GEMM and Mapping the Road to
+ * B300", section "Phase 3: The INT4 Marlin MoE Throughput Lever": the MoE
+ * layer's work is a grouped GEMM over the experts with INT4 weights fused into
+ * it (there the fused Marlin MoE kernel), run over the dense token batch;
+ * section "The Result: Two Regimes": each token's top-k expert outputs are
+ * combined with its routing weights.
  * Equivalent to moe_w4a16_fc1 followed by moe_w4a16_fc2 on the same stream.
  *   x_bf16      bf16 [M, H] activations, 16-byte aligned.
  *   topk_weights, sorted_token_ids, block_expert_ids, expert_offsets,
@@ -222,9 +228,10 @@ int moe_w4a16_fc2(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int
  *   - M <= 16 and M*top_k <= 256 while few experts are touched and the
  *     batch's x rows fit in 128 KB of LDS (the grouped FC1 would fill at
  *     most 1.75 rounds of the device's CUs; on the 384-expert top-8 layer
- *     M = 3..7): a persistent FC1 kernel that routes once per workgroup and
- *     splits the work into small items;
- *   - else M <= 4 with M*top_k <= 64: the decode path.
+ *     M = 2..7), and M = 2 or 3 wherever M*top_k <= 64: a persistent FC1
+ *     kernel that routes once per workgroup and splits the work into small
+ *     items (not when the tiled grouped GEMM below takes the batch);
+ *   - else M = 4 with M*top_k <= 64: the decode path.
  * Up to 16 tokens the output-stationary FC2 follows the FC1 while the
  * M*top_k expert reads stay within 1.2x the expected number of distinct
  * experts (no accumulator and no finalize kernel); otherwise the grouped FC2

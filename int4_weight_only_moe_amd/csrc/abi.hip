@@ -196,7 +196,10 @@ static moe::FcArgs fc_args(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, 
   if (use_tiled(fmt, M, E, H, I, top_k)) {
     a.tiles = (int2*)(ws + L.tiles_off);
     a.ntiles = (int32_t*)(ws + L.ntiles_off);
-    a.max_tiles = (int)FMT_CALL(fmt, tile_grid_tiles, M, E, top_k, block_m, cap);
+    // The grid is sized from the padded total this batch can reach, not from
+    // the caller's cap (route buffers may be allocated for a larger batch):
+    // the tile table in the workspace holds tile_table_entries(M, k) entries.
+    a.max_tiles = (int)FMT_CALL(fmt, tile_grid_tiles, M, E, top_k, block_m, capacity(M, E, top_k, block_m));
   }
   return a;
 }
@@ -282,12 +285,20 @@ static int layer_impl(int fmt, const float* logits, const uint16_t* x_bf16, int3
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t ev0 = stage_events ? (hipEvent_t)stage_events[0] : nullptr;
   hipEvent_t ev1 = stage_events ? (hipEvent_t)stage_events[1] : nullptr;
-  // decode path for one token; then the routed FC1 while few experts are
-  // touched (measured on the 384-expert layer: decode 42.9 vs routed 46.4 us
-  // at M = 1, 82.7 vs 80.4 at M = 2); the decode path where it fits; else
-  // the four kernels
-  const bool routed = FMT_CALL(fmt, routed_fc1_preferred, M, E, H, I, top_k);
-  if (moe::decode_path_fits(M, H, I, top_k) && (M == 1 || !routed)) {
+  // The decode path for one token (measured on the 384-expert layer: decode
+  // 42.9 vs routed 46.4 us at M = 1), and for four tokens where the routed
+  // FC1 would not fill the device; the routed FC1 while few experts are
+  // touched (82.7 vs 80.4 us at M = 2), and for two or three tokens wherever
+  // the decode path fits (the routed kernel always fits there); else the
+  // grouped kernels. The routed FC1 writes no tile table, so it is not
+  // combined with the tiled grouped FC2.
+  const bool tiled = use_tiled(fmt, M, E, H, I, top_k);
+  const bool decode_fits = moe::decode_path_fits(M, H, I, top_k);
+  const bool routed_pref = FMT_CALL(fmt, routed_fc1_preferred, M, E, H, I, top_k);
+  const bool decode = decode_fits && (M == 1 || (M == moe::kDecodeMaxTokens && !routed_pref));
+  const bool routed = !decode && !tiled &&
+                      (routed_pref || (decode_fits && FMT_CALL(fmt, routed_fc1_fits, M, E, H, I, top_k)));
+  if (decode) {
     moe::DecodeArgs d{};
     d.fc = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids, num_tokens_post_pad,
                    workspace);

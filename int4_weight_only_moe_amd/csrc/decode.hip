@@ -531,11 +531,12 @@ hipError_t launch_decode_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t
   const unsigned grid1 = (unsigned)(nblk * (d.fc.I / 16));
   const uint32_t xlds = (uint32_t)decode_fc1_lds_bytes(M, d.fc.H);  // staged x rows + corrections
   hipError_t err = hipSuccess;
+  // one token, or exactly four (the layer call sends two and three tokens
+  // to the routed FC1)
   switch (M) {
     case 1: err = launch_fc1_decode<VPL, 1>(d, grid1, xlds, stream, e0, e1); break;
-    case 2: err = launch_fc1_decode<VPL, 2>(d, grid1, xlds, stream, e0, e1); break;
-    case 3: err = launch_fc1_decode<VPL, 3>(d, grid1, xlds, stream, e0, e1); break;
-    default: err = launch_fc1_decode<VPL, 4>(d, grid1, xlds, stream, e0, e1); break;
+    case kDecodeMaxTokens: err = launch_fc1_decode<VPL, kDecodeMaxTokens>(d, grid1, xlds, stream, e0, e1); break;
+    default: return hipErrorInvalidValue;
   }
   if (err != hipSuccess) return err;
   err = hipGetLastError();
@@ -559,14 +560,9 @@ hipError_t launch_fc2_tokens(const DecodeArgs& d2, hipStream_t stream) {
     const unsigned grid2 = (unsigned)(M * (d2.fc.H / 32));
     if (i2048) fc2_decode_kernel<4, 16, 2><<<grid2, 128 * k, lds, stream>>>(d2);
     else fc2_decode_kernel<0, 16, 2><<<grid2, 128 * k, lds, stream>>>(d2);
-  } else {
+  } else {  // top_k > 8: one 16-column tile per workgroup, k <= 16 waves
     const unsigned grid2 = (unsigned)(M * (d2.fc.H / 16));
-    if (k <= 8) {
-      if (i2048) fc2_decode_kernel<4, 8, 1><<<grid2, 64 * k, lds, stream>>>(d2);
-      else fc2_decode_kernel<0, 8, 1><<<grid2, 64 * k, lds, stream>>>(d2);
-    } else {
-      fc2_decode_kernel<0, kMaxTopK, 1><<<grid2, 64 * k, lds, stream>>>(d2);
-    }
+    fc2_decode_kernel<0, kMaxTopK, 1><<<grid2, 64 * k, lds, stream>>>(d2);
   }
   return hipGetLastError();
 }

@@ -178,3 +178,22 @@ def test_layer_decode_ties_and_shared_experts():
                                  oracle_experts(shape, 21))
         assert_output_close(outs[0], ref, f"ties M={M}")
         assert np.array_equal(outs[0], outs[1])
+
+
+def test_layer_routed_sizes_with_tiled_grouped_gemm():
+    """Sixteen tokens on 8 experts with top-8: few experts are touched, so the
+    routed FC1 would be preferred, but every expert holds 16 assignments, so
+    the grouped GEMM is the tiled one. The routed FC1 writes no tile table, so
+    the layer call must take routing + tiled FC1 + tiled FC2 here."""
+    shape, M = wl.LayerShape(E=8, H=256, I=256, k=8), 16
+    assert M * shape.k / shape.E >= 16          # the tiled grouped GEMM's threshold
+    assert M <= 16 and M * shape.k <= 256       # the routed FC1's size limits
+    assert M * shape.k > 1.2 * shape.E          # not the per-token FC2: the grouped FC2 follows
+    layer = device_layer(shape, 31)
+    t = wl.tokens(shape, M, 32)
+    for block_m in (16, 32, 64):
+        rb, outs = run_layer_call(layer, t.logits, t.x_bits, block_m)
+        ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, block_m)
+        ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,
+                                 oracle_experts(shape, 31))
+        assert_output_close(outs[0], ref, f"routed-size tiled B={block_m}")

@@ -51,3 +51,28 @@ def test_tiled_skew_has_multi_tile_experts():
     counts = np.bincount(ids.reshape(-1), minlength=shape.E)
     assert counts.max() > 2 * 128
     assert any(c % 128 and (c % 128) // 16 + 1 in (3, 5, 6, 7) for c in counts)
+
+
+def test_tiled_with_oversized_route_buffers():
+    """Route buffers allocated for a much larger batch (cap far above the
+    capacity of this one): the tiled grid and its tile table depend only on
+    the batch, so the result is unchanged."""
+    import int4_weight_only_moe_amd as moe
+    import torch
+    from gpu_common import to_dev, x_device
+    shape, M, sigma, wseed, tseed = TILED[1]
+    layer = device_layer(shape, wseed)
+    t = wl.tokens(shape, M, tseed, sigma)
+    for block_m in (16, 64):
+        big = moe.alloc_route_buffers(40 * M, shape.E, shape.k, block_m)
+        assert big.cap >= 20 * moe.moe_route_align_capacity(M, shape.E, shape.k, block_m)
+        rb = moe.RouteBuffers(M, shape.E, shape.k, block_m, big.cap, big.topk_ids[:M], big.topk_weights[:M],
+                              big.sorted_token_ids, big.block_expert_ids, big.expert_offsets,
+                              big.num_tokens_post_pad)
+        moe.route_align(to_dev(t.logits), rb)
+        out = moe.forward(x_device(t.x_bits), rb, shape.I, layer.w13, layer.w2).float().cpu().numpy()
+        torch.cuda.synchronize()
+        ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, block_m)
+        ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,
+                                 oracle_experts(shape, wseed))
+        assert_output_close(out, ref, f"oversized cap B={block_m}")
