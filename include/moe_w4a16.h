@@ -66,7 +66,8 @@ enum {
     MOE_ERR_UNSUPPORTED = -2, /* a size outside the limits above */
     MOE_ERR_CAPACITY = -3,    /* cap smaller than moe_route_align_capacity() */
     MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_w4a16_workspace_bytes() */
-    MOE_ERR_HIP = -5          /* a HIP launch failed */
+    MOE_ERR_HIP = -5,         /* a HIP launch failed */
+    MOE_ERR_SCRATCH = -6      /* batch too large for moe_w4a16_layer_noalloc's static scratch */
 };
 
 /* Version of this interface (bumped on any signature or layout change). */
@@ -246,6 +247,31 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
                     int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed, const void* w2_packed,
                     void* workspace, int64_t workspace_bytes, uint16_t* out_bf16, void* stream,
                     void* const* stage_events);
+
+/*
+ * moe_w4a16_layer_noalloc: moe_w4a16_layer without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). The workspace is a
+ * static device array of MOE_W4A16_NOALLOC_SCRATCH_BYTES inside the library:
+ * each GPU the library runs on holds its own copy from the first call on that
+ * device until the process ends (the call resolves its address with
+ * hipGetSymbolAddress on the current device; `stream` must belong to that
+ * device). Arguments, outputs and results are those of moe_w4a16_layer (no
+ * stage events). A batch whose moe_w4a16_workspace_bytes exceeds the scratch
+ * size returns MOE_ERR_SCRATCH and launches nothing (48 MiB covers, e.g., up
+ * to 512 tokens of the 384-expert layer: E = 384, H = 7168, I = 2048, top-8).
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine). Every call on a GPU shares that GPU's scratch, which keeps the
+ * last call's contents (the kernels clear what must start at zero): calls
+ * that overlap on one GPU (several streams, several threads) race and must
+ * be serialised by the caller.
+ */
+#define MOE_W4A16_NOALLOC_SCRATCH_BYTES (48ll << 20)
+int moe_w4a16_layer_noalloc(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H,
+                            int32_t I, int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights,
+                            int32_t* sorted_token_ids, int32_t* block_expert_ids, int32_t* expert_offsets,
+                            int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed,
+                            const void* w2_packed, uint16_t* out_bf16, void* stream);
 
 /*
  * ---- MXFP4 weights --------------------------------------------------------

@@ -16,8 +16,8 @@ import torch
 
 from ._binding import (  # noqa: F401
     GROUP, KIND_W13, KIND_W2, MOE_ERR_CAPACITY, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
-    MOE_ERR_WORKSPACE, MOE_OK, MoeError, lib, library_path, moe_route_align, moe_route_align_capacity,
-    moe_w4a16_abi_version, moe_w4a16_fc1, moe_w4a16_fc2, moe_w4a16_forward, moe_w4a16_layer, moe_w4a16_packed_bytes,
+    MOE_ERR_SCRATCH, MOE_ERR_WORKSPACE, MOE_OK, NOALLOC_SCRATCH_BYTES, MoeError, lib, library_path, moe_route_align, moe_route_align_capacity,
+    moe_w4a16_abi_version, moe_w4a16_fc1, moe_w4a16_fc2, moe_w4a16_forward, moe_w4a16_layer, moe_w4a16_layer_noalloc, moe_w4a16_packed_bytes,
     moe_w4a16_preferred_block_m, moe_w4a16_repack, moe_w4a16_unpack, moe_w4a16_workspace_bytes,
     moe_mxfp4_fc1, moe_mxfp4_fc2, moe_mxfp4_forward, moe_mxfp4_layer, moe_mxfp4_packed_bytes, moe_mxfp4_repack,
     moe_mxfp4_unpack, status_string,

@@ -23,6 +23,7 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_CAPACITY = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_HIP = -5
+MOE_ERR_SCRATCH = -6
 
 KIND_W13 = 0
 KIND_W2 = 1
@@ -53,6 +54,8 @@ _SIGNATURES = {
     "moe_mxfp4_repack": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "moe_mxfp4_unpack": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
 }
+_SIGNATURES["moe_w4a16_layer_noalloc"] = (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                                          _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp])
 # the MXFP4 stages take the same arguments as the INT4 ones
 for _stage in ("fc1", "fc2", "forward", "layer"):
     _SIGNATURES["moe_mxfp4_" + _stage] = _SIGNATURES["moe_w4a16_" + _stage]
@@ -272,6 +275,33 @@ def moe_w4a16_layer(logits: torch.Tensor, x: torch.Tensor, I: int, top_k: int, b
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _ptr(out, torch.bfloat16, "out"),
         _stream(stream), ev)
     _check(_prefix + "_layer", st)
+
+
+def moe_w4a16_layer_noalloc(logits: torch.Tensor, x: torch.Tensor, I: int, top_k: int, block_m: int,
+                            topk_ids: torch.Tensor, topk_weights: torch.Tensor, sorted_token_ids: torch.Tensor,
+                            block_expert_ids: torch.Tensor, expert_offsets: torch.Tensor,
+                            num_tokens_post_pad: torch.Tensor, w13_packed: torch.Tensor, w2_packed: torch.Tensor,
+                            out: torch.Tensor, cap: int | None = None, stream=None) -> None:
+    """moe_w4a16_layer with the library's static scratch as the workspace."""
+    M, E = logits.shape
+    H = x.shape[1]
+    if x.shape[0] != M:
+        raise ValueError("logits and x must have the same number of rows")
+    if cap is None:
+        cap = sorted_token_ids.numel()
+    st = lib().moe_w4a16_layer_noalloc(
+        _ptr(logits, torch.float32, "logits"), _ptr(x, torch.bfloat16, "x"), M, E, H, I, top_k, block_m,
+        _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_weights, torch.float32, "topk_weights"),
+        _ptr(sorted_token_ids, torch.int32, "sorted_token_ids"),
+        _ptr(block_expert_ids, torch.int32, "block_expert_ids"),
+        _ptr(expert_offsets, torch.int32, "expert_offsets"),
+        _ptr(num_tokens_post_pad, torch.int32, "num_tokens_post_pad"), cap,
+        _ptr(w13_packed, torch.uint8, "w13_packed"), _ptr(w2_packed, torch.uint8, "w2_packed"),
+        _ptr(out, torch.bfloat16, "out"), _stream(stream))
+    _check("moe_w4a16_layer_noalloc", st)
+
+
+NOALLOC_SCRATCH_BYTES = 48 << 20  # MOE_W4A16_NOALLOC_SCRATCH_BYTES in the header
 
 
 def moe_mxfp4_forward(*args, **kw) -> None:

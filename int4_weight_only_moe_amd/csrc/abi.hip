@@ -1,6 +1,9 @@
 // Exported C entry points: host-side validation, sizes, and kernel launches.
 // Every check runs before the first HIP call, so an invalid call launches
 // nothing and touches no output.
+#include <atomic>
+#include <mutex>
+
 #include "../../include/moe_w4a16.h"
 #include "internal.h"
 
@@ -57,6 +60,9 @@ const char* moe_w4a16_status_string(int status) {
     case MOE_ERR_CAPACITY: return "cap is smaller than moe_route_align_capacity() or not a multiple of block_m";
     case MOE_ERR_WORKSPACE: return "workspace is smaller than moe_w4a16_workspace_bytes()";
     case MOE_ERR_HIP: return "a HIP kernel launch failed";
+    case MOE_ERR_SCRATCH:
+      return "the batch needs more workspace than moe_w4a16_layer_noalloc's static scratch "
+             "(MOE_W4A16_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -394,6 +400,58 @@ int moe_w4a16_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
   return layer_impl(moe::kFmtInt4, logits, x_bf16, M, E, H, I, top_k, block_m, topk_ids, topk_weights, sorted_token_ids,
                     block_expert_ids, expert_offsets, num_tokens_post_pad, cap, w13_packed, w2_packed, workspace,
                     workspace_bytes, out_bf16, stream, stage_events);
+}
+
+}  // extern "C"
+
+// ---- the no-allocation layer call -----------------------------------------
+// Its workspace: one static device array per GPU (the library allocates
+// nothing). In host code `scratch` names a host-side stand-in, not device
+// memory: the device address comes from hipGetSymbolAddress, once per device
+// with that device current, and only that address is handed to kernels.
+namespace {
+constexpr int64_t kScratchBytes = MOE_W4A16_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address (resolved on the first call on it).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_HIP;
+  if (dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_w4a16_layer_noalloc(const float* logits, const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I,
+                            int32_t top_k, int32_t block_m, int32_t* topk_ids, float* topk_weights,
+                            int32_t* sorted_token_ids, int32_t* block_expert_ids, int32_t* expert_offsets,
+                            int32_t* num_tokens_post_pad, int64_t cap, const void* w13_packed, const void* w2_packed,
+                            uint16_t* out_bf16, void* stream) {
+  int st = check_layer(M, E, H, I, top_k);
+  if (st != MOE_OK || M == 0) return st;
+  const int64_t need = moe::workspace_layout(M, H, I, top_k).total;
+  if (need > kScratchBytes) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MOE_OK) return st;
+  return layer_impl(moe::kFmtInt4, logits, x_bf16, M, E, H, I, top_k, block_m, topk_ids, topk_weights,
+                    sorted_token_ids, block_expert_ids, expert_offsets, num_tokens_post_pad, cap, w13_packed,
+                    w2_packed, ws, need, out_bf16, stream, nullptr);
 }
 
 int moe_mxfp4_fc1(const uint16_t* x_bf16, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
