@@ -354,31 +354,82 @@ class Bench:
         return r, c
 
     def cpu_baseline(self, c, budget_s=12.0):
-        """The oracle (as it stands) on the headline batch, repeated for about budget_s seconds."""
+        """The oracle (as it stands) on the headline batch, repeated for about
+        budget_s seconds on one thread (BLAS limited to one thread), and the
+        two costs the per-workload estimates are built from: dequantising one
+        expert (W13 and W2, float64) and one expert MLP on one token."""
         import oracle
         import workloads as wl
+        from threadpoolctl import threadpool_limits
         w13, s13, w2, s2 = self.host
-        cache = oracle.DequantCache(lambda e: (w13[e], s13[e], w2[e], s2[e]), max_items=0)
         t = c["t"]
         x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)
-        tokens, n = 0, 0
-        t0 = time.perf_counter()
-        while True:
-            oracle.layer(x, t.logits, self.s.k, cache)
-            tokens += t.logits.shape[0]
-            n += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        el = time.perf_counter() - t0
-        try:
-            from threadpoolctl import threadpool_info
-            blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-        except Exception:
-            blas = 1
-        return {"value": round(el / tokens * 1e6, 1), "unit": "us/token", "cores": int(blas), "kind": "oracle",
-                "sample": f"{n} full oracle calls (route, dequantise 8 experts in float64, expert MLPs, combine) "
-                          f"on the {c['w'].M}-token batch, {el:.1f} s; dequantisation single-threaded numpy, "
-                          f"matmuls on {blas} BLAS threads; host has {len(os.sched_getaffinity(0))} cores"}
+        with threadpool_limits(limits=1):
+            cache = oracle.DequantCache(lambda e: (w13[e], s13[e], w2[e], s2[e]), max_items=0)
+            tokens, n = 0, 0
+            t0 = time.perf_counter()
+            while True:
+                oracle.layer(x, t.logits, self.s.k, cache)
+                tokens += t.logits.shape[0]
+                n += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            el = time.perf_counter() - t0
+            # the parts: one expert's dequantisation, one expert MLP on one token
+            reps = 3
+            t1 = time.perf_counter()
+            for e in range(reps):
+                W13, W2 = cache(e)
+            t_deq = (time.perf_counter() - t1) / reps
+            t2 = time.perf_counter()
+            for _ in range(20):
+                oracle.expert_mlp(x[0], W13, W2)
+            t_mlp = (time.perf_counter() - t2) / 20
+        self.oracle_parts = (t_deq, t_mlp)
+        host = len(os.sched_getaffinity(0))
+        return {"value": round(el / tokens * 1e6, 1), "unit": "us/token", "cores": 1, "kind": "oracle",
+                "host_cores": host, "blas_threads": 1,
+                "dequant_expert_s": round(t_deq, 4), "expert_mlp_token_s": round(t_mlp, 5),
+                "sample": f"{n} full oracle calls (route, dequantise the 8 experts in float64, expert MLPs, "
+                          f"combine) on the {c['w'].M}-token batch, {el:.1f} s on one thread (numpy, BLAS limited "
+                          f"to one thread) of a {host}-core host"}
+
+    def cpu_estimate(self, r):
+        """Oracle time per token for a sweep entry from the measured parts: each
+        touched expert dequantised once (a cache holding the batch's experts)
+        plus one expert MLP per (token, slot); one thread."""
+        t_deq, t_mlp = self.oracle_parts
+        M, D = r["M"], r["experts_touched"]
+        return round((D * t_deq + M * self.s.k * t_mlp) / M * 1e6, 1)
+
+    def attainable(self):
+        """Attainable peaks measured here: HBM read+write rate of a 1 GiB device
+        copy, and the dense bf16 matrix rate of an 8192^3 torch matmul."""
+        torch = self.torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+        b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+        for _ in range(3):
+            dst.copy_(src)
+            torch.matmul(a, b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        bw = 2 * src.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        e0.record()
+        for _ in range(10):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        tf = 2 * 8192 ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        del src, dst, a, b
+        return {"hbm_GBps": round(bw, 1), "bf16_TFps": round(tf, 1),
+                "how": "1 GiB device copy (bytes read + written); 8192^3 bf16 torch.matmul"}
 
 
 def traffic_for(launch_bytes_alg):
@@ -430,6 +481,14 @@ def main():
             mxfp4.append(r)
             print(f"# {json.dumps(r)}", file=sys.stderr, flush=True)
     cpu = None if a.no_cpu_baseline else b.cpu_baseline(c)
+    att = b.attainable()
+    for r in [head] + sweep + mxfp4:
+        lb = layer_bytes(r["experts_touched"], r["M"], b.s, r.get("weights", "int4"))
+        r["frac_attainable"] = round(max(lb / (att["hbm_GBps"] * 1e9), flops(r["M"], b.s) / (att["bf16_TFps"] * 1e12))
+                                     / (r["us_per_call"] * 1e-6), 4)
+        if cpu is not None and r.get("weights", "int4") == "int4":
+            r["cpu_us_per_token"] = b.cpu_estimate(r)
+            r["cpu_cores"] = 1
     line = {
         "metric": "MoE layer us/token (+ achieved HBM TB/s, MFMA %) on the 384-expert INT4 g32 layer",
         "value": head["us_per_token"],
@@ -455,7 +514,9 @@ def main():
                      "kernel": "FC1 stage (fc1_decode_kernel at M = 1, fc1_routed_kernel for few touched experts, "
                                "else the grouped FC1 kernel)",
                      "kernel_avg_us": head["fc1_us"], "algorithmic_bytes": fc1_alg},
-        "layer": {k: head[k] for k in ("us_per_call", "hbm_TBps", "mfma_pct", "roofline_frac")},
+        "layer": {k: head[k] for k in ("us_per_call", "hbm_TBps", "mfma_pct", "roofline_frac", "frac_attainable",
+                                       "fc1_us_p10_p50_p90")},
+        "attainable_peaks": att,
         "repack_ms": round(b.repack_ms, 2),
         "sweep": sweep,
         "mxfp4_sweep": mxfp4,

@@ -120,7 +120,9 @@ int moe_route_align(const float* logits, int32_t M, int32_t E, int32_t top_k, in
 /*
  * moe_w4a16_packed_bytes (host): size of the repacked weights of E experts
  * of an [N, K] INT4 matrix with the given group size: E*N*K*9/16 (nibbles plus
- * fp16 scales). Returns -1 unless group == 32, N % 32 == 0 and K % 128 == 0.
+ * fp16 scales) + E*N (one int8 exponent shift per weight row, derived from its
+ * scales, used by the large-batch kernels). Returns -1 unless group == 32,
+ * N % 32 == 0 and K % 128 == 0.
  */
 int64_t moe_w4a16_packed_bytes(int32_t E, int32_t N, int32_t K, int32_t group);
 
@@ -134,7 +136,9 @@ int64_t moe_w4a16_packed_bytes(int32_t E, int32_t N, int32_t K, int32_t group);
  *   qweight  uint8 [E, N, K/2], scales_f16 uint16 [E, N, K/32] (canonical).
  *   kind     0 = W13 (N = 2I, K = H), 1 = W2 (N = H, K = I).
  *   packed   out, moe_w4a16_packed_bytes(E, N, K, group) bytes, 16-byte aligned.
- * The map is a bijection: moe_w4a16_unpack inverts it exactly.
+ * The map is a bijection: moe_w4a16_unpack inverts it exactly (the row
+ * shifts after the tiles are derived data: sigma = clamp(floor(log2(max over
+ * the row's groups of |scale|)) - 11, -15, 4), 0 for a row of zero scales).
  */
 int moe_w4a16_repack(const uint8_t* qweight, const uint16_t* scales_f16,
                      int32_t E, int32_t N, int32_t K, int32_t group, int32_t kind,
@@ -148,7 +152,9 @@ int moe_w4a16_unpack(const void* packed, int32_t E, int32_t N, int32_t K, int32_
  * moe_w4a16_workspace_bytes (host): scratch the forward needs for M tokens:
  * an fp32 [M, H] accumulator, the bf16 [M*top_k, I] FC1 activations, and
  * the tile table of the tiled grouped GEMM (256 bytes + (2*M*top_k + 16) x
- * 8 bytes), each padded to 256 bytes. Returns -1 on invalid sizes.
+ * 8 bytes); from M*top_k >= 16*E on also fp16 copies of the A rows
+ * (max(M*H, M*top_k*I) x 2 bytes) and their exponents (M*top_k x 4 bytes).
+ * Each part is padded to 256 bytes. Returns -1 on invalid sizes.
  */
 int64_t moe_w4a16_workspace_bytes(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k);
 
@@ -178,6 +184,14 @@ int32_t moe_w4a16_preferred_block_m(int32_t M, int32_t E, int32_t H, int32_t I, 
  *               FC2_e(SiLU(gate_e(x_t)) * up_e(x_t)), e = topk_ids[t, j],
  *               accumulated in fp32 and rounded once to bf16. The FC1
  *               activation is stored as bf16 between the two GEMMs.
+ * Numerics by regime. While experts average fewer than 16 assignments
+ * (M*top_k < 16*E) each group's partial product uses the exact weights
+ * q*s (scale applied to the fp32 product). From 16 on ("The Result: Two
+ * Regimes": the compute-heavy regime) the weights enter the matrix core as
+ * fp16(q * s * 2^-sigma), one rounding of the exact product (relative error
+ * <= 2^-11), and each activation row as an exact fp16 copy scaled by a power
+ * of two; the shifts are undone exactly in fp32. Both stay within the
+ * layer's error bound against a float64 reference.
  * Float results may differ in the last bits between calls (the k
  * contributions are added with fp32 atomics in arrival order).
  */

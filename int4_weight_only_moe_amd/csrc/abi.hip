@@ -13,7 +13,7 @@ using moe::kChunkK;
 using moe::kGroup;
 using moe::kPairRows;
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 constexpr int32_t kMaxExperts = 1024;
 using moe::kMaxTopK;
 
@@ -96,7 +96,7 @@ int moe_route_align(const float* logits, int32_t M, int32_t E, int32_t top_k, in
 
 int64_t moe_w4a16_packed_bytes(int32_t E, int32_t N, int32_t K, int32_t group) {
   if (E <= 0 || N <= 0 || K <= 0 || group != kGroup || N % kPairRows != 0 || K % kChunkK != 0) return -1;
-  return (int64_t)E * moe::packed_bytes_fmt(moe::kFmtInt4, N, K);
+  return (int64_t)E * moe::packed_bytes_fmt(moe::kFmtInt4, N, K) + moe::sigma_trailer_bytes(moe::kFmtInt4, E, N);
 }
 
 int64_t moe_mxfp4_packed_bytes(int32_t E, int32_t N, int32_t K) {
@@ -149,7 +149,7 @@ int moe_mxfp4_unpack(const void* packed, int32_t E, int32_t N, int32_t K, int32_
 
 int64_t moe_w4a16_workspace_bytes(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
   if (check_layer(M, E, H, I, top_k) != MOE_OK) return -1;
-  return moe::workspace_layout(M, H, I, top_k).total;
+  return moe::workspace_layout(M, E, H, I, top_k).total;
 }
 
 int32_t moe_w4a16_preferred_block_m(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
@@ -172,24 +172,41 @@ static int check_fc(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, i
   if (!block_m_ok(block_m)) return MOE_ERR_UNSUPPORTED;
   if (M == 0) return MOE_OK;
   if (cap < capacity(M, E, top_k, block_m) || cap % block_m != 0) return MOE_ERR_CAPACITY;
-  if (workspace_bytes < moe::workspace_layout(M, H, I, top_k).total) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < moe::workspace_layout(M, E, H, I, top_k).total) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 
-// The tiled grouped GEMM (up to 128-row tiles) takes over from the block
-// kernels once experts average this many assignments.
+// The tiled grouped GEMMs take over from the block kernels once experts
+// average this many assignments: the scale-before kernel (128-row tiles,
+// fc_tile128.hip) where the shape divides into its pair groups, else the
+// exact-scaling one (64-row tiles, fc_tile.hip).
 #ifndef MOE_TILED_MIN_PER_EXPERT
 #define MOE_TILED_MIN_PER_EXPERT 16.0
 #endif
+enum TiledKind { kNotTiled = 0, kTiledExact = 1, kTiledBig = 2 };
+static TiledKind tiled_kind(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
+  if (moe::big_tile_batch(M, E, top_k) && FMT_CALL(fmt, big_tile_supported, H, I)) return kTiledBig;
+  if (FMT_CALL(fmt, tile_path_supported, H, I) && (double)M * top_k / E >= MOE_TILED_MIN_PER_EXPERT)
+    return kTiledExact;
+  return kNotTiled;
+}
 static bool use_tiled(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
-  return FMT_CALL(fmt, tile_path_supported, H, I) && (double)M * top_k / E >= MOE_TILED_MIN_PER_EXPERT;
+  return tiled_kind(fmt, M, E, H, I, top_k) != kNotTiled;
+}
+
+// The weights a stage reads: the blob and, for INT4, its per-row shifts.
+static void set_weights(moe::FcArgs& a, int fmt, const void* packed, int32_t N, int32_t K) {
+  a.wpacked = (const uint8_t*)packed;
+  a.wsigma = fmt == moe::kFmtInt4
+                 ? (const int8_t*)(a.wpacked + (int64_t)a.E * moe::packed_bytes_fmt(moe::kFmtInt4, N, K))
+                 : nullptr;
 }
 
 static moe::FcArgs fc_args(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m,
                            int64_t cap, const int32_t* sorted_ids, const int32_t* block_expert,
                            const int32_t* npp, void* workspace) {
   moe::FcArgs a{};
-  const moe::WorkspaceLayout L = moe::workspace_layout(M, H, I, top_k);
+  const moe::WorkspaceLayout L = moe::workspace_layout(M, E, H, I, top_k);
   uint8_t* ws = (uint8_t*)workspace;
   a.sorted_ids = sorted_ids;
   a.block_expert = block_expert;
@@ -199,13 +216,20 @@ static moe::FcArgs fc_args(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, 
   a.M = M; a.E = E; a.H = H; a.I = I; a.k = top_k; a.block_m = block_m;
   a.cap = cap;
   a.zero_words16 = (int64_t)M * H * 4 / 16;
-  if (use_tiled(fmt, M, E, H, I, top_k)) {
+  const TiledKind tk = tiled_kind(fmt, M, E, H, I, top_k);
+  if (tk != kNotTiled) {
     a.tiles = (int2*)(ws + L.tiles_off);
     a.ntiles = (int32_t*)(ws + L.ntiles_off);
+    a.tile_rows = tk == kTiledBig ? moe::kBigTileRows : moe::kTileMaxRows;
     // The grid is sized from the padded total this batch can reach, not from
     // the caller's cap (route buffers may be allocated for a larger batch):
     // the tile table in the workspace holds tile_table_entries(M, k) entries.
-    a.max_tiles = (int)FMT_CALL(fmt, tile_grid_tiles, M, E, top_k, block_m, capacity(M, E, top_k, block_m));
+    a.max_tiles =
+        (int)FMT_CALL(fmt, tile_grid_tiles, M, E, top_k, block_m, capacity(M, E, top_k, block_m), a.tile_rows);
+    if (tk == kTiledBig) {  // the workspace has the fp16 row copies (big_tile_batch)
+      a.a16 = (uint16_t*)(ws + L.a16_off);
+      a.a16_exp = (int32_t*)(ws + L.a16exp_off);
+    }
   }
   return a;
 }
@@ -224,7 +248,7 @@ static int fc1_impl(int fmt, const uint16_t* x_bf16, int32_t M, int32_t E, int32
   moe::FcArgs a = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
                           num_tokens_post_pad, workspace);
   a.act_in = x_bf16;
-  a.wpacked = (const uint8_t*)w13_packed;
+  set_weights(a, fmt, w13_packed, 2 * I, H);
   return hip_status(FMT_CALL(fmt, launch_fc1, a, (hipStream_t)stream));
 }
 
@@ -244,7 +268,7 @@ static int fc2_impl(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t
                           num_tokens_post_pad, workspace);
   a.act_in = a.act_out;  // FC2 reads the FC1 activations
   a.act_out = nullptr;
-  a.wpacked = (const uint8_t*)w2_packed;
+  set_weights(a, fmt, w2_packed, H, I);
   a.topk_weights = topk_weights;
   a.out = out_bf16;
   return hip_status(FMT_CALL(fmt, launch_fc2, a, (hipStream_t)stream));
@@ -347,7 +371,7 @@ static int layer_impl(int fmt, const float* logits, const uint16_t* x_bf16, int3
     moe::FcArgs a = fc_args(fmt, M, E, H, I, top_k, block_m, cap, sorted_token_ids, block_expert_ids,
                             num_tokens_post_pad, workspace);
     a.act_in = x_bf16;
-    a.wpacked = (const uint8_t*)w13_packed;
+    set_weights(a, fmt, w13_packed, 2 * I, H);
     st = hip_status(FMT_CALL(fmt, launch_fc1, a, s, ev0, ev1));
   }
   if (st != MOE_OK) return st;
@@ -444,7 +468,7 @@ int moe_w4a16_layer_noalloc(const float* logits, const uint16_t* x_bf16, int32_t
                             uint16_t* out_bf16, void* stream) {
   int st = check_layer(M, E, H, I, top_k);
   if (st != MOE_OK || M == 0) return st;
-  const int64_t need = moe::workspace_layout(M, H, I, top_k).total;
+  const int64_t need = moe::workspace_layout(M, E, H, I, top_k).total;
   if (need > kScratchBytes) return MOE_ERR_SCRATCH;
   void* ws = nullptr;
   st = scratch_address(&ws);

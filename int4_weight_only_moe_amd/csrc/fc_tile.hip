@@ -13,9 +13,10 @@
 //
 // Work decomposition:
 //   * a plan kernel cuts each expert's row range (block_m-padded, from
-//     moe_route_align) into tiles of up to 64 rows: a tile starts at every
-//     expert change and at every 64-row boundary of the padded list, so an
-//     expert holding hundreds of rows gets several 64-row tiles; a tile
+//     moe_route_align) into tiles of up to 64 rows (128 for the scale-before
+//     kernel of fc_tile128.hip): a tile starts at every expert change and at
+//     every 64-row boundary of the padded list, so an expert holding hundreds
+//     of rows gets several 64-row tiles; a tile
 //     counts only the 16-row sub-tiles that hold a row (padding is not
 //     multiplied);
 //   * a workgroup = one tile x 8 tile pairs (one per wave, full K); the
@@ -52,15 +53,16 @@ constexpr int kTXcds = 8;
 
 // ---------------------------------------------------------------------------
 // Plan: one workgroup turns the block list into the tile list.
+// tile_rows: 64 (this file's kernel) or 128 (the scale-before kernel).
 __global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restrict__ block_expert,
                                                         const int32_t* __restrict__ sorted_ids,
                                                         const int32_t* __restrict__ npp_p, int block_m, int MK,
-                                                        int max_tiles, int2* __restrict__ tiles,
+                                                        int tile_rows, int max_tiles, int2* __restrict__ tiles,
                                                         int32_t* __restrict__ ntiles_out) {
   __shared__ int wave_cnt[16];
   __shared__ int base;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bpt = kTileMaxRows / block_m;  // blocks per full tile
+  const int bpt = tile_rows / block_m;  // blocks per full tile
   const int nblk = *npp_p / block_m;
   if (tid == 0) base = 0;
   __syncthreads();
@@ -318,8 +320,8 @@ __global__ __launch_bounds__(64 * kTW) __attribute__((amdgpu_waves_per_eu(4))) v
 
 }  // namespace
 
-int64_t tile_grid_tiles(int64_t M, int64_t E, int64_t k, int64_t block_m, int64_t cap) {
-  const int64_t bpt = kTileMaxRows / block_m;
+int64_t tile_grid_tiles(int64_t M, int64_t E, int64_t k, int64_t block_m, int64_t cap, int64_t tile_rows) {
+  const int64_t bpt = tile_rows / block_m;
   const int64_t nblk = cap / block_m;
   const int64_t mk = M * k;
   const int64_t t = (nblk + bpt - 1) / bpt + (mk < E ? mk : E);
@@ -334,7 +336,7 @@ bool tile_path_supported(int64_t H, int64_t I) {
 
 hipError_t launch_tile_plan(const FcArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, stream, a.block_expert, a.sorted_ids, a.npp,
-                     a.block_m, a.M * a.k, a.max_tiles, a.tiles, a.ntiles);
+                     a.block_m, a.M * a.k, a.tile_rows, a.max_tiles, a.tiles, a.ntiles);
   return hipGetLastError();
 }
 

@@ -1,0 +1,496 @@
+// Grouped GEMM (FC1 and FC2) with the group scales applied before the
+// product, on tiles of up to 128 rows: the large-batch regime.
+//
+// "The Throughput Lever: Quantifying the MoE GEMM and Mapping the Road to
+// B300", section "The Result: Two Regimes": once every expert holds tens to
+// hundreds of rows, the grouped GEMM is matrix work rather than a stream of
+// weights. On gfx950 the exact tiled kernel (fc_tile.hip) then runs out of
+// vector issue slots: it applies each group's scale to the fp32 MFMA result
+// (one FMA per output and group, plus a correction MFMA per group). Here the
+// weights enter the matrix core already scaled, so every MFMA accumulates
+// straight into its output and the vector work per weight is shared by all
+// rows of the tile:
+//   * INT4: B = fp16(q * s'), one rounding of the exact product, where
+//     s' = s * 2^-sigma and sigma is the per-weight-row exponent shift the
+//     repack stores after the tiles (it keeps q * s' a normal fp16 below 2^15
+//     for any finite scale; 2^sigma is applied exactly in the epilogue). The
+//     A rows are fp16 copies of the bf16 activations, each row scaled by a
+//     power of two so that its largest value lies in [2^14, 2^15) (exact:
+//     fp16 holds every bf16 significand); the row's exponent is applied in
+//     the epilogue. v_mfma_f32_16x16x32_f16 accumulates in fp32.
+//   * MXFP4: the exact bf16 values code * 2^(s - 127) with the bf16 MFMA, A
+//     the bf16 activations themselves.
+// Work decomposition:
+//   * tiles of up to 128 rows of one expert (the plan kernel of fc_tile.hip
+//     with 128-row tiles): one tile pair per wave, 8 waves per workgroup,
+//     one workgroup per CU (two waves per SIMD, up to 256 VGPRs; 72 KB of LDS);
+//   * the tile's activation chunk (128 rows x 128 channels) is copied from
+//     memory straight into LDS by gfx950's buffer loads to LDS (no staging
+//     registers or stores), double-buffered; a row's sixteen 16-byte vectors
+//     are stored XOR-swizzled with the row index, so the A reads of a wave
+//     (16 rows, one vector each) hit 16 different bank groups;
+//   * per 32-channel group a wave widens both tiles' codes once and runs
+//     2 x S MFMAs (S = sub-tiles of 16 rows: 2, 4, 6 or 8);
+//   * per chunk step: the next chunk's rows go to LDS, the current chunk is
+//     computed, the weight chunk after next is loaded, then one wait (the
+//     rows and the next weight chunk; the newest weight loads stay in flight)
+//     and one barrier. The waits are explicit: a workgroup fence would drain
+//     every load in flight.
+// Epilogues as in the other grouped kernels: FC1 stores bf16 SiLU(gate)*up,
+// FC2 adds w_f * y_f into the fp32 accumulator with atomics.
+#include "internal.h"
+#include "device_common.h"
+#include "fc_common.h"
+
+namespace moe {
+namespace MOE_FMT_NS {
+namespace {
+
+constexpr int kBW = 8;                       // waves (= tile pairs) per workgroup
+constexpr int kBVecs = kChunkK / 8;          // 16-byte vectors of a row's chunk slice
+constexpr int kBSlotVecs = kBigTileRows * kBVecs;  // one LDS slot: 128 rows x 16 vectors = 32 KB
+constexpr int kBXcds = 8;
+constexpr int kBWLoads = 4;                  // vector loads per weight chunk (2 tiles' codes + scales)
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= v, lgkmcnt <= l, expcnt not waited for.
+constexpr int waitcnt_imm(int v, int l) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (l << 8); }
+
+__device__ __forceinline__ f16x2_t as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2_t, u); }
+
+// Eight INT4 codes (one dword of the tile layout: code 2p in bits [4p, 4p+4),
+// code 2p+1 in bits [16+4p, 20+4p)) -> eight fp16 values fp16(q * s2), q = u - 8.
+// A code at bits 0..3 of a half, OR-ed into fp16 1024.0 (ulp 1), gives
+// 1032 + q; at bits 4..7, OR-ed into fp16 64.0 (ulp 1/16), 72 + q. Both
+// differences are exact, so the only rounding is that of the product.
+__device__ __forceinline__ f16x8_t dequant_int4_f16(uint32_t w, f16x2_t s2) {
+  uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, c0 = 0x64006400u, c1 = 0x54005400u;
+  asm("" : "+s"(m0));
+  asm("" : "+s"(m1));
+  asm("" : "+v"(c0));
+  asm("" : "+v"(c1));
+  uint32_t o0 = 0xE408E408u, o1 = 0xD480D480u;  // fp16 pairs (-1032, -1032), (-72, -72)
+  asm("" : "+s"(o0));
+  asm("" : "+s"(o1));
+  const uint32_t t = w >> 8;
+  const f16x2_t p0 = (as_f16x2((w & m0) | c0) + as_f16x2(o0)) * s2;
+  const f16x2_t p1 = (as_f16x2((w & m1) | c1) + as_f16x2(o1)) * s2;
+  const f16x2_t p2 = (as_f16x2((t & m0) | c0) + as_f16x2(o0)) * s2;
+  const f16x2_t p3 = (as_f16x2((t & m1) | c1) + as_f16x2(o1)) * s2;
+  return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                 __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// (2^-sigma0, 2^-sigma1) for two rows' shifts (|sigma| <= 15: normal fp16 values).
+__device__ __forceinline__ f16x2_t pow2_pair(int sigma0, int sigma1) {
+  return f16x2_t{(_Float16)__builtin_ldexpf(1.0f, -sigma0), (_Float16)__builtin_ldexpf(1.0f, -sigma1)};
+}
+// The shifts of this lane's two weight rows (column lane % 16 of each tile of
+// the pair) in the sigma trailer of expert e.
+template <bool kFc1>
+__device__ __forceinline__ void row_sigmas(const FcArgs& a, int e, int pair, int lane, int& sig0, int& sig1) {
+  const int N = kFc1 ? 2 * a.I : a.H;
+  const int r = lane & 15;
+  const int64_t n0 = kFc1 ? 16 * pair + r : 32 * pair + r;
+  const int64_t n1 = kFc1 ? a.I + 16 * pair + r : 32 * pair + 16 + r;
+  sig0 = a.wsigma[(int64_t)e * N + n0];
+  sig1 = a.wsigma[(int64_t)e * N + n1];
+}
+
+// The row id an A row of the tile reads: its token (FC1) or assignment (FC2).
+template <bool kFc1>
+__device__ __forceinline__ uint32_t a_row(int f, int k) { return (uint32_t)(kFc1 ? f / k : f); }
+
+// Epilogue of the tile pair for rows frow (per sub-tile, the row of lane % 16):
+// INT4 scales each output by 2^(row exponent + sigma of its weight row).
+template <int S, bool kFc1>
+__device__ __forceinline__ void big_epilogue(const FcArgs& a, const int e, const int pair, const int (&frow)[S],
+                                             const int nsub, const f32x4_t (&acc0)[S], const f32x4_t (&acc1)[S],
+                                             const int lane) {
+  const int MK = a.M * a.k;
+  const int col = lane & 15;
+  int sig0 = 0, sig1 = 0;  // read again here rather than kept live across the main loop
+  if constexpr (kFmt == kFmtInt4) row_sigmas<kFc1>(a, e, pair, lane, sig0, sig1);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if (s >= nsub) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = __shfl(frow[s], 4 * (lane >> 4) + i, 64);
+      if (f < 0 || f >= MK) continue;
+      float v0 = acc0[s][i], v1 = acc1[s][i];
+      if constexpr (kFmt == kFmtInt4) {
+        const int ex = a.row_exp[kFc1 ? f / a.k : f];
+        v0 = __builtin_ldexpf(v0, ex + sig0);
+        v1 = __builtin_ldexpf(v1, ex + sig1);
+      }
+      if constexpr (kFc1) {
+        const float act = v0 / (1.0f + __expf(-v0)) * v1;
+        a.act_out[(int64_t)f * a.I + 16 * pair + col] = (uint16_t)f32_to_bf16_bits(act);
+      } else {
+        const int t = f / a.k;
+        const float w = a.topk_weights[f];
+        float* dst = a.acc + (int64_t)t * a.H + kPairRows * pair;
+        unsafeAtomicAdd(dst + col, w * v0);
+        unsafeAtomicAdd(dst + 16 + col, w * v1);
+      }
+    }
+  }
+}
+
+// One workgroup's tile (rows row0 .. row0 + 16 * nsub of the sorted list,
+// expert e) times this wave's tile pair; S >= nsub sub-tiles (S even: each
+// wave copies S / 2 KB of every chunk to LDS), weights under cache policy
+// kPolicy.
+template <int S, bool kFc1, int kPolicy>
+__device__ __forceinline__ void big_tile_body(const FcArgs& a, const int e, const int pair, const int row0,
+                                              const int nsub, uint4* xt0, uint4* xt1, uint32_t* xoffs) {
+  static_assert(S % 2 == 0 && S * kTileRows <= kBigTileRows, "S even, at most 8 sub-tiles");
+  constexpr int kD = S / 2;  // 1 KB copies per wave per chunk
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = kFc1 ? a.H : a.I;
+  const int N = kFc1 ? 2 * a.I : a.H;
+  const int MK = a.M * a.k;
+  const int n = K / kChunkK;
+  const int32_t* rows = a.sorted_ids + row0;
+
+  // Weight stream of the pair (a chunk past the K range reads zeros).
+  const uint8_t* wbase = a.wpacked + (int64_t)e * packed_bytes_per_expert(N, K) + (int64_t)pair * n * kPairChunkBytes;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)n * kPairChunkBytes);
+  const uint32_t oq0 = 16u * lane, oq1 = kTileBytes + 16u * lane;
+  const uint32_t os0 = kTileNibbleBytes + kScaleRowBytes * (lane & 15);
+  const uint32_t os1 = kTileBytes + kTileNibbleBytes + kScaleRowBytes * (lane & 15);
+  auto load_w = [&](int c) {
+    const uint32_t base = (uint32_t)c * kPairChunkBytes;
+    WChunk w;
+    w.q0 = bload16<kPolicy>(wr, base + oq0);
+    w.q1 = bload16<kPolicy>(wr, base + oq1);
+    w.s0 = load_scales<kPolicy>(wr, base + os0);
+    w.s1 = load_scales<kPolicy>(wr, base + os1);
+    return w;
+  };
+  WChunk wb[2];
+  wb[0] = load_w(0);
+
+  // 2^-sigma of this lane's two weight rows (column lane % 16 of each tile).
+  f16x2_t m2 = {(_Float16)1.0f, (_Float16)1.0f};
+  if constexpr (kFmt == kFmtInt4) {
+    int sig0, sig1;
+    row_sigmas<kFc1>(a, e, pair, lane, sig0, sig1);
+    m2 = pow2_pair(sig0, sig1);
+  }
+
+  // A rows: copy i of this wave covers LDS rows 4 * (wave + 8i) .. +3 of a
+  // slot; lane L writes row 4 * (wave + 8i) + L / 16, LDS vector L % 16,
+  // which holds channel vector (L % 16) ^ (row % 16). Rows past the tile's
+  // sub-tiles and padding entries read the tile's first row (their D rows are
+  // not stored).
+  const int rows_total = kFc1 ? a.M : MK;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.act_in, (uint32_t)rows_total * (uint32_t)K * 2u);
+  const uint32_t rid0 = a_row<kFc1>(rows[0], a.k);
+  // The per-lane source offsets are kept in LDS (this thread's kD words),
+  // not in registers: they are needed only while the copies are issued.
+  uint32_t* myoff = xoffs + tid * (kBigTileRows / kTileRows / 2);
+#pragma unroll
+  for (int i = 0; i < kD; ++i) {
+    const int r = 4 * (wave + kBW * i) + (lane >> 4);
+    const int f = r < kTileRows * nsub ? rows[r] : MK;
+    const uint32_t rid = (f >= 0 && f < MK) ? a_row<kFc1>(f, a.k) : rid0;
+    const uint32_t v = (uint32_t)((lane & 15) ^ (r & 15));
+    myoff[i] = (rid * (uint32_t)K + 8u * v) * 2u;
+  }
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  auto copy_rows = [&](int c, int slot) {
+    uint32_t xoff[kD];
+#pragma unroll
+    for (int i = 0; i < kD; ++i) xoff[i] = myoff[i];
+#pragma unroll
+    for (int i = 0; i < kD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)((slot ? xt1 : xt0) + (wave + kBW * i) * 64), 16,
+                                               xoff[i], (uint32_t)c * (kChunkK * 2), 0, 0);
+  };
+  // LDS vector of this lane's A operand for group g of sub-tile 0 (slot 0):
+  // row m = lane % 16, channel vector 4g + lane / 16, stored at vector
+  // (4g + lane / 16) ^ m = 4 * (g ^ (m / 4)) + ((lane / 16) ^ (m % 4)).
+  const uint32_t abase = (uint32_t)((lane & 15) * kBVecs + (((lane >> 4) ^ lane) & 3));
+  const uint32_t am2 = (uint32_t)((lane & 15) >> 2);
+  auto aoff = [&](int g) { return abase + 4u * ((uint32_t)g ^ am2); };
+
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc0[S], acc1[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    acc0[s] = zero4;
+    acc1[s] = zero4;
+  }
+
+  // Issue order weights(0), rows(0), weights(1): after the wait only the
+  // newest weight chunk is in flight, as at the end of every chunk step.
+  __builtin_amdgcn_sched_barrier(0);
+  copy_rows(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  wb[1] = load_w(1);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(kBWLoads, 0));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto compute = [&](const WChunk& w, int slot) {
+    const uint32_t q0[4] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w};
+    const uint32_t q1[4] = {w.q1.x, w.q1.y, w.q1.z, w.q1.w};
+    f16x2_t s0lo, s0hi, s1lo, s1hi;
+    if constexpr (kFmt == kFmtInt4) {  // s' = s * 2^-sigma for the four groups
+      const f16x2_t m20 = __builtin_shufflevector(m2, m2, 0, 0), m21 = __builtin_shufflevector(m2, m2, 1, 1);
+      s0lo = as_f16x2(w.s0.x) * m20;
+      s0hi = as_f16x2(w.s0.y) * m20;
+      s1lo = as_f16x2(w.s1.x) * m21;
+      s1hi = as_f16x2(w.s1.y) * m21;
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if constexpr (kFmt == kFmtInt4) {
+        const f16x2_t t0 = g < 2 ? s0lo : s0hi, t1 = g < 2 ? s1lo : s1hi;
+        const f16x2_t g0 = (g & 1) ? __builtin_shufflevector(t0, t0, 1, 1) : __builtin_shufflevector(t0, t0, 0, 0);
+        const f16x2_t g1 = (g & 1) ? __builtin_shufflevector(t1, t1, 1, 1) : __builtin_shufflevector(t1, t1, 0, 0);
+        const f16x8_t b0 = dequant_int4_f16(q0[g], g0);
+        const f16x8_t b1 = dequant_int4_f16(q1[g], g1);
+        // one A fragment read ahead: sub-tile s + 1's rows load while sub-tile
+        // s's MFMAs are issued (more in flight would not fit the registers)
+        const uint4* ap = (slot ? xt1 : xt0) + aoff(g);
+        f16x8_t xv = __builtin_bit_cast(f16x8_t, ap[0]);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          f16x8_t xn = xv;
+          if (s + 1 < S) xn = __builtin_bit_cast(f16x8_t, ap[(s + 1) * kTileRows * kBVecs]);
+          acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b0, acc0[s], 0, 0, 0);
+          acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b1, acc1[s], 0, 0, 0);
+          xv = xn;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the next group's codes and rows are not hoisted above these MFMAs
+        // (their registers would not fit next to the accumulators)
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        const bf16x8_t b0 = dequant_group(q0[g], group_scale(w.s0, g));
+        const bf16x8_t b1 = dequant_group(q1[g], group_scale(w.s1, g));
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const bf16x8_t xv = as_bf16x8((slot ? xt1 : xt0)[s * kTileRows * kBVecs + aoff(g)]);
+          acc0[s] = mfma16x16x32(xv, b0, acc0[s]);
+          acc1[s] = mfma16x16x32(xv, b1, acc1[s]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // n is even (checked by the launcher): the slot of chunk c is c % 2 = j.
+  for (int c = 0; c < n; c += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int cc = c + j;
+      // The next chunk's rows into the other slot (every wave passed the
+      // last barrier after its reads of that slot completed). Past the last
+      // chunk the copy reads the next rows' data (or nothing) into a slot no
+      // one reads.
+      copy_rows(cc + 1, j ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wb[j], j);
+      __builtin_amdgcn_sched_barrier(0);
+      wb[j] = load_w(cc + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      // the rows of chunk cc + 1 and the weights of chunk cc + 1 have
+      // arrived; this step's weight loads may stay in flight. lgkmcnt(0):
+      // this wave's reads of slot j are done before anyone refills it.
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(kBWLoads, 0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // no copy into LDS may outlive the workgroup
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+
+  int frow[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) frow[s] = s < nsub ? rows[kTileRows * s + (lane & 15)] : MK;
+  big_epilogue<S, kFc1>(a, e, pair, frow, nsub, acc0, acc1, lane);
+}
+
+template <int S, bool kFc1>
+__device__ __forceinline__ void big_tile_policy(const FcArgs& a, const int e, const int pair, const int row0,
+                                                const int nsub, const bool reuse, uint4* xt0, uint4* xt1,
+                                                uint32_t* xoffs) {
+  if (reuse)
+    big_tile_body<S, kFc1, kPolicyDefault>(a, e, pair, row0, nsub, xt0, xt1, xoffs);
+  else
+    big_tile_body<S, kFc1, kPolicyWeights>(a, e, pair, row0, nsub, xt0, xt1, xoffs);
+}
+
+// Two waves per SIMD (one workgroup per CU, up to 256 VGPRs): the 8-sub-tile
+// body's 64 accumulators, the weight ring and the widened codes do not fit
+// the 128 VGPRs of four waves per SIMD.
+#ifndef MOE_BIG_TILE_WAVES_PER_EU
+#define MOE_BIG_TILE_WAVES_PER_EU 2
+#endif
+template <bool kFc1>
+__global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(MOE_BIG_TILE_WAVES_PER_EU)))
+void fc_tile128_kernel(FcArgs a) {
+  // the two slots of the tile's activation chunk, as separate objects: the
+  // compiler then knows that reads of one need not wait for copies into the
+  // other (with one array it drains every load before each chunk's reads)
+  __shared__ uint4 xt0[kBSlotVecs];
+  __shared__ uint4 xt1[kBSlotVecs];
+  __shared__ uint32_t xoffs[64 * kBW * (kBigTileRows / kTileRows / 2)];  // each thread's copy source offsets
+  constexpr int kThreads = 64 * kBW;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = kFc1 ? 2 * a.I : a.H;
+  const int npg = N / kPairRows / kBW;  // pair groups per tile
+
+  if constexpr (kFc1) {  // clear FC2's accumulator
+    uint4* z = reinterpret_cast<uint4*>(a.acc);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < a.zero_words16; i += stride)
+      z[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  // workgroups dealt to the XCDs: all pair groups of a tile on one XCD,
+  // consecutive tiles on different XCDs
+  const int xcd = blockIdx.x % kBXcds, gi = blockIdx.x / kBXcds;
+  const int tile = (gi / npg) * kBXcds + xcd;
+  const int pair = (gi % npg) * kBW + wave;
+  if (tile >= a.max_tiles) return;
+  const int2 te = a.tiles[tile];
+  const int ntiles = *a.ntiles;
+  asm volatile("" ::"s"(te.x), "s"(te.y), "s"(ntiles));
+  if (tile >= ntiles) return;
+  const int row0 = __builtin_amdgcn_readfirstlane(te.x);
+  const int meta = __builtin_amdgcn_readfirstlane(te.y);
+  const int nsub = meta & kTileNsubMask;
+  const bool reuse = (meta & kTileReuseBit) != 0;
+  const int e = meta >> kTileExpertShift;
+  if (e < 0 || e >= a.E || nsub < 1 || nsub > kBigTileRows / kTileRows) return;
+
+  if (nsub <= 2) big_tile_policy<2, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
+  else if (nsub <= 4) big_tile_policy<4, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
+  else if (nsub <= 6) big_tile_policy<6, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
+  else big_tile_policy<8, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
+}
+
+}  // namespace
+
+bool big_tile_supported(int64_t H, int64_t I) {
+  // whole pair groups and an even number of K chunks in both GEMMs
+  return (2 * I / kPairRows) % kBW == 0 && (H / kPairRows) % kBW == 0 && (H / kChunkK) % 2 == 0 &&
+         (I / kChunkK) % 2 == 0;
+}
+
+template <bool kFc1>
+hipError_t launch_fc_tile128(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  const int N = kFc1 ? 2 * a.I : a.H;
+  const int64_t grid = (int64_t)a.max_tiles * (N / kPairRows / kBW);
+  if (grid <= 0 || grid > 0x7FFFFFFF || a.max_tiles % kBXcds != 0) return hipErrorInvalidValue;
+  launch_kernel(fc_tile128_kernel<kFc1>, dim3((unsigned)grid), dim3(64 * kBW), 0, stream, e0, e1, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_fc_tile128<true>(const FcArgs&, hipStream_t, hipEvent_t, hipEvent_t);
+template hipError_t launch_fc_tile128<false>(const FcArgs&, hipStream_t, hipEvent_t, hipEvent_t);
+
+}  // namespace MOE_FMT_NS
+}  // namespace moe
+
+#if MOE_WEIGHT_FORMAT == 0
+// ---------------------------------------------------------------------------
+// Format-independent helpers of the scale-before path, built once (INT4 unit).
+namespace moe {
+namespace {
+
+constexpr int kRsWaves = 4;
+
+// One wave per row: the largest |value| (bf16 bit patterns of finite values
+// order as integers), e = floor(log2(max)) - 14, then every value times 2^-e
+// converted to fp16. Every bf16 significand fits fp16's, so a scaled value
+// of the normal fp16 range is exact; smaller ones (below 2^-28 of the row's
+// largest) are truncated to fp16's subnormal spacing.
+__global__ __launch_bounds__(64 * kRsWaves) void rowscale_kernel(const uint16_t* __restrict__ in, int64_t rows,
+                                                                 int K, uint16_t* __restrict__ out,
+                                                                 int32_t* __restrict__ exps) {
+  const int64_t row = (int64_t)blockIdx.x * kRsWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const uint4* src = reinterpret_cast<const uint4*>(in + row * K);
+  uint4* dst = reinterpret_cast<uint4*>(out + row * K);
+  const int nv = K / 8;
+  uint32_t mx = 0;
+  for (int i = lane; i < nv; i += 64) {
+    const uint4 v = src[i];
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = max(mx, max(d[j] & 0x7FFFu, (d[j] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+  int ex = 0;
+  if (mx != 0) {
+    const int be = (int)(mx >> 7);
+    // floor(log2) of the largest magnitude (a subnormal bf16 has exponent -133
+    // plus the position of its leading mantissa bit)
+    const int lg = be > 0 ? be - 127 : (31 - __builtin_clz(mx & 0x7Fu)) - 133;
+    ex = lg - 14;
+  }
+  if (lane == 0) exps[row] = ex;
+  for (int i = lane; i < nv; i += 64) {
+    const uint4 v = src[i];
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __builtin_ldexpf(__uint_as_float(d[j] << 16), -ex);
+      const float hi = __builtin_ldexpf(__uint_as_float(d[j] & 0xFFFF0000u), -ex);
+      o[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
+    dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// One thread per weight row: sigma = clamp(floor(log2(max_g |s|)) - 11, -15, 4).
+__global__ __launch_bounds__(256) void row_sigma_kernel(const uint16_t* __restrict__ s, int64_t nrows, int G,
+                                                        int8_t* __restrict__ sigma) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= nrows) return;
+  const uint16_t* p = s + r * G;
+  uint32_t mx = 0;
+  for (int g = 0; g < G; ++g) mx = max(mx, (uint32_t)(p[g] & 0x7FFFu));
+  int sg = 0;
+  if (mx != 0) {
+    const int be = (int)(mx >> 10);
+    const int lg = be > 0 ? be - 15 : (31 - __builtin_clz(mx)) - 24;  // fp16 subnormal: m * 2^-24
+    sg = min(max(lg - 11, -15), 4);
+  }
+  sigma[r] = (int8_t)sg;
+}
+
+}  // namespace
+
+hipError_t launch_rowscale(const uint16_t* in, int64_t rows, int64_t K, uint16_t* out, int32_t* exps,
+                           hipStream_t stream) {
+  const int64_t blocks = (rows + kRsWaves - 1) / kRsWaves;
+  if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  rowscale_kernel<<<(unsigned)blocks, 64 * kRsWaves, 0, stream>>>(in, rows, (int)K, out, exps);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_sigma(const uint16_t* scales_f16, int E, int N, int K, int8_t* sigma, hipStream_t stream) {
+  const int64_t rows = (int64_t)E * N;
+  const int64_t blocks = (rows + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  row_sigma_kernel<<<(unsigned)blocks, 256, 0, stream>>>(scales_f16, rows, K / kGroup, sigma);
+  return hipGetLastError();
+}
+
+}  // namespace moe
+#endif

@@ -48,6 +48,11 @@ constexpr int kPairChunkBytes = 2 * kTileBytes;
 __host__ __device__ constexpr int64_t packed_bytes_fmt(int fmt, int64_t N, int64_t K) {
   return (N / kPairRows) * (K / kChunkK) * 2 * (kTileNibbleBytes + tile_scale_bytes(fmt));
 }
+// INT4 blobs end with one int8 per weight row (E x N, canonical row order):
+// sigma = clamp(floor(log2(max_g |s[n, g]|)) - 11, -15, 4), 0 for a row of
+// zero scales. q * s * 2^-sigma is then a normal fp16 below 2^15 for every
+// finite scale (the rounded-weight kernels use it; the others ignore it).
+inline int64_t sigma_trailer_bytes(int fmt, int64_t E, int64_t N) { return fmt == kFmtInt4 ? E * N : 0; }
 static __host__ __device__ inline int64_t packed_bytes_per_expert(int64_t N, int64_t K) {
   return packed_bytes_fmt(kFmt, N, K);
 }
@@ -55,7 +60,8 @@ static __host__ __device__ inline int64_t packed_bytes_per_expert(int64_t N, int
 // Tiles of the tiled grouped GEMM (fc_tile.hip): up to 128 rows of one
 // expert, in 16-row sub-tiles. Table entry: (first row in the sorted list,
 // meta = sub-tiles | reuse flag | expert << 8). A sub-tile has kTileRows rows.
-constexpr int kTileMaxRows = 64;
+constexpr int kTileMaxRows = 64;   // exact-scaling tiled kernel (fc_tile.hip)
+constexpr int kBigTileRows = 128;  // scale-before tiled kernel (fc_tile128.hip)
 constexpr int kTileNsubMask = 15;
 constexpr int kTileReuseBit = 16;
 constexpr int kTileExpertShift = 8;
@@ -63,19 +69,39 @@ constexpr int kTileExpertShift = 8;
 // expert change and every 128 rows of the block_m-padded list).
 inline int64_t tile_table_entries(int64_t M, int64_t k) { return 2 * M * k + 16; }
 
+// The scale-before tiled kernel takes over once experts average this many
+// assignments (and the shape divides into its pair groups).
+#ifndef MOE_BIG_TILE_MIN_PER_EXPERT
+#define MOE_BIG_TILE_MIN_PER_EXPERT 16.0
+#endif
+inline bool big_tile_batch(int64_t M, int64_t E, int64_t k) {
+  return (double)M * (double)k / (double)E >= MOE_BIG_TILE_MIN_PER_EXPERT;
+}
+
 // Workspace layout of the forward:
 // [acc fp32 M x H][act bf16 M*k x I][tile count int32 (16 B)][tile table int2]
+// and, for batches the scale-before tiled kernel may take, the fp16 copies of
+// the A rows (x [M, H] for FC1, then act [M*k, I] for FC2, in the same
+// region) and their power-of-two row exponents.
 struct WorkspaceLayout {
-  int64_t acc_off, act_off, ntiles_off, tiles_off, total;
+  int64_t acc_off, act_off, ntiles_off, tiles_off, a16_off, a16exp_off, total;
 };
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
-inline WorkspaceLayout workspace_layout(int64_t M, int64_t H, int64_t I, int64_t k) {
+inline WorkspaceLayout workspace_layout(int64_t M, int64_t E, int64_t H, int64_t I, int64_t k) {
   WorkspaceLayout w;
   w.acc_off = 0;
   w.act_off = align256(M * H * 4);
   w.ntiles_off = w.act_off + align256(M * k * I * 2);
   w.tiles_off = w.ntiles_off + 256;
   w.total = w.tiles_off + align256(tile_table_entries(M, k) * 8);
+  w.a16_off = w.a16exp_off = 0;
+  if (big_tile_batch(M, E, k)) {
+    const int64_t a16_elems = M * H > M * k * I ? M * H : M * k * I;
+    const int64_t a16_rows = M * k;  // >= M
+    w.a16_off = w.total;
+    w.a16exp_off = w.a16_off + align256(a16_elems * 2);
+    w.total = w.a16exp_off + align256(a16_rows * 4);
+  }
   return w;
 }
 
@@ -104,10 +130,16 @@ struct FcArgs {
   int M, E, H, I, k, block_m;
   int64_t cap;
   int64_t zero_words16;         // FC1: 16-byte words of acc to clear
-  // tiled path only (tiles != nullptr): the tile table FC1's plan writes
+  // tiled paths only (tiles != nullptr): the tile table FC1's plan writes
   int2* tiles;                  // [max_tiles]
   int32_t* ntiles;              // [1]
   int max_tiles;                // grid tiles (a multiple of 8)
+  int tile_rows;                // kTileMaxRows (exact kernel) or kBigTileRows (scale-before kernel)
+  // scale-before kernel, INT4 weights only
+  uint16_t* a16;                // fp16 copies of the A rows (workspace)
+  int32_t* a16_exp;             // their row exponents
+  const int32_t* row_exp;       // the A rows' exponents as the kernel reads them
+  const int8_t* wsigma;         // per-weight-row shifts of the blob (E x N)
 };
 
 // Decode path (tiny batches): routing fused into FC1, output-stationary FC2.
@@ -187,7 +219,9 @@ inline bool token_fc2_fits(int64_t M, int64_t E, int64_t I, int64_t k) {
   hipError_t launch_fc1(const FcArgs& a, hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr); \
   hipError_t launch_fc2(const FcArgs& a, hipStream_t stream); \
   bool tile_path_supported(int64_t H, int64_t I); \
-  int64_t tile_grid_tiles(int64_t M, int64_t E, int64_t k, int64_t block_m, int64_t cap); \
+  int64_t tile_grid_tiles(int64_t M, int64_t E, int64_t k, int64_t block_m, int64_t cap, int64_t tile_rows); \
+  bool big_tile_supported(int64_t H, int64_t I); \
+  template <bool kFc1> hipError_t launch_fc_tile128(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1); \
   hipError_t launch_tile_plan(const FcArgs& a, hipStream_t stream); \
   template <bool kFc1> hipError_t launch_fc_tiled(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1); \
   hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop); \
@@ -201,6 +235,14 @@ MOE_FORMAT_LAUNCHERS
 namespace fmt_mxfp4 {
 MOE_FORMAT_LAUNCHERS
 }  // namespace fmt_mxfp4
+
+// fp16 copies of bf16 rows [rows, K], each scaled by 2^-e so that its
+// largest magnitude lies in [2^14, 2^15) (e = 0 for an all-zero row); e goes
+// to exps[row] (fc_tile128.hip, INT4 build).
+hipError_t launch_rowscale(const uint16_t* in, int64_t rows, int64_t K, uint16_t* out, int32_t* exps,
+                           hipStream_t stream);
+// One int8 per weight row (E x N) after the INT4 tiles: see sigma_trailer_bytes.
+hipError_t launch_row_sigma(const uint16_t* scales_f16, int E, int N, int K, int8_t* sigma, hipStream_t stream);
 
 // Launch with optional kernel-timestamp events.
 template <typename... KArgs, typename... Args>

@@ -13,6 +13,8 @@
 // MXFP4 (FP4 e2m1 codes, E8M0 scales): the same tiles with the codes in
 // canonical byte order (gfx950's FP4 conversion takes a byte's low nibble
 // first) and 64 bytes of scales, row r's 4 bytes at offset 4*r.
+// An INT4 blob ends with one int8 exponent shift per weight row (internal.h,
+// sigma_trailer_bytes), written here from the scales.
 #include "internal.h"
 
 namespace moe {
@@ -134,7 +136,11 @@ hipError_t launch_repack(int fmt, const uint8_t* q, const void* s, int E, int N,
   const int64_t blocks = grid_for(E, N, K);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   repack_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(fmt, q, s, E, N, K, kind, packed);
-  return hipGetLastError();
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || fmt != kFmtInt4) return err;
+  // the per-row exponent shifts after the tiles (sigma_trailer_bytes)
+  return launch_row_sigma(static_cast<const uint16_t*>(s), E, N, K,
+                          reinterpret_cast<int8_t*>(packed + (int64_t)E * packed_bytes_fmt(fmt, N, K)), stream);
 }
 
 hipError_t launch_unpack(int fmt, const uint8_t* packed, int E, int N, int K, int kind, uint8_t* q, void* s,

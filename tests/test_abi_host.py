@@ -30,11 +30,11 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) >= 12
     for name in names:
         assert hasattr(lib, name), name
-    assert moe.moe_w4a16_abi_version() == 2
+    assert moe.moe_w4a16_abi_version() == 3
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert moe.status_string(code) and moe.status_string(code) != "unknown status"
     assert moe.status_string(42) == "unknown status"
 
@@ -54,10 +54,11 @@ def test_capacity_rejects():
 
 
 def test_packed_bytes():
-    assert moe.moe_w4a16_packed_bytes(384, 4096, 7168) == 384 * 4096 * 7168 * 9 // 16
-    assert moe.moe_w4a16_packed_bytes(384, 7168, 2048) == 384 * 7168 * 2048 * 9 // 16
+    # nibbles + fp16 scales (9/16 byte per weight), then one int8 exponent shift per weight row
+    assert moe.moe_w4a16_packed_bytes(384, 4096, 7168) == 384 * 4096 * 7168 * 9 // 16 + 384 * 4096
+    assert moe.moe_w4a16_packed_bytes(384, 7168, 2048) == 384 * 7168 * 2048 * 9 // 16 + 384 * 7168
     total = moe.moe_w4a16_packed_bytes(384, 4096, 7168) + moe.moe_w4a16_packed_bytes(384, 7168, 2048)
-    assert total == 9_512_681_472  # nibbles + fp16 scales of the 384-expert layer
+    assert total == 9_512_681_472 + 384 * (4096 + 7168)  # the 384-expert layer
     assert moe.moe_w4a16_packed_bytes(1, 48, 128) == -1     # N not a multiple of 32
     assert moe.moe_w4a16_packed_bytes(1, 32, 96) == -1      # K not a multiple of 128
     assert moe.moe_w4a16_packed_bytes(1, 32, 128, 64) == -1  # only group 32
@@ -76,9 +77,15 @@ def test_mxfp4_packed_bytes():
 def test_workspace_bytes():
     def a256(v):
         return (v + 255) // 256 * 256
-    M, E, H, I, k = 1024, 384, 7168, 2048, 8
+    M, E, H, I, k = 512, 384, 7168, 2048, 8
     # fp32 accumulator, bf16 activations, tile count, tile table (2*M*k + 16 entries of 8 bytes)
     want = a256(M * H * 4) + a256(M * k * I * 2) + 256 + a256((2 * M * k + 16) * 8)
+    assert moe.moe_w4a16_workspace_bytes(M, E, H, I, k) == want
+    # from 16 assignments per expert on (M*k >= 16*E): also the fp16 copies of the
+    # A rows (x, then the activations, in one region) and their row exponents
+    M = 1024
+    want = (a256(M * H * 4) + a256(M * k * I * 2) + 256 + a256((2 * M * k + 16) * 8)
+            + a256(max(M * H, M * k * I) * 2) + a256(M * k * 4))
     assert moe.moe_w4a16_workspace_bytes(M, E, H, I, k) == want
     assert moe.moe_w4a16_workspace_bytes(1, E, 7000, I, k) == -1
 

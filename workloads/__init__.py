@@ -82,7 +82,9 @@ WORKLOADS = {
     "k26_m90": Workload("k26_m90", K26, 90, 2026, 90, note="tree verify, 10 streams x q_len 9"),
     "k26_m256": Workload("k26_m256", K26, 256, 2026, 256, note="all experts touched on average"),
     "k26_m512": Workload("k26_m512", K26, 512, 2026, 512, note="plateau sample point"),
+    "k26_m768": Workload("k26_m768", K26, 768, 2026, 768, note="multi-stream chunk (16 assignments per expert)"),
     "k26_m1024": Workload("k26_m1024", K26, 1024, 2026, 1024, note="dense multi-stream chunk"),
+    "k26_m1536": Workload("k26_m1536", K26, 1536, 2026, 1536, note="multi-stream chunk (32 assignments per expert)"),
     "k26_m1024_skew": Workload("k26_m1024_skew", K26, 1024, 2026, 2048, bias_sigma=2.0,
                                note="router logits + per-expert bias N(0, 2)"),
     # prefill chunks: past M ~ 4200 tokens the layer's arithmetic intensity
