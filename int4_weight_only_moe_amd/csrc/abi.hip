@@ -159,8 +159,12 @@ int32_t moe_w4a16_preferred_block_m(int32_t M, int32_t E, int32_t H, int32_t I, 
   // beat 16-row blocks from M = 9 up, and 64-row blocks only pay off once an
   // expert averages more than ~24 rows. Batches of a few assignments keep
   // 16-row blocks: the wide kernel would launch too few workgroups.
+  // From MOE_PRESCALED_MIN_PER_EXPERT on the pre-scaled tiled kernel runs,
+  // whose INT4 tiles are 96 rows with 16- or 32-row blocks (64 with 64-row
+  // blocks).
   const double per_expert = (double)M * top_k / E;
   if ((int64_t)M * top_k <= 32) return 16;
+  if (moe::prescaled_batch(M, E, top_k) && moe::fmt_int4::prescaled_supported(H, I)) return 32;
   if (per_expert <= 24.0) return 32;
   return 64;
 }
@@ -176,22 +180,11 @@ static int check_fc(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, i
   return MOE_OK;
 }
 
-// The tiled grouped GEMMs take over from the block kernels once experts
-// average this many assignments: the scale-before kernel (128-row tiles,
-// fc_tile128.hip) where the shape divides into its pair groups, else the
-// exact-scaling one (64-row tiles, fc_tile.hip).
-#ifndef MOE_TILED_MIN_PER_EXPERT
-#define MOE_TILED_MIN_PER_EXPERT 16.0
-#endif
-enum TiledKind { kNotTiled = 0, kTiledExact = 1, kTiledBig = 2 };
-static TiledKind tiled_kind(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
-  if (moe::big_tile_batch(M, E, top_k) && FMT_CALL(fmt, big_tile_supported, H, I)) return kTiledBig;
-  if (FMT_CALL(fmt, tile_path_supported, H, I) && (double)M * top_k / E >= MOE_TILED_MIN_PER_EXPERT)
-    return kTiledExact;
-  return kNotTiled;
-}
+// The pre-scaled tiled grouped GEMM (fc_prescaled.hip) takes the batch from
+// MOE_PRESCALED_MIN_PER_EXPERT assignments per expert on, where the shape
+// divides into its pair groups; the block kernels of fc.hip take the rest.
 static bool use_tiled(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
-  return tiled_kind(fmt, M, E, H, I, top_k) != kNotTiled;
+  return moe::prescaled_batch(M, E, top_k) && FMT_CALL(fmt, prescaled_supported, H, I);
 }
 
 // The weights a stage reads: the blob and, for INT4, its per-row shifts.
@@ -216,20 +209,18 @@ static moe::FcArgs fc_args(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, 
   a.M = M; a.E = E; a.H = H; a.I = I; a.k = top_k; a.block_m = block_m;
   a.cap = cap;
   a.zero_words16 = (int64_t)M * H * 4 / 16;
-  const TiledKind tk = tiled_kind(fmt, M, E, H, I, top_k);
-  if (tk != kNotTiled) {
+  if (use_tiled(fmt, M, E, H, I, top_k)) {
     a.tiles = (int2*)(ws + L.tiles_off);
     a.ntiles = (int32_t*)(ws + L.ntiles_off);
-    a.tile_rows = tk == kTiledBig ? moe::kBigTileRows : moe::kTileMaxRows;
+    a.tile_rows = moe::prescaled_tile_rows(fmt, block_m);
     // The grid is sized from the padded total this batch can reach, not from
     // the caller's cap (route buffers may be allocated for a larger batch):
     // the tile table in the workspace holds tile_table_entries(M, k) entries.
     a.max_tiles =
         (int)FMT_CALL(fmt, tile_grid_tiles, M, E, top_k, block_m, capacity(M, E, top_k, block_m), a.tile_rows);
-    if (tk == kTiledBig) {  // the workspace has the fp16 row copies (big_tile_batch)
-      a.a16 = (uint16_t*)(ws + L.a16_off);
-      a.a16_exp = (int32_t*)(ws + L.a16exp_off);
-    }
+    // the workspace has the fp16 row copies (prescaled_batch)
+    a.a16 = (uint16_t*)(ws + L.a16_off);
+    a.a16_exp = (int32_t*)(ws + L.a16exp_off);
   }
   return a;
 }

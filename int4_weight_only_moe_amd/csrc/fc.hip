@@ -576,20 +576,16 @@ hipError_t launch_fc(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEven
   if (a.tiles) {  // tiled path: FC1 first writes the tile table FC2 reuses
     hipError_t err = hipSuccess;
     if constexpr (kFc1) err = launch_tile_plan(a, stream);
-    if (a.tile_rows == kBigTileRows) {
-      // scale-before kernel; INT4 reads fp16 copies of its A rows (x for FC1,
-      // the activations for FC2), each row scaled by a power of two
-      FcArgs b = a;
-      if constexpr (kFmt == kFmtInt4) {
-        if (err == hipSuccess)
-          err = launch_rowscale(a.act_in, kFc1 ? a.M : (int64_t)a.M * a.k, kFc1 ? a.H : a.I, a.a16, a.a16_exp, stream);
-        b.act_in = a.a16;
-        b.row_exp = a.a16_exp;
-      }
-      if (err == hipSuccess) err = launch_fc_tile128<kFc1>(b, stream, e0, e1);
-    } else if (err == hipSuccess) {
-      err = launch_fc_tiled<kFc1>(a, stream, e0, e1);
+    // INT4 reads fp16 copies of its A rows (x for FC1, the activations for
+    // FC2), each row scaled by a power of two
+    FcArgs b = a;
+    if constexpr (kFmt == kFmtInt4) {
+      if (err == hipSuccess)
+        err = launch_rowscale(a.act_in, kFc1 ? a.M : (int64_t)a.M * a.k, kFc1 ? a.H : a.I, a.a16, a.a16_exp, stream);
+      b.act_in = a.a16;
+      b.row_exp = a.a16_exp;
     }
+    if (err == hipSuccess) err = launch_fc_prescaled<kFc1>(b, stream, e0, e1);
     if (err != hipSuccess || kFc1) return err;
     const int64_t n8 = (int64_t)a.M * a.H / 8;
     finalize_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, stream>>>(a.acc, a.out, n8);

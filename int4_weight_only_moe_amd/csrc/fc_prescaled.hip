@@ -1,15 +1,15 @@
 // Grouped GEMM (FC1 and FC2) with the group scales applied before the
-// product, on tiles of up to 128 rows: the large-batch regime.
+// product, on tiles of up to 96 or 128 rows: the large-batch regime.
 //
 // "The Throughput Lever: Quantifying the MoE GEMM and Mapping the Road to
 // B300", section "The Result: Two Regimes": once every expert holds tens to
 // hundreds of rows, the grouped GEMM is matrix work rather than a stream of
-// weights. On gfx950 the exact tiled kernel (fc_tile.hip) then runs out of
-// vector issue slots: it applies each group's scale to the fp32 MFMA result
-// (one FMA per output and group, plus a correction MFMA per group). Here the
-// weights enter the matrix core already scaled, so every MFMA accumulates
-// straight into its output and the vector work per weight is shared by all
-// rows of the tile:
+// weights. On gfx950 a kernel that applies each group's scale to the fp32
+// MFMA result (one FMA per output and group, plus a correction MFMA per
+// group), as the block kernels of fc.hip do, then runs out of vector issue
+// slots. Here the weights enter the matrix core already scaled, so every
+// MFMA accumulates straight into its output and the vector work per weight
+// is shared by all rows of the tile:
 //   * INT4: B = fp16(q * s'), one rounding of the exact product, where
 //     s' = s * 2^-sigma and sigma is the per-weight-row exponent shift the
 //     repack stores after the tiles (it keeps q * s' a normal fp16 below 2^15
@@ -21,16 +21,26 @@
 //   * MXFP4: the exact bf16 values code * 2^(s - 127) with the bf16 MFMA, A
 //     the bf16 activations themselves.
 // Work decomposition:
-//   * tiles of up to 128 rows of one expert (the plan kernel of fc_tile.hip
-//     with 128-row tiles): one tile pair per wave, 8 waves per workgroup,
-//     one workgroup per CU (two waves per SIMD, up to 256 VGPRs; 72 KB of LDS);
-//   * the tile's activation chunk (128 rows x 128 channels) is copied from
-//     memory straight into LDS by gfx950's buffer loads to LDS (no staging
-//     registers or stores), double-buffered; a row's sixteen 16-byte vectors
-//     are stored XOR-swizzled with the row index, so the A reads of a wave
-//     (16 rows, one vector each) hit 16 different bank groups;
+//   * a plan kernel cuts each expert's row range (block_m-padded, from
+//     moe_route_align) into tiles: a tile starts at every expert change and
+//     at every tile_rows boundary of the padded list, so an expert holding
+//     hundreds of rows gets several tiles; a tile counts only the 16-row
+//     sub-tiles that hold a row (padding is not multiplied), and carries a
+//     reuse flag when its expert has other tiles (then the weights are read
+//     with the default cache policy, else non-temporally);
+//   * tiles of up to 96 rows of one expert for INT4 (64 with 64-row blocks),
+//     128 for MXFP4: one tile pair per
+//     wave, 8 waves per workgroup, two workgroups per CU (four waves per
+//     SIMD, <= 128 VGPRs, 54 or 72 KB of LDS each): while one workgroup waits
+//     at a barrier or runs its epilogue, the other keeps the matrix core busy
+//     (INT4's widened fp16 codes leave registers for 6 sub-tiles, MXFP4's for 8);
+//   * the tile's activation chunk (up to 128 rows x 128 channels) is copied
+//     from memory straight into LDS by gfx950's buffer loads to LDS (no
+//     staging registers or stores), double-buffered; a row's sixteen 16-byte
+//     vectors are stored XOR-swizzled with the row index, so the A reads of a
+//     wave (16 rows, one vector each) hit 16 different bank groups;
 //   * per 32-channel group a wave widens both tiles' codes once and runs
-//     2 x S MFMAs (S = sub-tiles of 16 rows: 2, 4, 6 or 8);
+//     2 x S MFMAs (S = sub-tiles of 16 rows: 2, 4, 6, or 8 for MXFP4);
 //   * per chunk step: the next chunk's rows go to LDS, the current chunk is
 //     computed, the weight chunk after next is loaded, then one wait (the
 //     rows and the next weight chunk; the newest weight loads stay in flight)
@@ -48,7 +58,8 @@ namespace {
 
 constexpr int kBW = 8;                       // waves (= tile pairs) per workgroup
 constexpr int kBVecs = kChunkK / 8;          // 16-byte vectors of a row's chunk slice
-constexpr int kBSlotVecs = kBigTileRows * kBVecs;  // one LDS slot: 128 rows x 16 vectors = 32 KB
+constexpr int kBMaxRows = prescaled_max_rows(kFmt);   // 96 (INT4) or 128 (MXFP4)
+constexpr int kBSlotVecs = kBMaxRows * kBVecs;         // one LDS slot: up to 128 rows x 16 vectors
 constexpr int kBXcds = 8;
 constexpr int kBWLoads = 4;                  // vector loads per weight chunk (2 tiles' codes + scales)
 
@@ -83,6 +94,56 @@ __device__ __forceinline__ f16x8_t dequant_int4_f16(uint32_t w, f16x2_t s2) {
                                  __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// ---------------------------------------------------------------------------
+// Plan: one workgroup turns the block list into the tile list.
+// tile_rows: 64, 96 or 128 (whole blocks).
+__global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restrict__ block_expert,
+                                                        const int32_t* __restrict__ sorted_ids,
+                                                        const int32_t* __restrict__ npp_p, int block_m, int MK,
+                                                        int tile_rows, int max_tiles, int2* __restrict__ tiles,
+                                                        int32_t* __restrict__ ntiles_out) {
+  __shared__ int wave_cnt[16];
+  __shared__ int base;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bpt = tile_rows / block_m;  // blocks per full tile
+  const int nblk = *npp_p / block_m;
+  if (tid == 0) base = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < nblk; b0 += 1024) {
+    const int b = b0 + tid;
+    int e = -1;
+    bool head = false;
+    if (b < nblk) {
+      e = block_expert[b];
+      head = (b % bpt == 0) || block_expert[b - 1] != e;  // b % bpt != 0 implies b >= 1
+    }
+    const unsigned long long m = __ballot(head);
+    if (lane == 0) wave_cnt[wave] = __popcll(m);
+    __syncthreads();
+    int t = base + __popcll(m & ((1ull << lane) - 1ull));
+    for (int w = 0; w < wave; ++w) t += wave_cnt[w];
+    if (head && t < max_tiles) {
+      // the tile runs to the next full-tile boundary or the end of the expert
+      int nb = 1;
+      while (nb < bpt - b % bpt && b + nb < nblk && block_expert[b + nb] == e) ++nb;
+      // sub-tiles that hold a row: an expert's padding sits at the end of its
+      // range, so they are a prefix of the tile's
+      int nsub = nb * block_m / kTileRows;
+      while (nsub > 1 && sorted_ids[b * block_m + (nsub - 1) * kTileRows] >= MK) --nsub;
+      const bool reuse = (b > 0 && block_expert[b - 1] == e) || (b + nb < nblk && block_expert[b + nb] == e);
+      tiles[t] = make_int2(b * block_m, nsub | (reuse ? kTileReuseBit : 0) | (e << kTileExpertShift));
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int w = 0; w < 16; ++w) tot += wave_cnt[w];
+      base += tot;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) *ntiles_out = base < max_tiles ? base : max_tiles;
+}
+
 // (2^-sigma0, 2^-sigma1) for two rows' shifts (|sigma| <= 15: normal fp16 values).
 __device__ __forceinline__ f16x2_t pow2_pair(int sigma0, int sigma1) {
   return f16x2_t{(_Float16)__builtin_ldexpf(1.0f, -sigma0), (_Float16)__builtin_ldexpf(1.0f, -sigma1)};
@@ -106,7 +167,7 @@ __device__ __forceinline__ uint32_t a_row(int f, int k) { return (uint32_t)(kFc1
 // Epilogue of the tile pair for rows frow (per sub-tile, the row of lane % 16):
 // INT4 scales each output by 2^(row exponent + sigma of its weight row).
 template <int S, bool kFc1>
-__device__ __forceinline__ void big_epilogue(const FcArgs& a, const int e, const int pair, const int (&frow)[S],
+__device__ __forceinline__ void prescaled_epilogue(const FcArgs& a, const int e, const int pair, const int (&frow)[S],
                                              const int nsub, const f32x4_t (&acc0)[S], const f32x4_t (&acc1)[S],
                                              const int lane) {
   const int MK = a.M * a.k;
@@ -145,9 +206,9 @@ __device__ __forceinline__ void big_epilogue(const FcArgs& a, const int e, const
 // wave copies S / 2 KB of every chunk to LDS), weights under cache policy
 // kPolicy.
 template <int S, bool kFc1, int kPolicy>
-__device__ __forceinline__ void big_tile_body(const FcArgs& a, const int e, const int pair, const int row0,
+__device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, const int pair, const int row0,
                                               const int nsub, uint4* xt0, uint4* xt1, uint32_t* xoffs) {
-  static_assert(S % 2 == 0 && S * kTileRows <= kBigTileRows, "S even, at most 8 sub-tiles");
+  static_assert(S % 2 == 0 && S * kTileRows <= kBMaxRows, "S even, at most the tile's sub-tiles");
   constexpr int kD = S / 2;  // 1 KB copies per wave per chunk
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -193,7 +254,7 @@ __device__ __forceinline__ void big_tile_body(const FcArgs& a, const int e, cons
   const uint32_t rid0 = a_row<kFc1>(rows[0], a.k);
   // The per-lane source offsets are kept in LDS (this thread's kD words),
   // not in registers: they are needed only while the copies are issued.
-  uint32_t* myoff = xoffs + tid * (kBigTileRows / kTileRows / 2);
+  uint32_t* myoff = xoffs + tid * (kBMaxRows / kTileRows / 2);
 #pragma unroll
   for (int i = 0; i < kD; ++i) {
     const int r = 4 * (wave + kBW * i) + (lane >> 4);
@@ -316,34 +377,28 @@ __device__ __forceinline__ void big_tile_body(const FcArgs& a, const int e, cons
   int frow[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) frow[s] = s < nsub ? rows[kTileRows * s + (lane & 15)] : MK;
-  big_epilogue<S, kFc1>(a, e, pair, frow, nsub, acc0, acc1, lane);
+  prescaled_epilogue<S, kFc1>(a, e, pair, frow, nsub, acc0, acc1, lane);
 }
 
 template <int S, bool kFc1>
-__device__ __forceinline__ void big_tile_policy(const FcArgs& a, const int e, const int pair, const int row0,
+__device__ __forceinline__ void prescaled_policy(const FcArgs& a, const int e, const int pair, const int row0,
                                                 const int nsub, const bool reuse, uint4* xt0, uint4* xt1,
                                                 uint32_t* xoffs) {
   if (reuse)
-    big_tile_body<S, kFc1, kPolicyDefault>(a, e, pair, row0, nsub, xt0, xt1, xoffs);
+    prescaled_body<S, kFc1, kPolicyDefault>(a, e, pair, row0, nsub, xt0, xt1, xoffs);
   else
-    big_tile_body<S, kFc1, kPolicyWeights>(a, e, pair, row0, nsub, xt0, xt1, xoffs);
+    prescaled_body<S, kFc1, kPolicyWeights>(a, e, pair, row0, nsub, xt0, xt1, xoffs);
 }
 
-// Two waves per SIMD (one workgroup per CU, up to 256 VGPRs): the 8-sub-tile
-// body's 64 accumulators, the weight ring and the widened codes do not fit
-// the 128 VGPRs of four waves per SIMD.
-#ifndef MOE_BIG_TILE_WAVES_PER_EU
-#define MOE_BIG_TILE_WAVES_PER_EU 2
-#endif
 template <bool kFc1>
-__global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(MOE_BIG_TILE_WAVES_PER_EU)))
-void fc_tile128_kernel(FcArgs a) {
+__global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(4)))
+void fc_prescaled_kernel(FcArgs a) {
   // the two slots of the tile's activation chunk, as separate objects: the
   // compiler then knows that reads of one need not wait for copies into the
   // other (with one array it drains every load before each chunk's reads)
   __shared__ uint4 xt0[kBSlotVecs];
   __shared__ uint4 xt1[kBSlotVecs];
-  __shared__ uint32_t xoffs[64 * kBW * (kBigTileRows / kTileRows / 2)];  // each thread's copy source offsets
+  __shared__ uint32_t xoffs[64 * kBW * (kBMaxRows / kTileRows / 2)];  // each thread's copy source offsets
   constexpr int kThreads = 64 * kBW;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -372,33 +427,47 @@ void fc_tile128_kernel(FcArgs a) {
   const int nsub = meta & kTileNsubMask;
   const bool reuse = (meta & kTileReuseBit) != 0;
   const int e = meta >> kTileExpertShift;
-  if (e < 0 || e >= a.E || nsub < 1 || nsub > kBigTileRows / kTileRows) return;
+  if (e < 0 || e >= a.E || nsub < 1 || nsub > a.tile_rows / kTileRows) return;
 
-  if (nsub <= 2) big_tile_policy<2, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
-  else if (nsub <= 4) big_tile_policy<4, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
-  else if (nsub <= 6) big_tile_policy<6, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
-  else big_tile_policy<8, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
+  if (nsub <= 2) prescaled_policy<2, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
+  else if (nsub <= 4) prescaled_policy<4, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
+  else if (kBMaxRows <= 96 || nsub <= 6) prescaled_policy<6, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
+  else if constexpr (kBMaxRows >= 128) prescaled_policy<8, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
 }
 
 }  // namespace
 
-bool big_tile_supported(int64_t H, int64_t I) {
+int64_t tile_grid_tiles(int64_t M, int64_t E, int64_t k, int64_t block_m, int64_t cap, int64_t tile_rows) {
+  const int64_t bpt = tile_rows / block_m;
+  const int64_t nblk = cap / block_m;
+  const int64_t mk = M * k;
+  const int64_t t = (nblk + bpt - 1) / bpt + (mk < E ? mk : E);
+  return (t + kBXcds - 1) / kBXcds * kBXcds;
+}
+
+hipError_t launch_tile_plan(const FcArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, stream, a.block_expert, a.sorted_ids, a.npp,
+                     a.block_m, a.M * a.k, a.tile_rows, a.max_tiles, a.tiles, a.ntiles);
+  return hipGetLastError();
+}
+
+bool prescaled_supported(int64_t H, int64_t I) {
   // whole pair groups and an even number of K chunks in both GEMMs
   return (2 * I / kPairRows) % kBW == 0 && (H / kPairRows) % kBW == 0 && (H / kChunkK) % 2 == 0 &&
          (I / kChunkK) % 2 == 0;
 }
 
 template <bool kFc1>
-hipError_t launch_fc_tile128(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+hipError_t launch_fc_prescaled(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int N = kFc1 ? 2 * a.I : a.H;
   const int64_t grid = (int64_t)a.max_tiles * (N / kPairRows / kBW);
   if (grid <= 0 || grid > 0x7FFFFFFF || a.max_tiles % kBXcds != 0) return hipErrorInvalidValue;
-  launch_kernel(fc_tile128_kernel<kFc1>, dim3((unsigned)grid), dim3(64 * kBW), 0, stream, e0, e1, a);
+  launch_kernel(fc_prescaled_kernel<kFc1>, dim3((unsigned)grid), dim3(64 * kBW), 0, stream, e0, e1, a);
   return hipGetLastError();
 }
 
-template hipError_t launch_fc_tile128<true>(const FcArgs&, hipStream_t, hipEvent_t, hipEvent_t);
-template hipError_t launch_fc_tile128<false>(const FcArgs&, hipStream_t, hipEvent_t, hipEvent_t);
+template hipError_t launch_fc_prescaled<true>(const FcArgs&, hipStream_t, hipEvent_t, hipEvent_t);
+template hipError_t launch_fc_prescaled<false>(const FcArgs&, hipStream_t, hipEvent_t, hipEvent_t);
 
 }  // namespace MOE_FMT_NS
 }  // namespace moe

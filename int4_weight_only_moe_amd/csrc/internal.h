@@ -11,7 +11,7 @@ namespace moe {
 // Weight formats. kFmtInt4: INT4 codes (offset binary, q = u - 8), one fp16
 // scale per 32 channels. kFmtMxfp4: FP4 e2m1 codes, one E8M0 scale
 // (2^(s - 127)) per 32 channels. The grouped-GEMM sources (fc.hip,
-// fc_tile.hip, decode.hip) are compiled once per format: MOE_WEIGHT_FORMAT
+// fc_prescaled.hip, decode.hip) are compiled once per format: MOE_WEIGHT_FORMAT
 // selects it (the *_mxfp4.hip wrappers set 1), and their format-dependent
 // code lives in the namespace MOE_FMT_NS.
 constexpr int kFmtInt4 = 0;
@@ -57,30 +57,41 @@ static __host__ __device__ inline int64_t packed_bytes_per_expert(int64_t N, int
   return packed_bytes_fmt(kFmt, N, K);
 }
 
-// Tiles of the tiled grouped GEMM (fc_tile.hip): up to 128 rows of one
+// Tiles of the tiled grouped GEMM (fc_prescaled.hip): up to 128 rows of one
 // expert, in 16-row sub-tiles. Table entry: (first row in the sorted list,
 // meta = sub-tiles | reuse flag | expert << 8). A sub-tile has kTileRows rows.
-constexpr int kTileMaxRows = 64;   // exact-scaling tiled kernel (fc_tile.hip)
-constexpr int kBigTileRows = 128;  // scale-before tiled kernel (fc_tile128.hip)
+// Largest tile of the pre-scaled tiled kernel (fc_prescaled.hip): 96 rows
+// for INT4 (the widened fp16 codes take the registers of two more
+// sub-tiles), 128 for MXFP4.
+__host__ __device__ constexpr int prescaled_max_rows(int fmt) { return fmt == kFmtMxfp4 ? 128 : 96; }
+// Tile rows of the pre-scaled kernel for a block size: whole blocks per tile.
+inline int prescaled_tile_rows(int fmt, int block_m) {
+  const int r = prescaled_max_rows(fmt);
+  return r % block_m == 0 ? r : block_m;
+}
 constexpr int kTileNsubMask = 15;
 constexpr int kTileReuseBit = 16;
 constexpr int kTileExpertShift = 8;
-// Upper bound of the tile count for any block_m (a tile starts at every
-// expert change and every 128 rows of the block_m-padded list).
+// Upper bound of the tile count for any block_m and tile size of at least 64
+// rows (a tile starts at every expert change and every tile_rows rows of the
+// block_m-padded list).
 inline int64_t tile_table_entries(int64_t M, int64_t k) { return 2 * M * k + 16; }
 
-// The scale-before tiled kernel takes over once experts average this many
-// assignments (and the shape divides into its pair groups).
-#ifndef MOE_BIG_TILE_MIN_PER_EXPERT
-#define MOE_BIG_TILE_MIN_PER_EXPERT 16.0
+// The pre-scaled tiled kernel takes over from the block kernels once experts
+// average this many assignments (and the shape divides into its pair
+// groups). Measured on the 384-expert layer: at 16 (M = 768) it beats the
+// wide block kernel by 2 %, at 21 (M = 1024) by 7 % with uniform routing
+// and by 27 % with the skewed batch.
+#ifndef MOE_PRESCALED_MIN_PER_EXPERT
+#define MOE_PRESCALED_MIN_PER_EXPERT 16.0
 #endif
-inline bool big_tile_batch(int64_t M, int64_t E, int64_t k) {
-  return (double)M * (double)k / (double)E >= MOE_BIG_TILE_MIN_PER_EXPERT;
+inline bool prescaled_batch(int64_t M, int64_t E, int64_t k) {
+  return (double)M * (double)k / (double)E >= MOE_PRESCALED_MIN_PER_EXPERT;
 }
 
 // Workspace layout of the forward:
 // [acc fp32 M x H][act bf16 M*k x I][tile count int32 (16 B)][tile table int2]
-// and, for batches the scale-before tiled kernel may take, the fp16 copies of
+// and, for batches the pre-scaled tiled kernel may take, the fp16 copies of
 // the A rows (x [M, H] for FC1, then act [M*k, I] for FC2, in the same
 // region) and their power-of-two row exponents.
 struct WorkspaceLayout {
@@ -95,7 +106,7 @@ inline WorkspaceLayout workspace_layout(int64_t M, int64_t E, int64_t H, int64_t
   w.tiles_off = w.ntiles_off + 256;
   w.total = w.tiles_off + align256(tile_table_entries(M, k) * 8);
   w.a16_off = w.a16exp_off = 0;
-  if (big_tile_batch(M, E, k)) {
+  if (prescaled_batch(M, E, k)) {
     const int64_t a16_elems = M * H > M * k * I ? M * H : M * k * I;
     const int64_t a16_rows = M * k;  // >= M
     w.a16_off = w.total;
@@ -134,8 +145,8 @@ struct FcArgs {
   int2* tiles;                  // [max_tiles]
   int32_t* ntiles;              // [1]
   int max_tiles;                // grid tiles (a multiple of 8)
-  int tile_rows;                // kTileMaxRows (exact kernel) or kBigTileRows (scale-before kernel)
-  // scale-before kernel, INT4 weights only
+  int tile_rows;                // rows per tile (whole blocks)
+  // INT4 weights only
   uint16_t* a16;                // fp16 copies of the A rows (workspace)
   int32_t* a16_exp;             // their row exponents
   const int32_t* row_exp;       // the A rows' exponents as the kernel reads them
@@ -192,13 +203,13 @@ inline bool token_fc2_fits(int64_t M, int64_t E, int64_t I, int64_t k) {
 
 // Launchers of the format-dependent kernels, declared for both formats
 // (namespaces fmt_int4 and fmt_mxfp4); each is defined by that format's
-// build of fc.hip, fc_tile.hip or decode.hip.
+// build of fc.hip, fc_prescaled.hip or decode.hip.
 //   launch_fc1 / launch_fc2   grouped GEMM stages; ev_start / ev_stop (may be
 //                             null) take FC1's own start and end timestamps
 //                             (hipExtLaunchKernel), for timing the stage
 //                             without extra packets
-//   tile_path_supported, tile_grid_tiles, launch_tile_plan, launch_fc_tiled
-//                             the tiled grouped GEMM (fc_tile.hip)
+//   tile_grid_tiles, launch_tile_plan, prescaled_supported, launch_fc_prescaled
+//                             the pre-scaled tiled grouped GEMM (fc_prescaled.hip)
 //   launch_decode             routing fused into FC1 + output-stationary FC2
 //                             for tiny batches; events as for launch_fc1
 //   launch_fc2_tokens         FC2 + combine per token (output-stationary, no
@@ -218,12 +229,10 @@ inline bool token_fc2_fits(int64_t M, int64_t E, int64_t I, int64_t k) {
 #define MOE_FORMAT_LAUNCHERS \
   hipError_t launch_fc1(const FcArgs& a, hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr); \
   hipError_t launch_fc2(const FcArgs& a, hipStream_t stream); \
-  bool tile_path_supported(int64_t H, int64_t I); \
   int64_t tile_grid_tiles(int64_t M, int64_t E, int64_t k, int64_t block_m, int64_t cap, int64_t tile_rows); \
-  bool big_tile_supported(int64_t H, int64_t I); \
-  template <bool kFc1> hipError_t launch_fc_tile128(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1); \
+  bool prescaled_supported(int64_t H, int64_t I); \
+  template <bool kFc1> hipError_t launch_fc_prescaled(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1); \
   hipError_t launch_tile_plan(const FcArgs& a, hipStream_t stream); \
-  template <bool kFc1> hipError_t launch_fc_tiled(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1); \
   hipError_t launch_decode(const DecodeArgs& d, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop); \
   hipError_t launch_fc2_tokens(const DecodeArgs& d, hipStream_t stream); \
   bool routed_fc1_fits(int64_t M, int64_t E, int64_t H, int64_t I, int64_t k); \
@@ -238,7 +247,7 @@ MOE_FORMAT_LAUNCHERS
 
 // fp16 copies of bf16 rows [rows, K], each scaled by 2^-e so that its
 // largest magnitude lies in [2^14, 2^15) (e = 0 for an all-zero row); e goes
-// to exps[row] (fc_tile128.hip, INT4 build).
+// to exps[row] (fc_prescaled.hip, INT4 build).
 hipError_t launch_rowscale(const uint16_t* in, int64_t rows, int64_t K, uint16_t* out, int32_t* exps,
                            hipStream_t stream);
 // One int8 per weight row (E x N) after the INT4 tiles: see sigma_trailer_bytes.

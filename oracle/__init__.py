@@ -266,6 +266,51 @@ class DequantCache:
         return self.items[e]
 
 
+def expert_outputs(x: np.ndarray, topk_ids: np.ndarray,
+                   experts: Callable[[int], Tuple[np.ndarray, np.ndarray]],
+                   tokens_subset=None, map_fn=map) -> Dict[Tuple[int, int], np.ndarray]:
+    """y[(t, j)] = MLP_{ids[t, j]}(x_t) for every slot j of the given tokens.
+
+    Each expert is asked for once (``experts(e)`` may dequantise it) and
+    applied to every (token, slot) routed to it. ``map_fn`` runs the
+    per-expert work (the built-in map: one expert after another in ascending
+    order; a pool's map runs them concurrently, which needs an ``experts``
+    that is safe to call from several threads).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rows = range(x.shape[0]) if tokens_subset is None else tokens_subset
+    by_expert: Dict[int, list] = {}
+    for t in rows:
+        for j in range(topk_ids.shape[1]):
+            by_expert.setdefault(int(topk_ids[t, j]), []).append((t, j))
+
+    def one_expert(e):
+        W13, W2 = experts(e)
+        return [((t, j), expert_mlp(x[t], W13, W2)) for t, j in by_expert[e]]
+
+    y = {}
+    for part in map_fn(one_expert, sorted(by_expert)):
+        y.update(part)
+    return y
+
+
+def combine(topk_weights: np.ndarray, y: Dict[Tuple[int, int], np.ndarray], M: int, H: int,
+            tokens_subset=None) -> np.ndarray:
+    """out[t] = sum_j w[t, j] * y[(t, j)], accumulated in slot order (float64).
+
+    "The Result: Two Regimes": a token's output is the routing-weighted sum of
+    its k experts' outputs. Token rows not computed are NaN.
+    """
+    out = np.full((M, H), np.nan)
+    rows = range(M) if tokens_subset is None else tokens_subset
+    for t in rows:
+        acc = np.zeros(H, dtype=np.float64)
+        for j in range(topk_weights.shape[1]):
+            acc += topk_weights[t, j] * y[(t, j)]
+        out[t] = acc
+    return out
+
+
 def moe_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
                 experts: Callable[[int], Tuple[np.ndarray, np.ndarray]],
                 tokens_subset=None) -> np.ndarray:
@@ -278,15 +323,8 @@ def moe_forward(x: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
     """
     x = np.asarray(x, dtype=np.float64)
     M, H = x.shape
-    out = np.full((M, H), np.nan)
-    rows = range(M) if tokens_subset is None else tokens_subset
-    for t in rows:
-        acc = np.zeros(H, dtype=np.float64)
-        for j in range(topk_ids.shape[1]):
-            W13, W2 = experts(int(topk_ids[t, j]))
-            acc += topk_weights[t, j] * expert_mlp(x[t], W13, W2)
-        out[t] = acc
-    return out
+    y = expert_outputs(x, topk_ids, experts, tokens_subset)
+    return combine(topk_weights, y, M, H, tokens_subset)
 
 
 def layer(x: np.ndarray, logits: np.ndarray, k: int, experts, tokens_subset=None):

@@ -3,6 +3,8 @@ HIP path through the binding, and oracle references on the CPU."""
 from __future__ import annotations
 
 import functools
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -122,3 +124,52 @@ def k26_layer() -> DeviceLayer:
 def k26_mxfp4_layer() -> DeviceLayer:
     """The 384-expert layer with MXFP4 weights (9.0 GB), generated and repacked once per session."""
     return device_layer(wl.K26, 2026, fmt="mxfp4")
+
+
+def covering_rows(ids: np.ndarray, must=()) -> list:
+    """Token rows that together hold every expert the batch routes to, chosen
+    greedily (each pick the row with the most experts not yet held), plus the
+    rows in ``must``; ascending."""
+    E = int(ids.max()) + 1
+    inc = np.zeros((ids.shape[0], E), bool)
+    inc[np.arange(ids.shape[0])[:, None], ids] = True
+    rows = set(int(r) for r in must)
+    left = inc.any(axis=0)
+    for r in rows:
+        left &= ~inc[r]
+    while left.any():
+        r = int(np.argmax(inc[:, left].sum(axis=1)))
+        rows.add(r)
+        left &= ~inc[r]
+    return sorted(rows)
+
+
+def tile_rows_of_hot_experts(ids: np.ndarray, tile_rows: int) -> list:
+    """One token per tile of every expert holding more than one tile: the
+    expert's assignments in ascending f, cut every tile_rows entries (the
+    tiles of the tiled kernels start at each expert and every tile_rows rows)."""
+    k = ids.shape[1]
+    flat = ids.reshape(-1)
+    rows = []
+    for e in np.unique(flat):
+        fs = np.nonzero(flat == e)[0]
+        if fs.size > tile_rows:
+            rows += [int(fs[i] // k) for i in range(0, fs.size, tile_rows)]
+    return rows
+
+
+def oracle_rows_parallel(shape: wl.LayerShape, seed: int, x: np.ndarray, ids: np.ndarray, w: np.ndarray,
+                         rows: list, fmt: str = "int4") -> np.ndarray:
+    """The oracle's output for the given token rows, its per-expert work run
+    on the host's cores (each worker generates and dequantises one expert)."""
+    from threadpoolctl import threadpool_limits
+
+    def experts(e):
+        ew = wl.expert_weights(shape, seed, e, fmt)
+        dq = oracle.DEQUANT[fmt]
+        return dq(ew.w13, ew.s13), dq(ew.w2, ew.s2)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as pool:
+        y = oracle.expert_outputs(x, ids, experts, rows, map_fn=pool.map)
+    return oracle.combine(w, y, x.shape[0], x.shape[1], rows)

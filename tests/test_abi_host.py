@@ -83,7 +83,7 @@ def test_workspace_bytes():
     assert moe.moe_w4a16_workspace_bytes(M, E, H, I, k) == want
     # from 16 assignments per expert on (M*k >= 16*E): also the fp16 copies of the
     # A rows (x, then the activations, in one region) and their row exponents
-    M = 1024
+    M = 768
     want = (a256(M * H * 4) + a256(M * k * I * 2) + 256 + a256((2 * M * k + 16) * 8)
             + a256(max(M * H, M * k * I) * 2) + a256(M * k * 4))
     assert moe.moe_w4a16_workspace_bytes(M, E, H, I, k) == want
@@ -95,8 +95,14 @@ def test_preferred_block_m():
     assert moe.moe_w4a16_preferred_block_m(4, 384, 7168, 2048, 8) == 16
     assert moe.moe_w4a16_preferred_block_m(9, 384, 7168, 2048, 8) == 32
     assert moe.moe_w4a16_preferred_block_m(90, 384, 7168, 2048, 8) == 32
+    # 16 per expert and up: the pre-scaled tiled kernel, 96-row tiles of 32-row blocks
+    assert moe.moe_w4a16_preferred_block_m(768, 384, 7168, 2048, 8) == 32
     assert moe.moe_w4a16_preferred_block_m(1024, 384, 7168, 2048, 8) == 32
-    assert moe.moe_w4a16_preferred_block_m(4096, 384, 7168, 2048, 8) == 64
+    assert moe.moe_w4a16_preferred_block_m(4096, 384, 7168, 2048, 8) == 32
+    # H/32 not whole pair groups: no pre-scaled kernel; the wide block kernel,
+    # 64-row blocks above 24 assignments per expert
+    assert moe.moe_w4a16_preferred_block_m(1024, 384, 7040, 2048, 8) == 32
+    assert moe.moe_w4a16_preferred_block_m(1200, 384, 7040, 2048, 8) == 64
 
 
 def _route(lib, M=4, E=384, k=8, B=16, cap=None, ptr=FAKE, logits=FAKE):

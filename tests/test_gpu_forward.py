@@ -11,8 +11,9 @@ import torch
 import int4_weight_only_moe_amd as moe
 import oracle
 import workloads as wl
-from gpu_common import (DeviceLayer, assert_output_close, assert_route_matches, device_layer, k26_layer,
-                        oracle_experts, route_host, run_layer, to_dev, x_device)
+from gpu_common import (DeviceLayer, assert_output_close, assert_route_matches, covering_rows, device_layer,
+                        k26_layer, oracle_experts, oracle_rows_parallel, route_host, run_layer,
+                        tile_rows_of_hot_experts, to_dev, x_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +136,10 @@ def test_output_guard_bands_and_reuse():
 
 
 # ---------------------------------------------------------------- 384-expert layer
+# Token rows compared with the oracle at the 384-expert sizes: a few fixed
+# rows, and for the workloads named in COVER a greedy set of rows that
+# together hold every expert the batch routes to (for the skewed batch also
+# one row in every 96-row tile of each expert holding more than one tile).
 K26_SAMPLES = {
     "k26_m1": [0],
     "k26_m9": [0, 4, 8],
@@ -147,6 +152,7 @@ K26_SAMPLES = {
     "k26_m4096": [1, 4095],
     "k26_m8192": [0, 5000, 8191],
 }
+COVER = ("k26_m90", "k26_m1024", "k26_m1024_skew", "k26_m4096")
 
 
 @pytest.mark.parametrize("name", list(K26_SAMPLES))
@@ -162,13 +168,17 @@ def test_k26_sampled_parity(name):
     ids, wts = assert_route_matches(route_host(rb), t.logits, s.E, s.k, block_m)
     assert np.all(np.isfinite(out))
     rows = list(K26_SAMPLES[name])
-    if name.endswith("skew"):  # also a token routed to the hottest expert
-        hot = np.bincount(ids.reshape(-1), minlength=s.E).argmax()
-        rows.append(int(np.nonzero((ids == hot).any(axis=1))[0][5]))
+    if name in COVER:
+        rows = covering_rows(ids, rows + (tile_rows_of_hot_experts(ids, 96) if name.endswith("skew") else []))
+    touched = np.unique(ids)
+    covered = np.unique(ids[rows])
     x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)
-    ref = oracle.moe_forward(x, ids, wts, oracle_experts(s, 2026, keep=0), tokens_subset=rows)
+    ref = oracle_rows_parallel(s, 2026, x, ids, wts, rows)
     rel, mx = assert_output_close(out[rows], ref[rows], name)
-    print(f"forward {name}: rows {rows} rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
+    print(f"forward {name}: {len(rows)} rows, experts covered {covered.size}/{touched.size}, "
+          f"rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
+    if name in COVER:
+        assert covered.size == touched.size
 
 
 @pytest.mark.parametrize("block_m", [16, 32, 64])

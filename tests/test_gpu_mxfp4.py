@@ -10,8 +10,8 @@ import torch
 import int4_weight_only_moe_amd as moe
 import oracle
 import workloads as wl
-from gpu_common import (DeviceLayer, assert_output_close, assert_route_matches, device_layer, k26_mxfp4_layer,
-                        oracle_experts, route_host, run_layer, to_dev, x_device)
+from gpu_common import (DeviceLayer, assert_output_close, assert_route_matches, covering_rows, device_layer,
+                        k26_mxfp4_layer, oracle_experts, oracle_rows_parallel, route_host, run_layer, to_dev, x_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -113,7 +113,9 @@ def test_mxfp4_k26_closed_form():
     del w13, w2
 
 
-K26_SAMPLES = {"k26_m1": [0], "k26_m4": [0, 3], "k26_m9": [0, 8], "k26_m90": [0, 89], "k26_m1024": [0, 1023]}
+K26_SAMPLES = {"k26_m1": [0], "k26_m4": [0, 3], "k26_m9": [0, 8], "k26_m90": [0, 89], "k26_m1024": [0, 1023],
+               "k26_m4096": [0, 4095]}
+COVER = ("k26_m1024", "k26_m4096")  # every routed expert in a checked row
 
 
 @pytest.mark.parametrize("name", list(K26_SAMPLES))
@@ -130,9 +132,12 @@ def test_mxfp4_k26_sampled(name):
     ids, wts = assert_route_matches(route_host(rb), t.logits, s.E, s.k, block_m)
     assert np.all(np.isfinite(out))
     rows = K26_SAMPLES[name]
-    ref = oracle.moe_forward(_x(t), ids, wts, oracle_experts(s, 2026, keep=0, fmt="mxfp4"), tokens_subset=rows)
+    if name in COVER:
+        rows = covering_rows(ids, rows)
+    ref = oracle_rows_parallel(s, 2026, _x(t), ids, wts, rows, fmt="mxfp4")
     rel, mx = assert_output_close(out[rows], ref[rows], f"mxfp4 {name}")
-    print(f"mxfp4 {name}: rows {rows} rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
+    print(f"mxfp4 {name}: {len(rows)} rows, experts covered {np.unique(ids[rows]).size}/{np.unique(ids).size}, "
+          f"rel-L2 {rel:.2e} max abs {mx:.3f}", flush=True)
 
 
 @pytest.mark.parametrize("M", [2, 5])

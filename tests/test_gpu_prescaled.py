@@ -1,4 +1,4 @@
-"""The scale-before tiled GEMM (128-row tiles; INT4 weights enter the matrix
+"""The pre-scaled tiled GEMM (96-row INT4 tiles; INT4 weights enter the matrix
 core as fp16(q * s * 2^-sigma), the activation rows as fp16 copies scaled by a
 power of two): the per-row exponent shifts the repack stores after the INT4
 tiles, and every element against the oracle where fp16 alone would overflow
@@ -16,7 +16,7 @@ from gpu_common import (DeviceLayer, assert_output_close, assert_route_matches, 
 pytestmark = pytest.mark.gpu
 
 SHAPE = wl.LayerShape(E=8, H=256, I=256, k=2)
-M = 300  # 75 assignments per expert: the scale-before kernel's regime
+M = 300  # 75 assignments per expert: the pre-scaled kernel's regime
 
 
 def expected_sigma(scales_f16: np.ndarray) -> np.ndarray:
@@ -58,7 +58,7 @@ def test_sigma_trailer_matches_the_scales():
 
 
 @pytest.mark.parametrize("factor13,factor2", [(2.0 ** 19, 2.0 ** 18), (2.0 ** -12, 2.0 ** -11), (2.0 ** 19, 2.0 ** -12)])
-def test_big_tile_extreme_scales(factor13, factor2):
+def test_prescaled_extreme_scales(factor13, factor2):
     """Group scales up to ~1e4 (q * s beyond fp16's range without the row shift)
     and fp16-subnormal scales (rows shifted up by 2^15)."""
     host, layer = layer_with_scales(factor13, factor2)
@@ -69,10 +69,10 @@ def test_big_tile_extreme_scales(factor13, factor2):
         ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w, experts_of(host))
         assert np.all(np.isfinite(out))
         rel, mx = assert_output_close(out, ref, f"scales x{factor13:g}/x{factor2:g} B={block_m}")
-        print(f"big tile scales x{factor13:g}/x{factor2:g} B={block_m}: rel-L2 {rel:.2e}", flush=True)
+        print(f"prescaled scales x{factor13:g}/x{factor2:g} B={block_m}: rel-L2 {rel:.2e}", flush=True)
 
 
-def test_big_tile_activation_rows_outside_fp16():
+def test_prescaled_activation_rows_outside_fp16():
     """Rows scaled by 1e6 (beyond 65504) and 1e-6, and all-zero rows: each row
     keeps its own power-of-two scale; zero rows give exactly zero."""
     host, layer = layer_with_scales(1.0, 1.0)

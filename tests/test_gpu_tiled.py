@@ -1,9 +1,10 @@
 """The tiled grouped GEMM, which the forward takes once experts average at
-least 16 assignments (and every pair group and K-chunk count divides evenly):
-every element against the oracle on shapes whose experts hold from one small
-tile up to several 128-row tiles, with partial tiles of every sub-tile count,
-all block sizes, and skewed routing (a per-expert logit bias) that piles
-hundreds of rows onto a few experts."""
+least 16 assignments (and every pair group and K-chunk count divides
+evenly): the pre-scaled kernel (INT4: 96-row tiles with 16- or 32-row
+blocks, 64-row tiles with 64-row blocks). Every element against the oracle on shapes
+whose experts hold from one small tile up to several full tiles, with
+partial tiles of every sub-tile count, all block sizes, and skewed routing
+(a per-expert logit bias) that piles hundreds of rows onto a few experts."""
 import numpy as np
 import pytest
 
@@ -19,9 +20,10 @@ WIDER = wl.LayerShape(E=32, H=512, I=512, k=4)
 TILED = [
     # (shape, M, bias sigma, weight seed, token seed)
     (SMALL, 64, 0.0, 11, 12),    # 16 assignments per expert: tiles of 1-2 sub-tiles
-    (SMALL, 300, 0.0, 11, 13),   # ~75 per expert: 5-sub-tile tiles (run as 8)
-    (SMALL, 700, 2.0, 11, 14),   # skewed: several 128-row tiles on the hot experts
-    (WIDER, 160, 1.0, 15, 16),   # 20 per expert, mildly skewed
+    (SMALL, 128, 0.0, 11, 17),   # 32 per expert: tiles of 2-3 sub-tiles
+    (SMALL, 300, 0.0, 11, 13),   # ~75 per expert: 5-sub-tile tiles (run as 6), two tiles with 64-row blocks
+    (SMALL, 700, 2.0, 11, 14),   # skewed: several full tiles on the hot experts
+    (WIDER, 320, 1.0, 15, 16),   # 40 per expert, mildly skewed
 ]
 
 
@@ -44,13 +46,15 @@ def test_tiled_full_parity(case, block_m):
 
 
 def test_tiled_skew_has_multi_tile_experts():
-    """The skewed case really exercises experts with several 128-row tiles."""
-    shape, M, sigma, _, tseed = TILED[2]
+    """The skewed case really exercises experts with several full 96-row tiles
+    and partial last tiles with an odd sub-tile count (run with one empty
+    sub-tile)."""
+    shape, M, sigma, _, tseed = TILED[3]
     t = wl.tokens(shape, M, tseed, sigma)
     ids, _ = oracle.route(t.logits, shape.k)
     counts = np.bincount(ids.reshape(-1), minlength=shape.E)
-    assert counts.max() > 2 * 128
-    assert any(c % 128 and (c % 128) // 16 + 1 in (3, 5, 6, 7) for c in counts)
+    assert counts.max() > 2 * 96
+    assert any(c % 96 and ((c % 96) + 15) // 16 in (3, 5) for c in counts)
 
 
 def test_tiled_with_oversized_route_buffers():
@@ -60,7 +64,7 @@ def test_tiled_with_oversized_route_buffers():
     import int4_weight_only_moe_amd as moe
     import torch
     from gpu_common import to_dev, x_device
-    shape, M, sigma, wseed, tseed = TILED[1]
+    shape, M, sigma, wseed, tseed = TILED[2]
     layer = device_layer(shape, wseed)
     t = wl.tokens(shape, M, tseed, sigma)
     for block_m in (16, 64):
