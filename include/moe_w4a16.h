@@ -41,7 +41,10 @@
  *   W2  (kind 1): N = H,   K = I.
  *
  * Limits (MOE_ERR_UNSUPPORTED otherwise): 1 <= E <= 1024, 1 <= top_k <= min(E, 16),
- * H and I multiples of 128, block_m in {16, 32, 64}, M*top_k*max(H, I) < 2^31.
+ * H and I multiples of 128, block_m in {16, 32, 64}, M*top_k*max(H, I) < 2^31,
+ * and one expert's repacked W13 or W2 (moe_w4a16_packed_bytes with E = 1,
+ * less its trailer) below 2^31 bytes (H*I below about 1.9e9; the repack and size
+ * calls apply the same per-tensor limit, and -1 / MOE_ERR_UNSUPPORTED past it).
  *
  * MXFP4 expert weights (the moe_mxfp4_* entry points at the end): "From
  * 1,060 to 4,016 tok/s on one B300, and why it wasn't the kernels" serves a

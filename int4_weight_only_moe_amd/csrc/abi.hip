@@ -21,11 +21,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool block_m_ok(int32_t b) { return b == 16 || b == 32 || b == 64; }
 
+// One expert's repacked tensor (N rows of K channels, either format) stays
+// below 2^31 bytes, so in-expert offsets fit 32 bits and E times it fits int64.
+bool expert_bytes_ok(int32_t N, int32_t K) {
+  return moe::packed_bytes_fmt(moe::kFmtInt4, N, K) < (int64_t(1) << 31);
+}
+
 // Size checks shared by the entry points. Returns MOE_OK or an error code.
 int check_layer(int32_t M, int32_t E, int32_t H, int32_t I, int32_t k) {
   if (M < 0 || E <= 0 || H <= 0 || I <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
   if (E > kMaxExperts || k > kMaxTopK || k > E) return MOE_ERR_UNSUPPORTED;
   if (H % kChunkK != 0 || I % kChunkK != 0) return MOE_ERR_UNSUPPORTED;
+  if (I > (int32_t(1) << 30) || !expert_bytes_ok(2 * I, H) || !expert_bytes_ok(H, I)) return MOE_ERR_UNSUPPORTED;
   const int64_t mk = (int64_t)M * k;
   const int64_t widest = H > I ? H : I;
   if (mk * widest >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
@@ -96,11 +103,13 @@ int moe_route_align(const float* logits, int32_t M, int32_t E, int32_t top_k, in
 
 int64_t moe_w4a16_packed_bytes(int32_t E, int32_t N, int32_t K, int32_t group) {
   if (E <= 0 || N <= 0 || K <= 0 || group != kGroup || N % kPairRows != 0 || K % kChunkK != 0) return -1;
+  if (E > kMaxExperts || !expert_bytes_ok(N, K)) return -1;
   return (int64_t)E * moe::packed_bytes_fmt(moe::kFmtInt4, N, K) + moe::sigma_trailer_bytes(moe::kFmtInt4, E, N);
 }
 
 int64_t moe_mxfp4_packed_bytes(int32_t E, int32_t N, int32_t K) {
   if (E <= 0 || N <= 0 || K <= 0 || N % kPairRows != 0 || K % kChunkK != 0) return -1;
+  if (E > kMaxExperts || !expert_bytes_ok(N, K)) return -1;
   return (int64_t)E * moe::packed_bytes_fmt(moe::kFmtMxfp4, N, K);
 }
 
@@ -109,6 +118,7 @@ static int check_repack(const void* a, const void* b, const void* c, int32_t E, 
   if (E <= 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
   if (kind != 0 && kind != 1) return MOE_ERR_INVALID_ARG;
   if (group != kGroup || N % kPairRows != 0 || K % kChunkK != 0) return MOE_ERR_UNSUPPORTED;
+  if (E > kMaxExperts || !expert_bytes_ok(N, K)) return MOE_ERR_UNSUPPORTED;
   if (kind == 0 && (N / 2) % 16 != 0) return MOE_ERR_UNSUPPORTED;
   if (!a || !b || !c) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return MOE_ERR_INVALID_ARG;
