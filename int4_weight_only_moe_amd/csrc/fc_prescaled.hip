@@ -62,6 +62,23 @@ constexpr int kBMaxRows = prescaled_max_rows(kFmt);   // 96 (INT4) or 128 (MXFP4
 constexpr int kBSlotVecs = kBMaxRows * kBVecs;         // one LDS slot: up to 128 rows x 16 vectors
 constexpr int kBXcds = 8;
 constexpr int kBWLoads = 4;                  // vector loads per weight chunk (2 tiles' codes + scales)
+#ifndef MOE_PRESCALED_APRE
+#define MOE_PRESCALED_APRE 3
+#endif
+constexpr int kAPre = MOE_PRESCALED_APRE;    // A fragments in flight per group (INT4)
+// Pipeline depth: chunks whose weights (registers) and rows (LDS slots) are
+// in flight or resident at once; waves per SIMD (4: two workgroups per CU).
+#ifndef MOE_PRESCALED_DEPTH
+#define MOE_PRESCALED_DEPTH 2
+#endif
+#ifndef MOE_PRESCALED_WPE
+#define MOE_PRESCALED_WPE 4
+#endif
+constexpr int kDepth = MOE_PRESCALED_DEPTH;
+constexpr int kWpe = MOE_PRESCALED_WPE;
+struct XSlots {
+  uint4* x[kDepth];
+};
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -207,7 +224,7 @@ __device__ __forceinline__ void prescaled_epilogue(const FcArgs& a, const int e,
 // kPolicy.
 template <int S, bool kFc1, int kPolicy>
 __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, const int pair, const int row0,
-                                              const int nsub, uint4* xt0, uint4* xt1, uint32_t* xoffs) {
+                                              const int nsub, const XSlots xs, uint32_t* xoffs) {
   static_assert(S % 2 == 0 && S * kTileRows <= kBMaxRows, "S even, at most the tile's sub-tiles");
   constexpr int kD = S / 2;  // 1 KB copies per wave per chunk
   const int tid = threadIdx.x, lane = tid & 63;
@@ -233,8 +250,7 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
     w.s1 = load_scales<kPolicy>(wr, base + os1);
     return w;
   };
-  WChunk wb[2];
-  wb[0] = load_w(0);
+  WChunk wb[kDepth];
 
   // 2^-sigma of this lane's two weight rows (column lane % 16 of each tile).
   f16x2_t m2 = {(_Float16)1.0f, (_Float16)1.0f};
@@ -270,7 +286,7 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
     for (int i = 0; i < kD; ++i) xoff[i] = myoff[i];
 #pragma unroll
     for (int i = 0; i < kD; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)((slot ? xt1 : xt0) + (wave + kBW * i) * 64), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xs.x[slot] + (wave + kBW * i) * 64), 16,
                                                xoff[i], (uint32_t)c * (kChunkK * 2), 0, 0);
   };
   // LDS vector of this lane's A operand for group g of sub-tile 0 (slot 0):
@@ -288,14 +304,22 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
     acc1[s] = zero4;
   }
 
-  // Issue order weights(0), rows(0), weights(1): after the wait only the
-  // newest weight chunk is in flight, as at the end of every chunk step.
+  // Chunk step c issues the rows of chunk c + kDepth - 1 into LDS, computes
+  // chunk c, then loads the weights of chunk c + kDepth; the prologue is the
+  // steps before chunk 0 without their compute, so that the same wait holds
+  // after every step: the rows and weights of the next chunk have arrived,
+  // the newer loads may stay in flight (kVmAfter of them).
+  constexpr int kVmAfter = (kDepth - 2) * (kD + kBWLoads) + kBWLoads;
+  static_assert(kVmAfter < 64, "vmcnt holds at most 63");
+#pragma unroll
+  for (int c = -kDepth; c < 0; ++c) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + kDepth - 1 >= 0) copy_rows(c + kDepth - 1, (c + kDepth - 1) % kDepth);
+    __builtin_amdgcn_sched_barrier(0);
+    wb[c + kDepth] = load_w(c + kDepth);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  copy_rows(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  wb[1] = load_w(1);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(kBWLoads, 0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(kVmAfter, 0));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
@@ -316,19 +340,24 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
         const f16x2_t t0 = g < 2 ? s0lo : s0hi, t1 = g < 2 ? s1lo : s1hi;
         const f16x2_t g0 = (g & 1) ? __builtin_shufflevector(t0, t0, 1, 1) : __builtin_shufflevector(t0, t0, 0, 0);
         const f16x2_t g1 = (g & 1) ? __builtin_shufflevector(t1, t1, 1, 1) : __builtin_shufflevector(t1, t1, 0, 0);
+        // A fragments in a ring of kAPre registers: the first kAPre - 1
+        // sub-tiles' rows are read before the widening, and sub-tile
+        // s + kAPre - 1's while sub-tile s's MFMAs are issued
+        const uint4* ap = xs.x[slot] + aoff(g);
+        f16x8_t ar[kAPre];
+#pragma unroll
+        for (int p = 0; p + 1 < kAPre; ++p)
+          if (p < S) ar[p] = __builtin_bit_cast(f16x8_t, ap[p * kTileRows * kBVecs]);
+        __builtin_amdgcn_sched_barrier(0);
         const f16x8_t b0 = dequant_int4_f16(q0[g], g0);
         const f16x8_t b1 = dequant_int4_f16(q1[g], g1);
-        // one A fragment read ahead: sub-tile s + 1's rows load while sub-tile
-        // s's MFMAs are issued (more in flight would not fit the registers)
-        const uint4* ap = (slot ? xt1 : xt0) + aoff(g);
-        f16x8_t xv = __builtin_bit_cast(f16x8_t, ap[0]);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          f16x8_t xn = xv;
-          if (s + 1 < S) xn = __builtin_bit_cast(f16x8_t, ap[(s + 1) * kTileRows * kBVecs]);
+          if (s + kAPre - 1 < S)
+            ar[(s + kAPre - 1) % kAPre] = __builtin_bit_cast(f16x8_t, ap[(s + kAPre - 1) * kTileRows * kBVecs]);
+          const f16x8_t xv = ar[s % kAPre];
           acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b0, acc0[s], 0, 0, 0);
           acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b1, acc1[s], 0, 0, 0);
-          xv = xn;
           __builtin_amdgcn_sched_barrier(0);
         }
         // the next group's codes and rows are not hoisted above these MFMAs
@@ -339,7 +368,7 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
         const bf16x8_t b1 = dequant_group(q1[g], group_scale(w.s1, g));
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          const bf16x8_t xv = as_bf16x8((slot ? xt1 : xt0)[s * kTileRows * kBVecs + aoff(g)]);
+          const bf16x8_t xv = as_bf16x8(xs.x[slot][s * kTileRows * kBVecs + aoff(g)]);
           acc0[s] = mfma16x16x32(xv, b0, acc0[s]);
           acc1[s] = mfma16x16x32(xv, b1, acc1[s]);
         }
@@ -348,25 +377,27 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
     }
   };
 
-  // n is even (checked by the launcher): the slot of chunk c is c % 2 = j.
-  for (int c = 0; c < n; c += 2) {
+  // The slot and weight buffer of chunk c are c % kDepth = j. Steps past the
+  // last chunk (n need not be a multiple of kDepth) are skipped.
+  for (int c = 0; c < n; c += kDepth) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kDepth; ++j) {
       const int cc = c + j;
-      // The next chunk's rows into the other slot (every wave passed the
-      // last barrier after its reads of that slot completed). Past the last
-      // chunk the copy reads the next rows' data (or nothing) into a slot no
-      // one reads.
-      copy_rows(cc + 1, j ^ 1);
+      if (kDepth > 2 && cc >= n) break;
+      // Rows of chunk cc + kDepth - 1 into the slot chunk cc - 1 used (every
+      // wave passed the last barrier after its reads of that slot
+      // completed). Past the last chunk the copy reads the next rows' data
+      // (or nothing) into a slot no one reads.
+      copy_rows(cc + kDepth - 1, (j + kDepth - 1) % kDepth);
       __builtin_amdgcn_sched_barrier(0);
       compute(wb[j], j);
       __builtin_amdgcn_sched_barrier(0);
-      wb[j] = load_w(cc + 2);
+      wb[j] = load_w(cc + kDepth);
       __builtin_amdgcn_sched_barrier(0);
-      // the rows of chunk cc + 1 and the weights of chunk cc + 1 have
-      // arrived; this step's weight loads may stay in flight. lgkmcnt(0):
-      // this wave's reads of slot j are done before anyone refills it.
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(kBWLoads, 0));
+      // the rows and weights of chunk cc + 1 have arrived; newer loads may
+      // stay in flight. lgkmcnt(0): this wave's reads of slot j are done
+      // before anyone refills it.
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(kVmAfter, 0));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -382,22 +413,30 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
 
 template <int S, bool kFc1>
 __device__ __forceinline__ void prescaled_policy(const FcArgs& a, const int e, const int pair, const int row0,
-                                                const int nsub, const bool reuse, uint4* xt0, uint4* xt1,
+                                                const int nsub, const bool reuse, const XSlots xs,
                                                 uint32_t* xoffs) {
   if (reuse)
-    prescaled_body<S, kFc1, kPolicyDefault>(a, e, pair, row0, nsub, xt0, xt1, xoffs);
+    prescaled_body<S, kFc1, kPolicyDefault>(a, e, pair, row0, nsub, xs, xoffs);
   else
-    prescaled_body<S, kFc1, kPolicyWeights>(a, e, pair, row0, nsub, xt0, xt1, xoffs);
+    prescaled_body<S, kFc1, kPolicyWeights>(a, e, pair, row0, nsub, xs, xoffs);
 }
 
 template <bool kFc1>
-__global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(kWpe)))
 void fc_prescaled_kernel(FcArgs a) {
-  // the two slots of the tile's activation chunk, as separate objects: the
-  // compiler then knows that reads of one need not wait for copies into the
-  // other (with one array it drains every load before each chunk's reads)
+  // the slots of the tile's activation chunks, as separate objects: the
+  // compiler then knows that reads of one need not wait for copies into
+  // another (with one array it drains every load before each chunk's reads)
   __shared__ uint4 xt0[kBSlotVecs];
   __shared__ uint4 xt1[kBSlotVecs];
+  __shared__ uint4 xt2[kDepth > 2 ? kBSlotVecs : 1];
+  __shared__ uint4 xt3[kDepth > 3 ? kBSlotVecs : 1];
+  static_assert(kDepth >= 2 && kDepth <= 4, "two to four slots");
+  XSlots xs;
+  xs.x[0] = xt0;
+  xs.x[1] = xt1;
+  if constexpr (kDepth > 2) xs.x[2] = xt2;
+  if constexpr (kDepth > 3) xs.x[3] = xt3;
   __shared__ uint32_t xoffs[64 * kBW * (kBMaxRows / kTileRows / 2)];  // each thread's copy source offsets
   constexpr int kThreads = 64 * kBW;
   const int tid = threadIdx.x;
@@ -429,10 +468,10 @@ void fc_prescaled_kernel(FcArgs a) {
   const int e = meta >> kTileExpertShift;
   if (e < 0 || e >= a.E || nsub < 1 || nsub > a.tile_rows / kTileRows) return;
 
-  if (nsub <= 2) prescaled_policy<2, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
-  else if (nsub <= 4) prescaled_policy<4, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
-  else if (kBMaxRows <= 96 || nsub <= 6) prescaled_policy<6, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
-  else if constexpr (kBMaxRows >= 128) prescaled_policy<8, kFc1>(a, e, pair, row0, nsub, reuse, xt0, xt1, xoffs);
+  if (nsub <= 2) prescaled_policy<2, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
+  else if (nsub <= 4) prescaled_policy<4, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
+  else if (kBMaxRows <= 96 || nsub <= 6) prescaled_policy<6, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
+  else if constexpr (kBMaxRows >= 128) prescaled_policy<8, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
 }
 
 }  // namespace

@@ -63,7 +63,12 @@ static __host__ __device__ inline int64_t packed_bytes_per_expert(int64_t N, int
 // Largest tile of the pre-scaled tiled kernel (fc_prescaled.hip): 96 rows
 // for INT4 (the widened fp16 codes take the registers of two more
 // sub-tiles), 128 for MXFP4.
-__host__ __device__ constexpr int prescaled_max_rows(int fmt) { return fmt == kFmtMxfp4 ? 128 : 96; }
+#ifndef MOE_PRESCALED_INT4_ROWS
+#define MOE_PRESCALED_INT4_ROWS 96
+#endif
+__host__ __device__ constexpr int prescaled_max_rows(int fmt) {
+  return fmt == kFmtMxfp4 ? 128 : MOE_PRESCALED_INT4_ROWS;
+}
 // Tile rows of the pre-scaled kernel for a block size: whole blocks per tile.
 inline int prescaled_tile_rows(int fmt, int block_m) {
   const int r = prescaled_max_rows(fmt);
