@@ -40,7 +40,8 @@
 //     vectors are stored XOR-swizzled with the row index, so the A reads of a
 //     wave (16 rows, one vector each) hit 16 different bank groups;
 //   * per 32-channel group a wave widens both tiles' codes once and runs
-//     2 x S MFMAs (S = sub-tiles of 16 rows: 2, 4, 6, or 8 for MXFP4);
+//     2 x S MFMAs (S = the tile's sub-tiles of 16 rows, at most 6, or 8 for
+//     MXFP4: padding sub-tiles are not multiplied);
 //   * per chunk step: the next chunk's rows go to LDS, the current chunk is
 //     computed, the weight chunk after next is loaded, then one wait (the
 //     rows and the next weight chunk; the newest weight loads stay in flight)
@@ -73,6 +74,9 @@ constexpr int kAPre = MOE_PRESCALED_APRE;    // A fragments in flight per group 
 #endif
 #ifndef MOE_PRESCALED_WPE
 #define MOE_PRESCALED_WPE 4
+#endif
+#ifndef MOE_PRESCALED_SWP
+#define MOE_PRESCALED_SWP 0
 #endif
 constexpr int kDepth = MOE_PRESCALED_DEPTH;
 constexpr int kWpe = MOE_PRESCALED_WPE;
@@ -109,6 +113,18 @@ __device__ __forceinline__ f16x8_t dequant_int4_f16(uint32_t w, f16x2_t s2) {
   const f16x2_t p3 = (as_f16x2((t & m1) | c1) + as_f16x2(o1)) * s2;
   return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
                                  __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// One quarter of dequant_int4_f16: codes k (bits [4k, 4k+4) of each half of
+// w >> (k < 2 ? 0 : 8)... written as the two values fp16(q * s2) of piece k.
+__device__ __forceinline__ f16x2_t dequant_int4_piece(uint32_t w, f16x2_t s2, int k) {
+  uint32_t m = (k & 1) ? 0x00F000F0u : 0x000F000Fu, c = (k & 1) ? 0x54005400u : 0x64006400u;
+  uint32_t o = (k & 1) ? 0xD480D480u : 0xE408E408u;
+  asm("" : "+s"(m));
+  asm("" : "+v"(c));
+  asm("" : "+s"(o));
+  const uint32_t src = k < 2 ? w : (w >> 8);
+  return (as_f16x2((src & m) | c) + as_f16x2(o)) * s2;
 }
 
 // ---------------------------------------------------------------------------
@@ -181,39 +197,99 @@ __device__ __forceinline__ void row_sigmas(const FcArgs& a, int e, int pair, int
 template <bool kFc1>
 __device__ __forceinline__ uint32_t a_row(int f, int k) { return (uint32_t)(kFc1 ? f / k : f); }
 
-// Epilogue of the tile pair for rows frow (per sub-tile, the row of lane % 16):
-// INT4 scales each output by 2^(row exponent + sigma of its weight row).
-template <int S, bool kFc1>
-__device__ __forceinline__ void prescaled_epilogue(const FcArgs& a, const int e, const int pair, const int (&frow)[S],
-                                             const int nsub, const f32x4_t (&acc0)[S], const f32x4_t (&acc1)[S],
-                                             const int lane) {
+// Epilogues of the tile pair. INT4 scales each output by 2^(row exponent +
+// sigma of its weight row). Per sub-tile, lane L first derives what belongs
+// to its own A row (L % 16): the row's token, exponent and, for FC2, routing
+// weight (one load each, issued together).
+//
+// FC1 multiplies with the operands swapped (the weights as the first MFMA
+// operand), so the accumulators hold D transposed: lane L has A row L % 16
+// and output columns 4 (L / 16) .. +3, and writes its 4 SiLU(gate) * up
+// values as one 8-byte store.
+template <int S>
+__device__ __forceinline__ void prescaled_epilogue_fc1(const FcArgs& a, const int e, const int pair,
+                                                       const int (&frow)[S], const int nsub, const f32x4_t (&acc0)[S],
+                                                       const f32x4_t (&acc1)[S], const int lane) {
+  const int MK = a.M * a.k;
+  const int c0 = 4 * (lane >> 4);
+  int sg0[4] = {0, 0, 0, 0}, sg1[4] = {0, 0, 0, 0};
+  if constexpr (kFmt == kFmtInt4) {
+    const int8_t* sig = a.wsigma + (int64_t)e * (2 * a.I) + 16 * pair + c0;
+    const uint32_t d0 = *reinterpret_cast<const uint32_t*>(sig);
+    const uint32_t d1 = *reinterpret_cast<const uint32_t*>(sig + a.I);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sg0[i] = (int)(int8_t)(d0 >> (8 * i));
+      sg1[i] = (int)(int8_t)(d1 >> (8 * i));
+    }
+  }
+  int ex[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int f = frow[s];
+    ex[s] = 0;
+    if constexpr (kFmt == kFmtInt4)
+      if (s < nsub && f >= 0 && f < MK) ex[s] = a.row_exp[f / a.k];
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int f = frow[s];
+    if (s >= nsub || f < 0 || f >= MK) continue;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float g = acc0[s][i], u = acc1[s][i];
+      if constexpr (kFmt == kFmtInt4) {
+        g = __builtin_ldexpf(g, ex[s] + sg0[i]);
+        u = __builtin_ldexpf(u, ex[s] + sg1[i]);
+      }
+      // SiLU(g) * u; the reciprocal's rounding is far below the bf16 store's
+      o[i] = f32_to_bf16_bits(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u);
+    }
+    *reinterpret_cast<uint2*>(a.act_out + (uint32_t)(f * a.I + 16 * pair + c0)) =
+        make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+  }
+}
+
+// FC2: lane L has rows 4 (L / 16) + i and output column L % 16 of each tile;
+// the per-row values come from the owning lane by a shuffle.
+template <int S>
+__device__ __forceinline__ void prescaled_epilogue_fc2(const FcArgs& a, const int e, const int pair,
+                                                       const int (&frow)[S], const int nsub, const f32x4_t (&acc0)[S],
+                                                       const f32x4_t (&acc1)[S], const int lane) {
   const int MK = a.M * a.k;
   const int col = lane & 15;
   int sig0 = 0, sig1 = 0;  // read again here rather than kept live across the main loop
-  if constexpr (kFmt == kFmtInt4) row_sigmas<kFc1>(a, e, pair, lane, sig0, sig1);
+  if constexpr (kFmt == kFmtInt4) row_sigmas<false>(a, e, pair, lane, sig0, sig1);
+  int off[S], ex[S];
+  float w[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int f = frow[s];
+    const bool ok = s < nsub && f >= 0 && f < MK;
+    off[s] = ok ? (f / a.k) * a.H + kPairRows * pair : -1;  // < M * H < 2^31
+    w[s] = ok ? a.topk_weights[f] : 0.0f;
+    ex[s] = 0;
+    if constexpr (kFmt == kFmtInt4) ex[s] = ok ? a.row_exp[f] : 0;
+  }
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     if (s >= nsub) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int f = __shfl(frow[s], 4 * (lane >> 4) + i, 64);
-      if (f < 0 || f >= MK) continue;
+      const int src = 4 * (lane >> 4) + i;
+      const int o = __shfl(off[s], src, 64);
+      if (o < 0) continue;
+      const float wt = __shfl(w[s], src, 64);
       float v0 = acc0[s][i], v1 = acc1[s][i];
       if constexpr (kFmt == kFmtInt4) {
-        const int ex = a.row_exp[kFc1 ? f / a.k : f];
-        v0 = __builtin_ldexpf(v0, ex + sig0);
-        v1 = __builtin_ldexpf(v1, ex + sig1);
+        const int x = __shfl(ex[s], src, 64);
+        v0 = __builtin_ldexpf(v0, x + sig0);
+        v1 = __builtin_ldexpf(v1, x + sig1);
       }
-      if constexpr (kFc1) {
-        const float act = v0 / (1.0f + __expf(-v0)) * v1;
-        a.act_out[(int64_t)f * a.I + 16 * pair + col] = (uint16_t)f32_to_bf16_bits(act);
-      } else {
-        const int t = f / a.k;
-        const float w = a.topk_weights[f];
-        float* dst = a.acc + (int64_t)t * a.H + kPairRows * pair;
-        unsafeAtomicAdd(dst + col, w * v0);
-        unsafeAtomicAdd(dst + 16 + col, w * v1);
-      }
+      float* dst = a.acc + (uint32_t)o;
+      unsafeAtomicAdd(dst + col, wt * v0);
+      unsafeAtomicAdd(dst + 16 + col, wt * v1);
     }
   }
 }
@@ -225,8 +301,8 @@ __device__ __forceinline__ void prescaled_epilogue(const FcArgs& a, const int e,
 template <int S, bool kFc1, int kPolicy>
 __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, const int pair, const int row0,
                                               const int nsub, const XSlots xs, uint32_t* xoffs) {
-  static_assert(S % 2 == 0 && S * kTileRows <= kBMaxRows, "S even, at most the tile's sub-tiles");
-  constexpr int kD = S / 2;  // 1 KB copies per wave per chunk
+  constexpr int kD = (S + 1) / 2;  // 1 KB copies per wave per chunk (32 rows per round of 8 waves)
+  static_assert(S >= 1 && 2 * kD * kTileRows <= kBMaxRows, "the copies fit the slot");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = kFc1 ? a.H : a.I;
@@ -334,6 +410,57 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
       s1lo = as_f16x2(w.s1.x) * m21;
       s1hi = as_f16x2(w.s1.y) * m21;
     }
+#if MOE_PRESCALED_SWP
+    if constexpr (kFmt == kFmtInt4) {
+      // Software-pipelined: the codes of group g + 1 are widened between the
+      // MFMAs of group g (two B buffers), and the A fragments run in one ring
+      // across the chunk's groups.
+      auto gscale = [&](int g, int t) {
+        const f16x2_t v = t == 0 ? (g < 2 ? s0lo : s0hi) : (g < 2 ? s1lo : s1hi);
+        return (g & 1) ? __builtin_shufflevector(v, v, 1, 1) : __builtin_shufflevector(v, v, 0, 0);
+      };
+      constexpr int NF = 4 * S;
+      auto rd = [&](int f) {
+        return __builtin_bit_cast(f16x8_t, xs.x[slot][aoff(f / S) + (f % S) * kTileRows * kBVecs]);
+      };
+      f16x8_t ar[kAPre];
+#pragma unroll
+      for (int p = 0; p + 1 < kAPre; ++p) ar[p] = rd(p);
+      f16x8_t b0 = dequant_int4_f16(q0[0], gscale(0, 0));
+      f16x8_t b1 = dequant_int4_f16(q1[0], gscale(0, 1));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f16x2_t bn[8];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int f = g * S + s;
+          if (f + kAPre - 1 < NF) ar[(f + kAPre - 1) % kAPre] = rd(f + kAPre - 1);
+          const f16x8_t xv = ar[f % kAPre];
+          if constexpr (kFc1) {
+            acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b0, xv, acc0[s], 0, 0, 0);
+            acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1, xv, acc1[s], 0, 0, 0);
+          } else {
+            acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b0, acc0[s], 0, 0, 0);
+            acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b1, acc1[s], 0, 0, 0);
+          }
+          if (g < 3) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if ((i * S) / 8 == s) bn[i] = dequant_int4_piece(i < 4 ? q0[g + 1] : q1[g + 1], gscale(g + 1, i / 4), i & 3);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (g < 3) {
+          b0 = __builtin_shufflevector(__builtin_shufflevector(bn[0], bn[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(bn[2], bn[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+          b1 = __builtin_shufflevector(__builtin_shufflevector(bn[4], bn[5], 0, 1, 2, 3),
+                                       __builtin_shufflevector(bn[6], bn[7], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
+      return;
+    }
+#endif
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       if constexpr (kFmt == kFmtInt4) {
@@ -356,8 +483,13 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
           if (s + kAPre - 1 < S)
             ar[(s + kAPre - 1) % kAPre] = __builtin_bit_cast(f16x8_t, ap[(s + kAPre - 1) * kTileRows * kBVecs]);
           const f16x8_t xv = ar[s % kAPre];
-          acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b0, acc0[s], 0, 0, 0);
-          acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b1, acc1[s], 0, 0, 0);
+          if constexpr (kFc1) {  // D transposed (see the FC1 epilogue)
+            acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b0, xv, acc0[s], 0, 0, 0);
+            acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1, xv, acc1[s], 0, 0, 0);
+          } else {
+            acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b0, acc0[s], 0, 0, 0);
+            acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b1, acc1[s], 0, 0, 0);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         // the next group's codes and rows are not hoisted above these MFMAs
@@ -369,8 +501,13 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           const bf16x8_t xv = as_bf16x8(xs.x[slot][s * kTileRows * kBVecs + aoff(g)]);
-          acc0[s] = mfma16x16x32(xv, b0, acc0[s]);
-          acc1[s] = mfma16x16x32(xv, b1, acc1[s]);
+          if constexpr (kFc1) {
+            acc0[s] = mfma16x16x32(b0, xv, acc0[s]);
+            acc1[s] = mfma16x16x32(b1, xv, acc1[s]);
+          } else {
+            acc0[s] = mfma16x16x32(xv, b0, acc0[s]);
+            acc1[s] = mfma16x16x32(xv, b1, acc1[s]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -408,7 +545,10 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
   int frow[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) frow[s] = s < nsub ? rows[kTileRows * s + (lane & 15)] : MK;
-  prescaled_epilogue<S, kFc1>(a, e, pair, frow, nsub, acc0, acc1, lane);
+  if constexpr (kFc1)
+    prescaled_epilogue_fc1<S>(a, e, pair, frow, nsub, acc0, acc1, lane);
+  else
+    prescaled_epilogue_fc2<S>(a, e, pair, frow, nsub, acc0, acc1, lane);
 }
 
 template <int S, bool kFc1>
@@ -468,10 +608,20 @@ void fc_prescaled_kernel(FcArgs a) {
   const int e = meta >> kTileExpertShift;
   if (e < 0 || e >= a.E || nsub < 1 || nsub > a.tile_rows / kTileRows) return;
 
-  if (nsub <= 2) prescaled_policy<2, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
-  else if (nsub <= 4) prescaled_policy<4, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
-  else if (kBMaxRows <= 96 || nsub <= 6) prescaled_policy<6, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
-  else if constexpr (kBMaxRows >= 128) prescaled_policy<8, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
+  // exactly the tile's sub-tiles are multiplied
+  switch (nsub) {
+    case 1: prescaled_policy<1, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
+    case 2: prescaled_policy<2, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
+    case 3: prescaled_policy<3, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
+    case 4: prescaled_policy<4, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
+    case 5: prescaled_policy<5, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
+    case 6: prescaled_policy<6, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
+    default:
+      if constexpr (kBMaxRows >= 128) {
+        if (nsub == 7) prescaled_policy<7, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
+        else prescaled_policy<8, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
+      }
+  }
 }
 
 }  // namespace
