@@ -78,10 +78,15 @@ constexpr int kAPre = MOE_PRESCALED_APRE;    // A fragments in flight per group 
 #ifndef MOE_PRESCALED_SWP
 #define MOE_PRESCALED_SWP 0
 #endif
-constexpr int kDepth = MOE_PRESCALED_DEPTH;
+#ifndef MOE_PRESCALED_ASLOTS
+#define MOE_PRESCALED_ASLOTS MOE_PRESCALED_DEPTH
+#endif
+constexpr int kDepth = MOE_PRESCALED_DEPTH;   // weight chunks held in registers
+constexpr int kASlots = MOE_PRESCALED_ASLOTS; // activation chunks held in LDS
+constexpr int kUnroll = kDepth == kASlots ? kDepth : kDepth * kASlots;  // lcm for depths 2..4 with |difference| 1
 constexpr int kWpe = MOE_PRESCALED_WPE;
 struct XSlots {
-  uint4* x[kDepth];
+  uint4* x[kASlots];
 };
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -380,19 +385,23 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
     acc1[s] = zero4;
   }
 
-  // Chunk step c issues the rows of chunk c + kDepth - 1 into LDS, computes
+  // Chunk step c issues the rows of chunk c + kASlots - 1 into LDS, computes
   // chunk c, then loads the weights of chunk c + kDepth; the prologue is the
   // steps before chunk 0 without their compute, so that the same wait holds
   // after every step: the rows and weights of the next chunk have arrived,
-  // the newer loads may stay in flight (kVmAfter of them).
-  constexpr int kVmAfter = (kDepth - 2) * (kD + kBWLoads) + kBWLoads;
+  // the newer loads may stay in flight (kVmAfter of them: those issued after
+  // the later of the two).
+  constexpr int kAfterW = (kDepth - 1) * (kD + kBWLoads);
+  constexpr int kAfterRows = kBWLoads + (kASlots - 2) * (kD + kBWLoads);
+  constexpr int kVmAfter = kAfterW < kAfterRows ? kAfterW : kAfterRows;
   static_assert(kVmAfter < 64, "vmcnt holds at most 63");
+  constexpr int kPro = kASlots - 1 > kDepth ? kASlots - 1 : kDepth;
 #pragma unroll
-  for (int c = -kDepth; c < 0; ++c) {
+  for (int c = -kPro; c < 0; ++c) {
     __builtin_amdgcn_sched_barrier(0);
-    if (c + kDepth - 1 >= 0) copy_rows(c + kDepth - 1, (c + kDepth - 1) % kDepth);
+    if (c + kASlots - 1 >= 0) copy_rows(c + kASlots - 1, (c + kASlots - 1) % kASlots);
     __builtin_amdgcn_sched_barrier(0);
-    wb[c + kDepth] = load_w(c + kDepth);
+    if (c + kDepth >= 0) wb[c + kDepth] = load_w(c + kDepth);
   }
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(kVmAfter, 0));
@@ -514,22 +523,23 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
     }
   };
 
-  // The slot and weight buffer of chunk c are c % kDepth = j. Steps past the
-  // last chunk (n need not be a multiple of kDepth) are skipped.
-  for (int c = 0; c < n; c += kDepth) {
+  // Chunk c uses weight buffer c % kDepth and slot c % kASlots (static in
+  // the unrolled body). Steps past the last chunk (n need not be a multiple
+  // of the unroll) are skipped.
+  for (int c = 0; c < n; c += kUnroll) {
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
+    for (int j = 0; j < kUnroll; ++j) {
       const int cc = c + j;
-      if (kDepth > 2 && cc >= n) break;
-      // Rows of chunk cc + kDepth - 1 into the slot chunk cc - 1 used (every
+      if (kUnroll > 2 && cc >= n) break;
+      // Rows of chunk cc + kASlots - 1 into the slot chunk cc - 1 used (every
       // wave passed the last barrier after its reads of that slot
       // completed). Past the last chunk the copy reads the next rows' data
       // (or nothing) into a slot no one reads.
-      copy_rows(cc + kDepth - 1, (j + kDepth - 1) % kDepth);
+      copy_rows(cc + kASlots - 1, (j + kASlots - 1) % kASlots);
       __builtin_amdgcn_sched_barrier(0);
-      compute(wb[j], j);
+      compute(wb[j % kDepth], j % kASlots);
       __builtin_amdgcn_sched_barrier(0);
-      wb[j] = load_w(cc + kDepth);
+      wb[j % kDepth] = load_w(cc + kDepth);
       __builtin_amdgcn_sched_barrier(0);
       // the rows and weights of chunk cc + 1 have arrived; newer loads may
       // stay in flight. lgkmcnt(0): this wave's reads of slot j are done
@@ -569,14 +579,15 @@ void fc_prescaled_kernel(FcArgs a) {
   // another (with one array it drains every load before each chunk's reads)
   __shared__ uint4 xt0[kBSlotVecs];
   __shared__ uint4 xt1[kBSlotVecs];
-  __shared__ uint4 xt2[kDepth > 2 ? kBSlotVecs : 1];
-  __shared__ uint4 xt3[kDepth > 3 ? kBSlotVecs : 1];
-  static_assert(kDepth >= 2 && kDepth <= 4, "two to four slots");
+  __shared__ uint4 xt2[kASlots > 2 ? kBSlotVecs : 1];
+  __shared__ uint4 xt3[kASlots > 3 ? kBSlotVecs : 1];
+  static_assert(kDepth >= 2 && kDepth <= 4 && kASlots >= 2 && kASlots <= 4, "two to four buffers");
+  static_assert(kDepth == kASlots || kDepth - kASlots == 1 || kASlots - kDepth == 1, "unroll = lcm");
   XSlots xs;
   xs.x[0] = xt0;
   xs.x[1] = xt1;
-  if constexpr (kDepth > 2) xs.x[2] = xt2;
-  if constexpr (kDepth > 3) xs.x[3] = xt3;
+  if constexpr (kASlots > 2) xs.x[2] = xt2;
+  if constexpr (kASlots > 3) xs.x[3] = xt3;
   __shared__ uint32_t xoffs[64 * kBW * (kBMaxRows / kTileRows / 2)];  // each thread's copy source offsets
   constexpr int kThreads = 64 * kBW;
   const int tid = threadIdx.x;
