@@ -109,6 +109,7 @@ def output_errors(got: np.ndarray, ref: np.ndarray):
 
 def assert_output_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
     rel, mx, bound = output_errors(got, ref)
+    print(f"parity {what}: rel-L2 {rel:.3e} (<= 5e-3), max abs {mx:.3e} (<= {bound:.3e})", flush=True)
     assert rel <= 5e-3, f"{what}: rel-L2 {rel:.3e} > 5e-3"
     assert mx <= bound, f"{what}: max abs {mx:.3e} > {bound:.3e}"
     return rel, mx
