@@ -75,9 +75,6 @@ constexpr int kAPre = MOE_PRESCALED_APRE;    // A fragments in flight per group 
 #ifndef MOE_PRESCALED_WPE
 #define MOE_PRESCALED_WPE 4
 #endif
-#ifndef MOE_PRESCALED_SWP
-#define MOE_PRESCALED_SWP 0
-#endif
 #ifndef MOE_PRESCALED_ASLOTS
 #define MOE_PRESCALED_ASLOTS MOE_PRESCALED_DEPTH
 #endif
@@ -118,18 +115,6 @@ __device__ __forceinline__ f16x8_t dequant_int4_f16(uint32_t w, f16x2_t s2) {
   const f16x2_t p3 = (as_f16x2((t & m1) | c1) + as_f16x2(o1)) * s2;
   return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
                                  __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// One quarter of dequant_int4_f16: codes k (bits [4k, 4k+4) of each half of
-// w >> (k < 2 ? 0 : 8)... written as the two values fp16(q * s2) of piece k.
-__device__ __forceinline__ f16x2_t dequant_int4_piece(uint32_t w, f16x2_t s2, int k) {
-  uint32_t m = (k & 1) ? 0x00F000F0u : 0x000F000Fu, c = (k & 1) ? 0x54005400u : 0x64006400u;
-  uint32_t o = (k & 1) ? 0xD480D480u : 0xE408E408u;
-  asm("" : "+s"(m));
-  asm("" : "+v"(c));
-  asm("" : "+s"(o));
-  const uint32_t src = k < 2 ? w : (w >> 8);
-  return (as_f16x2((src & m) | c) + as_f16x2(o)) * s2;
 }
 
 // ---------------------------------------------------------------------------
@@ -419,57 +404,6 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
       s1lo = as_f16x2(w.s1.x) * m21;
       s1hi = as_f16x2(w.s1.y) * m21;
     }
-#if MOE_PRESCALED_SWP
-    if constexpr (kFmt == kFmtInt4) {
-      // Software-pipelined: the codes of group g + 1 are widened between the
-      // MFMAs of group g (two B buffers), and the A fragments run in one ring
-      // across the chunk's groups.
-      auto gscale = [&](int g, int t) {
-        const f16x2_t v = t == 0 ? (g < 2 ? s0lo : s0hi) : (g < 2 ? s1lo : s1hi);
-        return (g & 1) ? __builtin_shufflevector(v, v, 1, 1) : __builtin_shufflevector(v, v, 0, 0);
-      };
-      constexpr int NF = 4 * S;
-      auto rd = [&](int f) {
-        return __builtin_bit_cast(f16x8_t, xs.x[slot][aoff(f / S) + (f % S) * kTileRows * kBVecs]);
-      };
-      f16x8_t ar[kAPre];
-#pragma unroll
-      for (int p = 0; p + 1 < kAPre; ++p) ar[p] = rd(p);
-      f16x8_t b0 = dequant_int4_f16(q0[0], gscale(0, 0));
-      f16x8_t b1 = dequant_int4_f16(q1[0], gscale(0, 1));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f16x2_t bn[8];
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const int f = g * S + s;
-          if (f + kAPre - 1 < NF) ar[(f + kAPre - 1) % kAPre] = rd(f + kAPre - 1);
-          const f16x8_t xv = ar[f % kAPre];
-          if constexpr (kFc1) {
-            acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b0, xv, acc0[s], 0, 0, 0);
-            acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1, xv, acc1[s], 0, 0, 0);
-          } else {
-            acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b0, acc0[s], 0, 0, 0);
-            acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, b1, acc1[s], 0, 0, 0);
-          }
-          if (g < 3) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              if ((i * S) / 8 == s) bn[i] = dequant_int4_piece(i < 4 ? q0[g + 1] : q1[g + 1], gscale(g + 1, i / 4), i & 3);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (g < 3) {
-          b0 = __builtin_shufflevector(__builtin_shufflevector(bn[0], bn[1], 0, 1, 2, 3),
-                                       __builtin_shufflevector(bn[2], bn[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-          b1 = __builtin_shufflevector(__builtin_shufflevector(bn[4], bn[5], 0, 1, 2, 3),
-                                       __builtin_shufflevector(bn[6], bn[7], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      }
-      return;
-    }
-#endif
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       if constexpr (kFmt == kFmtInt4) {
