@@ -57,10 +57,15 @@ namespace moe {
 namespace MOE_FMT_NS {
 namespace {
 
-constexpr int kBW = 8;                       // waves (= tile pairs) per workgroup
+#ifndef MOE_PRESCALED_WAVES
+#define MOE_PRESCALED_WAVES 8
+#endif
+constexpr int kBW = MOE_PRESCALED_WAVES;     // waves (= tile pairs) per workgroup
 constexpr int kBVecs = kChunkK / 8;          // 16-byte vectors of a row's chunk slice
 constexpr int kBMaxRows = prescaled_max_rows(kFmt);   // 96 (INT4) or 128 (MXFP4)
-constexpr int kBSlotVecs = kBMaxRows * kBVecs;         // one LDS slot: up to 128 rows x 16 vectors
+constexpr int kCopyRows = 4 * kBW;                      // A rows one copy round of the workgroup covers
+constexpr int kBSlotRows = (kBMaxRows + kCopyRows - 1) / kCopyRows * kCopyRows;  // whole rounds
+constexpr int kBSlotVecs = kBSlotRows * kBVecs;         // one LDS slot: up to 128 rows x 16 vectors
 constexpr int kBXcds = 8;
 constexpr int kBWLoads = 4;                  // vector loads per weight chunk (2 tiles' codes + scales)
 #ifndef MOE_PRESCALED_APRE
@@ -291,8 +296,8 @@ __device__ __forceinline__ void prescaled_epilogue_fc2(const FcArgs& a, const in
 template <int S, bool kFc1, int kPolicy>
 __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, const int pair, const int row0,
                                               const int nsub, const XSlots xs, uint32_t* xoffs) {
-  constexpr int kD = (S + 1) / 2;  // 1 KB copies per wave per chunk (32 rows per round of 8 waves)
-  static_assert(S >= 1 && 2 * kD * kTileRows <= kBMaxRows, "the copies fit the slot");
+  constexpr int kD = (S * kTileRows + kCopyRows - 1) / kCopyRows;  // 1 KB copies per wave per chunk
+  static_assert(S >= 1 && kD * kCopyRows <= kBSlotRows, "the copies fit the slot");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = kFc1 ? a.H : a.I;
@@ -336,7 +341,7 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
   const uint32_t rid0 = a_row<kFc1>(rows[0], a.k);
   // The per-lane source offsets are kept in LDS (this thread's kD words),
   // not in registers: they are needed only while the copies are issued.
-  uint32_t* myoff = xoffs + tid * (kBMaxRows / kTileRows / 2);
+  uint32_t* myoff = xoffs + tid * (kBSlotRows / kCopyRows);
 #pragma unroll
   for (int i = 0; i < kD; ++i) {
     const int r = 4 * (wave + kBW * i) + (lane >> 4);
@@ -522,7 +527,7 @@ void fc_prescaled_kernel(FcArgs a) {
   xs.x[1] = xt1;
   if constexpr (kASlots > 2) xs.x[2] = xt2;
   if constexpr (kASlots > 3) xs.x[3] = xt3;
-  __shared__ uint32_t xoffs[64 * kBW * (kBMaxRows / kTileRows / 2)];  // each thread's copy source offsets
+  __shared__ uint32_t xoffs[64 * kBW * (kBSlotRows / kCopyRows)];  // each thread's copy source offsets
   constexpr int kThreads = 64 * kBW;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
