@@ -426,11 +426,11 @@ class Bench:
         bw = 2 * src.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         acc = torch.empty((), dtype=torch.float32, device="cuda")
         for _ in range(3):
-            torch.sum(src, out=acc)
+            torch.sum(src, dim=0, out=acc)
         torch.cuda.synchronize()
         e0.record()
         for _ in range(10):
-            torch.sum(src, out=acc)
+            torch.sum(src, dim=0, out=acc)
         e1.record()
         torch.cuda.synchronize()
         rd = src.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
