@@ -21,7 +21,7 @@ TILED = [
     # (shape, M, bias sigma, weight seed, token seed)
     (SMALL, 64, 0.0, 11, 12),    # 16 assignments per expert: tiles of 1-2 sub-tiles
     (SMALL, 128, 0.0, 11, 17),   # 32 per expert: tiles of 2-3 sub-tiles
-    (SMALL, 300, 0.0, 11, 13),   # ~75 per expert: 5-sub-tile tiles (run as 6), two tiles with 64-row blocks
+    (SMALL, 300, 0.0, 11, 13),   # ~75 per expert: 5- and 6-sub-tile tiles, two tiles with 64-row blocks
     (SMALL, 700, 2.0, 11, 14),   # skewed: several full tiles on the hot experts
     (WIDER, 320, 1.0, 15, 16),   # 40 per expert, mildly skewed
 ]
@@ -45,10 +45,29 @@ def test_tiled_full_parity(case, block_m):
     assert_output_close(out, ref, f"tiled {shape} M={M} B={block_m}")
 
 
+@pytest.mark.parametrize("block_m", [16, 32, 64])
+def test_tiled_at_the_size_limits(block_m):
+    """1024 experts (the largest E) with top-16 (the largest k) at 16
+    assignments per expert: the pre-scaled kernel with 1024 experts' tiles;
+    every element of 12 token rows (173 of the experts) against the oracle."""
+    shape = wl.LayerShape(E=1024, H=256, I=256, k=16)
+    M = 1024
+    assert M * shape.k / shape.E >= 16
+    layer = device_layer(shape, 21)
+    t = wl.tokens(shape, M, 22, 0.0)
+    rb, out = run_layer(layer, t.logits, t.x_bits, block_m)
+    ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, block_m)
+    rows = list(range(0, M, M // 12))[:12]
+    x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)
+    ref = oracle.moe_forward(x, ids, w, oracle_experts(shape, 21), tokens_subset=rows)
+    assert np.all(np.isfinite(out))
+    print(f"size limits B={block_m}: experts covered {np.unique(ids[rows]).size}/{np.unique(ids).size}", flush=True)
+    assert_output_close(out[rows], ref[rows], f"E=1024 k=16 M={M} B={block_m}")
+
+
 def test_tiled_skew_has_multi_tile_experts():
     """The skewed case really exercises experts with several full 96-row tiles
-    and partial last tiles with an odd sub-tile count (run with one empty
-    sub-tile)."""
+    and partial last tiles with an odd sub-tile count."""
     shape, M, sigma, _, tseed = TILED[3]
     t = wl.tokens(shape, M, tseed, sigma)
     ids, _ = oracle.route(t.logits, shape.k)
