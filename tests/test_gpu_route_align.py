@@ -76,7 +76,7 @@ def test_deterministic_integers():
     lg = to_dev(t.logits)
     moe.route_align(lg, rb)
     first = route_host(rb)
-    for _ in range(50):
+    for _ in range(100):
         rb.sorted_token_ids.fill_(-7)
         moe.route_align(lg, rb)
         again = route_host(rb)
