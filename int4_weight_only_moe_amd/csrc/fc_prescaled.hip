@@ -176,113 +176,98 @@ __global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restri
 __device__ __forceinline__ f16x2_t pow2_pair(int sigma0, int sigma1) {
   return f16x2_t{(_Float16)__builtin_ldexpf(1.0f, -sigma0), (_Float16)__builtin_ldexpf(1.0f, -sigma1)};
 }
-// The shifts of this lane's two weight rows (column lane % 16 of each tile of
-// the pair) in the sigma trailer of expert e.
-template <bool kFc1>
-__device__ __forceinline__ void row_sigmas(const FcArgs& a, int e, int pair, int lane, int& sig0, int& sig1) {
-  const int N = kFc1 ? 2 * a.I : a.H;
-  const int r = lane & 15;
-  const int64_t n0 = kFc1 ? 16 * pair + r : 32 * pair + r;
-  const int64_t n1 = kFc1 ? a.I + 16 * pair + r : 32 * pair + 16 + r;
-  sig0 = a.wsigma[(int64_t)e * N + n0];
-  sig1 = a.wsigma[(int64_t)e * N + n1];
-}
 
 // The row id an A row of the tile reads: its token (FC1) or assignment (FC2).
 template <bool kFc1>
 __device__ __forceinline__ uint32_t a_row(int f, int k) { return (uint32_t)(kFc1 ? f / k : f); }
 
-// Epilogues of the tile pair. INT4 scales each output by 2^(row exponent +
-// sigma of its weight row). Per sub-tile, lane L first derives what belongs
-// to its own A row (L % 16): the row's token, exponent and, for FC2, routing
-// weight (one load each, issued together).
+// What the epilogues need of each row of the tile, gathered into LDS while
+// the workgroup's first chunks are in flight (rather than loaded after the
+// main loop): the output offset (FC1: f * I into act; FC2: token * H into
+// the accumulator; -1 for a padding row), FC2's routing weight and, for INT4,
+// the A row's exponent.
+struct TileRows {
+  int32_t dst[kBSlotRows];
+  float w[kBSlotRows];
+  int32_t ex[kBSlotRows];
+};
+// INT4: the shifts of each wave's weight rows, per tile of its pair.
+typedef int8_t PairSigmas[kBW][2][kTileRows];
+
+// Epilogues of a tile pair. INT4 scales each output by 2^(row exponent +
+// sigma of its weight row).
 //
 // FC1 multiplies with the operands swapped (the weights as the first MFMA
 // operand), so the accumulators hold D transposed: lane L has A row L % 16
 // and output columns 4 (L / 16) .. +3, and writes its 4 SiLU(gate) * up
 // values as one 8-byte store.
 template <int S>
-__device__ __forceinline__ void prescaled_epilogue_fc1(const FcArgs& a, const int e, const int pair,
-                                                       const int (&frow)[S], const int nsub, const f32x4_t (&acc0)[S],
-                                                       const f32x4_t (&acc1)[S], const int lane) {
-  const int MK = a.M * a.k;
+__device__ __forceinline__ void prescaled_epilogue_fc1(const FcArgs& a, const int pair, const int nsub,
+                                                       const f32x4_t (&acc0)[S], const f32x4_t (&acc1)[S],
+                                                       const int lane, const TileRows& tr,
+                                                       const int8_t (&sg)[2][kTileRows]) {
   const int c0 = 4 * (lane >> 4);
   int sg0[4] = {0, 0, 0, 0}, sg1[4] = {0, 0, 0, 0};
   if constexpr (kFmt == kFmtInt4) {
-    const int8_t* sig = a.wsigma + (int64_t)e * (2 * a.I) + 16 * pair + c0;
-    const uint32_t d0 = *reinterpret_cast<const uint32_t*>(sig);
-    const uint32_t d1 = *reinterpret_cast<const uint32_t*>(sig + a.I);
+    const uint32_t d0 = *reinterpret_cast<const uint32_t*>(&sg[0][c0]);
+    const uint32_t d1 = *reinterpret_cast<const uint32_t*>(&sg[1][c0]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sg0[i] = (int)(int8_t)(d0 >> (8 * i));
       sg1[i] = (int)(int8_t)(d1 >> (8 * i));
     }
   }
-  int ex[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const int f = frow[s];
-    ex[s] = 0;
-    if constexpr (kFmt == kFmtInt4)
-      if (s < nsub && f >= 0 && f < MK) ex[s] = a.row_exp[f / a.k];
-  }
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int f = frow[s];
-    if (s >= nsub || f < 0 || f >= MK) continue;
+    if (s >= nsub) continue;
+    const int r = kTileRows * s + (lane & 15);
+    const int dst = tr.dst[r];
+    if (dst < 0) continue;
+    const int ex = kFmt == kFmtInt4 ? tr.ex[r] : 0;
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float g = acc0[s][i], u = acc1[s][i];
       if constexpr (kFmt == kFmtInt4) {
-        g = __builtin_ldexpf(g, ex[s] + sg0[i]);
-        u = __builtin_ldexpf(u, ex[s] + sg1[i]);
+        g = __builtin_ldexpf(g, ex + sg0[i]);
+        u = __builtin_ldexpf(u, ex + sg1[i]);
       }
       // SiLU(g) * u; the reciprocal's rounding is far below the bf16 store's
       o[i] = f32_to_bf16_bits(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u);
     }
-    *reinterpret_cast<uint2*>(a.act_out + (uint32_t)(f * a.I + 16 * pair + c0)) =
+    *reinterpret_cast<uint2*>(a.act_out + (uint32_t)(dst + 16 * pair + c0)) =
         make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
   }
 }
 
-// FC2: lane L has rows 4 (L / 16) + i and output column L % 16 of each tile;
-// the per-row values come from the owning lane by a shuffle.
+// FC2: lane L has rows 4 (L / 16) + i and output column L % 16 of each tile.
 template <int S>
-__device__ __forceinline__ void prescaled_epilogue_fc2(const FcArgs& a, const int e, const int pair,
-                                                       const int (&frow)[S], const int nsub, const f32x4_t (&acc0)[S],
-                                                       const f32x4_t (&acc1)[S], const int lane) {
-  const int MK = a.M * a.k;
+__device__ __forceinline__ void prescaled_epilogue_fc2(const FcArgs& a, const int pair, const int nsub,
+                                                       const f32x4_t (&acc0)[S], const f32x4_t (&acc1)[S],
+                                                       const int lane, const TileRows& tr,
+                                                       const int8_t (&sg)[2][kTileRows]) {
   const int col = lane & 15;
-  int sig0 = 0, sig1 = 0;  // read again here rather than kept live across the main loop
-  if constexpr (kFmt == kFmtInt4) row_sigmas<false>(a, e, pair, lane, sig0, sig1);
-  int off[S], ex[S];
-  float w[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int f = frow[s];
-    const bool ok = s < nsub && f >= 0 && f < MK;
-    off[s] = ok ? (f / a.k) * a.H + kPairRows * pair : -1;  // < M * H < 2^31
-    w[s] = ok ? a.topk_weights[f] : 0.0f;
-    ex[s] = 0;
-    if constexpr (kFmt == kFmtInt4) ex[s] = ok ? a.row_exp[f] : 0;
+  int sig0 = 0, sig1 = 0;
+  if constexpr (kFmt == kFmtInt4) {
+    sig0 = sg[0][col];
+    sig1 = sg[1][col];
   }
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     if (s >= nsub) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int src = 4 * (lane >> 4) + i;
-      const int o = __shfl(off[s], src, 64);
+      const int r = kTileRows * s + 4 * (lane >> 4) + i;
+      const int o = tr.dst[r];
       if (o < 0) continue;
-      const float wt = __shfl(w[s], src, 64);
+      const float wt = tr.w[r];
       float v0 = acc0[s][i], v1 = acc1[s][i];
       if constexpr (kFmt == kFmtInt4) {
-        const int x = __shfl(ex[s], src, 64);
+        const int x = tr.ex[r];
         v0 = __builtin_ldexpf(v0, x + sig0);
         v1 = __builtin_ldexpf(v1, x + sig1);
       }
-      float* dst = a.acc + (uint32_t)o;
+      float* dst = a.acc + (uint32_t)(o + kPairRows * pair);  // < M * H < 2^31
       unsafeAtomicAdd(dst + col, wt * v0);
       unsafeAtomicAdd(dst + 16 + col, wt * v1);
     }
@@ -290,12 +275,12 @@ __device__ __forceinline__ void prescaled_epilogue_fc2(const FcArgs& a, const in
 }
 
 // One workgroup's tile (rows row0 .. row0 + 16 * nsub of the sorted list,
-// expert e) times this wave's tile pair; S >= nsub sub-tiles (S even: each
-// wave copies S / 2 KB of every chunk to LDS), weights under cache policy
-// kPolicy.
+// expert e) times this wave's tile pair; S >= nsub sub-tiles, weights under
+// cache policy kPolicy.
 template <int S, bool kFc1, int kPolicy>
 __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, const int pair, const int row0,
-                                              const int nsub, const XSlots xs, uint32_t* xoffs) {
+                                              const int nsub, const XSlots xs, uint32_t* xoffs, TileRows& tr,
+                                              PairSigmas& psig) {
   constexpr int kD = (S * kTileRows + kCopyRows - 1) / kCopyRows;  // 1 KB copies per wave per chunk
   static_assert(S >= 1 && kD * kCopyRows <= kBSlotRows, "the copies fit the slot");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -322,13 +307,30 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
     return w;
   };
   WChunk wb[kDepth];
+  // The first kDepth weight chunks do not depend on the tile's rows: they go
+  // out before the row ids are read.
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) wb[d] = load_w(d);
 
-  // 2^-sigma of this lane's two weight rows (column lane % 16 of each tile).
-  f16x2_t m2 = {(_Float16)1.0f, (_Float16)1.0f};
+  // The row ids: those of the A rows this lane copies and, for thread
+  // t < 16 S, row t's for the epilogues. Indices are clamped into the tile so
+  // that the loads are unconditional and go out together.
+  const int last = kTileRows * nsub - 1;
+  int fr[kD];
+#pragma unroll
+  for (int i = 0; i < kD; ++i) {
+    const int r = 4 * (wave + kBW * i) + (lane >> 4);
+    fr[i] = rows[r < last ? r : last];
+  }
+  const int rf0 = rows[tid < last ? tid : last];
+  // INT4: the shifts of this wave's weight rows, lane l < 32: tile l / 16,
+  // row l % 16 (FC1: gate column 16 pair + r, up column I + 16 pair + r;
+  // FC2: row 32 pair + 16 t + r).
+  int8_t sgv = 0;
   if constexpr (kFmt == kFmtInt4) {
-    int sig0, sig1;
-    row_sigmas<kFc1>(a, e, pair, lane, sig0, sig1);
-    m2 = pow2_pair(sig0, sig1);
+    const int t = (lane / kTileRows) & 1, r = lane & (kTileRows - 1);
+    const int nrow = kFc1 ? (t ? a.I : 0) + kTileRows * pair + r : kPairRows * pair + kTileRows * t + r;
+    sgv = a.wsigma[(int64_t)e * N + nrow];
   }
 
   // A rows: copy i of this wave covers LDS rows 4 * (wave + 8i) .. +3 of a
@@ -345,10 +347,20 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
 #pragma unroll
   for (int i = 0; i < kD; ++i) {
     const int r = 4 * (wave + kBW * i) + (lane >> 4);
-    const int f = r < kTileRows * nsub ? rows[r] : MK;
+    const int f = r <= last ? fr[i] : MK;
     const uint32_t rid = (f >= 0 && f < MK) ? a_row<kFc1>(f, a.k) : rid0;
     const uint32_t v = (uint32_t)((lane & 15) ^ (r & 15));
     myoff[i] = (rid * (uint32_t)K + 8u * v) * 2u;
+  }
+  // The epilogue's row data (two more loads for thread t < 16 S), stored to
+  // LDS before the prologue's barrier.
+  const int rf = tid <= last ? rf0 : MK;
+  int rdst = -1, rex = 0;
+  float rw = 0.f;
+  if (tid < kTileRows * S && rf >= 0 && rf < MK) {
+    rdst = kFc1 ? rf * a.I : (rf / a.k) * a.H;  // < M * k * I, M * H < 2^31
+    if constexpr (!kFc1) rw = a.topk_weights[rf];
+    if constexpr (kFmt == kFmtInt4) rex = a.row_exp[kFc1 ? rf / a.k : rf];
   }
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   auto copy_rows = [&](int c, int slot) {
@@ -376,27 +388,33 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
   }
 
   // Chunk step c issues the rows of chunk c + kASlots - 1 into LDS, computes
-  // chunk c, then loads the weights of chunk c + kDepth; the prologue is the
-  // steps before chunk 0 without their compute, so that the same wait holds
-  // after every step: the rows and weights of the next chunk have arrived,
-  // the newer loads may stay in flight (kVmAfter of them: those issued after
-  // the later of the two).
+  // chunk c, then loads the weights of chunk c + kDepth, and waits until the
+  // rows and weights of chunk c + 1 have arrived: the newer loads may stay in
+  // flight (kVmAfter of them: those issued after the later of the two). The
+  // prologue has issued the weights of chunks 0 .. kDepth - 1, then issues
+  // the rows of chunks 0 .. kASlots - 2 and waits for those of chunk 0.
   constexpr int kAfterW = (kDepth - 1) * (kD + kBWLoads);
   constexpr int kAfterRows = kBWLoads + (kASlots - 2) * (kD + kBWLoads);
   constexpr int kVmAfter = kAfterW < kAfterRows ? kAfterW : kAfterRows;
   static_assert(kVmAfter < 64, "vmcnt holds at most 63");
-  constexpr int kPro = kASlots - 1 > kDepth ? kASlots - 1 : kDepth;
-#pragma unroll
-  for (int c = -kPro; c < 0; ++c) {
-    __builtin_amdgcn_sched_barrier(0);
-    if (c + kASlots - 1 >= 0) copy_rows(c + kASlots - 1, (c + kASlots - 1) % kASlots);
-    __builtin_amdgcn_sched_barrier(0);
-    if (c + kDepth >= 0) wb[c + kDepth] = load_w(c + kDepth);
-  }
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(kVmAfter, 0));
+#pragma unroll
+  for (int c = 0; c + 1 < kASlots; ++c) copy_rows(c, c);
+  __builtin_amdgcn_sched_barrier(0);
+  if (tid < kTileRows * S) {
+    tr.dst[tid] = rdst;
+    tr.w[tid] = rw;
+    tr.ex[tid] = rex;
+  }
+  if constexpr (kFmt == kFmtInt4)
+    if (lane < 2 * kTileRows) (&psig[wave][0][0])[lane] = sgv;
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm((kASlots - 2) * kD, 0));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
+
+  // 2^-sigma of this lane's two weight rows (column lane % 16 of each tile).
+  f16x2_t m2 = {(_Float16)1.0f, (_Float16)1.0f};
+  if constexpr (kFmt == kFmtInt4) m2 = pow2_pair(psig[wave][0][lane & 15], psig[wave][1][lane & 15]);
 
   auto compute = [&](const WChunk& w, int slot) {
     const uint32_t q0[4] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w};
@@ -491,23 +509,20 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
   // no copy into LDS may outlive the workgroup
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
-  int frow[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) frow[s] = s < nsub ? rows[kTileRows * s + (lane & 15)] : MK;
   if constexpr (kFc1)
-    prescaled_epilogue_fc1<S>(a, e, pair, frow, nsub, acc0, acc1, lane);
+    prescaled_epilogue_fc1<S>(a, pair, nsub, acc0, acc1, lane, tr, psig[wave]);
   else
-    prescaled_epilogue_fc2<S>(a, e, pair, frow, nsub, acc0, acc1, lane);
+    prescaled_epilogue_fc2<S>(a, pair, nsub, acc0, acc1, lane, tr, psig[wave]);
 }
 
 template <int S, bool kFc1>
 __device__ __forceinline__ void prescaled_policy(const FcArgs& a, const int e, const int pair, const int row0,
                                                 const int nsub, const bool reuse, const XSlots xs,
-                                                uint32_t* xoffs) {
+                                                uint32_t* xoffs, TileRows& tr, PairSigmas& psig) {
   if (reuse)
-    prescaled_body<S, kFc1, kPolicyDefault>(a, e, pair, row0, nsub, xs, xoffs);
+    prescaled_body<S, kFc1, kPolicyDefault>(a, e, pair, row0, nsub, xs, xoffs, tr, psig);
   else
-    prescaled_body<S, kFc1, kPolicyWeights>(a, e, pair, row0, nsub, xs, xoffs);
+    prescaled_body<S, kFc1, kPolicyWeights>(a, e, pair, row0, nsub, xs, xoffs, tr, psig);
 }
 
 template <bool kFc1>
@@ -528,6 +543,8 @@ void fc_prescaled_kernel(FcArgs a) {
   if constexpr (kASlots > 2) xs.x[2] = xt2;
   if constexpr (kASlots > 3) xs.x[3] = xt3;
   __shared__ uint32_t xoffs[64 * kBW * (kBSlotRows / kCopyRows)];  // each thread's copy source offsets
+  __shared__ TileRows tr;
+  __shared__ PairSigmas psig;
   constexpr int kThreads = 64 * kBW;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -560,16 +577,16 @@ void fc_prescaled_kernel(FcArgs a) {
 
   // exactly the tile's sub-tiles are multiplied
   switch (nsub) {
-    case 1: prescaled_policy<1, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
-    case 2: prescaled_policy<2, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
-    case 3: prescaled_policy<3, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
-    case 4: prescaled_policy<4, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
-    case 5: prescaled_policy<5, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
-    case 6: prescaled_policy<6, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs); break;
+    case 1: prescaled_policy<1, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
+    case 2: prescaled_policy<2, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
+    case 3: prescaled_policy<3, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
+    case 4: prescaled_policy<4, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
+    case 5: prescaled_policy<5, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
+    case 6: prescaled_policy<6, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
     default:
       if constexpr (kBMaxRows >= 128) {
-        if (nsub == 7) prescaled_policy<7, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
-        else prescaled_policy<8, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs);
+        if (nsub == 7) prescaled_policy<7, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig);
+        else prescaled_policy<8, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig);
       }
   }
 }
