@@ -215,16 +215,22 @@ void fc1_decode_kernel(DecodeArgs d) {
   float* xcorr = reinterpret_cast<float*>(xcorr4);
   const uint4* xg = reinterpret_cast<const uint4*>(d.fc.act_in);
 
-  // The x loads do not depend on the routing: issue them first.
+  // One token: the logits go out first (the routing is the critical path),
+  // then the x loads, which do not depend on the routing.
+  float lg[VPL];
+  if constexpr (MR == 1) topk_load<VPL>(d.logits, E, lg);
   constexpr bool kEarly = NCH > 0 && MR <= kXEarlyRows;
   uint4 xr[MR][kXPerThread];
   if constexpr (kEarly) {
+    // unconditional (indices past the row read its last vector, which the
+    // staging does not store): as a conditional load each would be waited for
+    // where its branch joins, before the routing
 #pragma unroll
     for (int r = 0; r < MR; ++r)
 #pragma unroll
       for (int v = 0; v < kXPerThread; ++v) {
         const int i = threadIdx.x + v * 64 * kDecKSplit;
-        xr[r][v] = (i < hv) ? xg[(int64_t)r * hv + i] : make_uint4(0, 0, 0, 0);
+        xr[r][v] = xg[(int64_t)r * hv + (i < hv ? i : hv - 1)];
       }
   }
 
@@ -320,7 +326,11 @@ void fc1_decode_kernel(DecodeArgs d) {
     // the other slots; wave 0 of workgroup 0 routes completely (the routing
     // outputs).
     const bool full = blockIdx.x == 0 && wave == 0;
-    const int eb = topk_route<VPL>(d.logits, 0, E, k, full ? k : blk + 1, blk, full ? sh.ids : nullptr, sh.w);
+    uint32_t key[VPL];
+    topk_keys_of<VPL>(lg, E, key);
+    const int rounds = full ? k : blk + 1;
+    __builtin_assume(rounds >= 1);  // else the logits loads are sunk below the x loads, into the rounds' branch
+    const int eb = topk_route_keys<VPL>(key, 0, k, rounds, blk, full ? sh.ids : nullptr, sh.w);
     const int tokf = lane == 0 ? blk : -1;
     fc1_decode_body<MR, NCH>(d, xs, row16, xcorr4, eb, pair, tokf, wave, lane, [&]() {
       stage();

@@ -104,15 +104,30 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 }
 
 // One wave's routing state for a token: lane l holds the order keys of
-// experts l, l+64, ... (VPL of them); 0 = absent or already taken.
+// experts l, l+64, ... (VPL of them); 0 = absent or already taken. The VPL
+// loads are unconditional (indices past E read expert E - 1, then drop it),
+// so they go out together: as conditional loads each became a branch with a
+// wait for every load in flight, VPL round trips one after another.
 template <int VPL>
-__device__ __forceinline__ void topk_keys(const float* __restrict__ row, int E, uint32_t (&key)[VPL]) {
+__device__ __forceinline__ void topk_load(const float* __restrict__ row, int E, float (&x)[VPL]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = v * 64 + lane;
-    key[v] = (e < E) ? order_key(row[e]) : 0u;
+    x[v] = row[e < E ? e : E - 1];
   }
+}
+template <int VPL>
+__device__ __forceinline__ void topk_keys_of(const float (&x)[VPL], int E, uint32_t (&key)[VPL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) key[v] = (v * 64 + lane < E) ? order_key(x[v]) : 0u;
+}
+template <int VPL>
+__device__ __forceinline__ void topk_keys(const float* __restrict__ row, int E, uint32_t (&key)[VPL]) {
+  float x[VPL];
+  topk_load<VPL>(row, E, x);
+  topk_keys_of<VPL>(x, E, key);
 }
 
 // Takes the largest remaining key (equal keys: the lower expert index) and
@@ -157,13 +172,12 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // routing is complete (rounds = k) and lanes < k write expert and weight of
 // their slot: weights = softmax over the k kept logits. (Each wave that
 // needs only slot s stops after s + 1 takes.)
+// The keys may be passed in (topk_keys or topk_load + topk_keys_of of row t).
 template <int VPL>
-__device__ __forceinline__ int topk_route(const float* __restrict__ logits, int t, int E, int k, int rounds,
-                                          int slot, int32_t* __restrict__ out_ids, float* __restrict__ out_w,
-                                          int32_t* ids_copy = nullptr) {
+__device__ __forceinline__ int topk_route_keys(uint32_t (&key)[VPL], int t, int k, int rounds, int slot,
+                                               int32_t* __restrict__ out_ids, float* __restrict__ out_w,
+                                               int32_t* ids_copy = nullptr) {
   const int lane = threadIdx.x & 63;
-  uint32_t key[VPL];
-  topk_keys<VPL>(logits + (int64_t)t * E, E, key);
   uint32_t my_key = 0;
   int my_e = 0, e_slot = 0;
   for (int r = 0; r < rounds; ++r) {
@@ -186,6 +200,14 @@ __device__ __forceinline__ int topk_route(const float* __restrict__ logits, int 
     }
   }
   return e_slot;
+}
+template <int VPL>
+__device__ __forceinline__ int topk_route(const float* __restrict__ logits, int t, int E, int k, int rounds,
+                                          int slot, int32_t* __restrict__ out_ids, float* __restrict__ out_w,
+                                          int32_t* ids_copy = nullptr) {
+  uint32_t key[VPL];
+  topk_keys<VPL>(logits + (int64_t)t * E, E, key);
+  return topk_route_keys<VPL>(key, t, k, rounds, slot, out_ids, out_w, ids_copy);
 }
 
 // One wave routes token t completely: topk_ids / topk_w [t*k + j] for j < k.
