@@ -260,17 +260,24 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
   // All of the block's metadata is read in one round trip (the block list
   // entries of the neighbours too, for the cache policy below) before any
   // of it is used.
+  // The loads are unconditional (indices clamped into range, the value then
+  // dropped): a conditional load becomes a branch with a wait for every load
+  // in flight.
   const int32_t* rows = a.sorted_ids + (int64_t)blk * BM;
   int frow[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) frow[s] = rows[16 * s + (lane & 15)];
   const bool stager = tid < kItems;
   const int srow = tid / kRowVecs, svec = tid % kRowVecs;
-  const int sf = stager ? rows[srow] : MK;
+  const int sf0 = rows[stager ? srow : 0];
+  const bool has_next = (int64_t)(blk + 1) * BM < a.cap;
   const int npp = __builtin_amdgcn_readfirstlane(*a.npp);
   const int e = __builtin_amdgcn_readfirstlane(a.block_expert[blk]);
-  const int e_prev = blk > 0 ? __builtin_amdgcn_readfirstlane(a.block_expert[blk - 1]) : -1;
-  const int e_next = (int64_t)(blk + 1) * BM < a.cap ? __builtin_amdgcn_readfirstlane(a.block_expert[blk + 1]) : -1;
+  const int e_prev0 = __builtin_amdgcn_readfirstlane(a.block_expert[blk > 0 ? blk - 1 : blk]);
+  const int e_next0 = __builtin_amdgcn_readfirstlane(a.block_expert[has_next ? blk + 1 : blk]);
+  const int sf = stager ? sf0 : MK;
+  const int e_prev = blk > 0 ? e_prev0 : -1;
+  const int e_next = has_next ? e_next0 : -1;
   if (blk * BM >= npp) return;
   if (e < 0 || e >= a.E) return;
 
