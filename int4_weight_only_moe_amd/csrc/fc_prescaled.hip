@@ -31,7 +31,7 @@
 //   * tiles of up to 96 rows of one expert for INT4 (64 with 64-row blocks),
 //     128 for MXFP4: one tile pair per
 //     wave, 8 waves per workgroup, two workgroups per CU (four waves per
-//     SIMD, <= 128 VGPRs, 54 or 72 KB of LDS each): while one workgroup waits
+//     SIMD, <= 128 VGPRs, 56 or 74 KB of LDS each): while one workgroup waits
 //     at a barrier or runs its epilogue, the other keeps the matrix core busy
 //     (INT4's widened fp16 codes leave registers for 6 sub-tiles, MXFP4's for 8);
 //   * the tile's activation chunk (up to 128 rows x 128 channels) is copied
@@ -42,6 +42,10 @@
 //   * per 32-channel group a wave widens both tiles' codes once and runs
 //     2 x S MFMAs (S = the tile's sub-tiles of 16 rows, at most 6, or 8 for
 //     MXFP4: padding sub-tiles are not multiplied);
+//   * a workgroup's start costs one memory round trip: the first weight
+//     chunks go out before the tile's row ids (they do not depend on them),
+//     the row ids in one batch, and what the epilogue needs of each row
+//     lands in LDS while the first chunks are in flight;
 //   * per chunk step: the next chunk's rows go to LDS, the current chunk is
 //     computed, the weight chunk after next is loaded, then one wait (the
 //     rows and the next weight chunk; the newest weight loads stay in flight)
