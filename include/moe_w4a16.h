@@ -341,6 +341,31 @@ int moe_mxfp4_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
                     void* workspace, int64_t workspace_bytes, uint16_t* out_bf16, void* stream,
                     void* const* stage_events);
 
+/* Measurement helpers (not part of the layer). They measure what this GPU
+ * sustains, so that a layer kernel's rate can be stated as a fraction of the
+ * attainable rate as well as of the published peaks ("The Throughput Lever",
+ * section "The Result: Two Regimes", judges the layer by its fraction of the
+ * memory bandwidth).
+ *
+ * moe_calib_read_granule (host): the byte multiple moe_calib_hbm_read reads
+ *   (131072).
+ * moe_calib_hbm_read: reads `bytes` of `buf` once (non-temporal 16-byte loads,
+ *   `workgroups` workgroups of 256 threads; each thread writes the XOR of the
+ *   32-bit words it read to sink[workgroup * 256 + thread], so the XOR of the
+ *   whole sink is the XOR of every word of the buffer). bytes > 0, a multiple
+ *   of the granule; buf 16-byte and sink 4-byte aligned; sink holds
+ *   workgroups * 256 words; 1 <= workgroups <= 2^20. MOE_ERR_INVALID_ARG
+ *   otherwise (nothing launched).
+ * moe_calib_mfma_f16: `workgroups` workgroups of 4 waves each issue
+ *   iters * 8 v_mfma_f32_16x16x32_f16 on register operands (16384 flops
+ *   each; operand values are a fixed hash of lane, element and operand
+ *   index). Each thread writes the sum of its accumulators to
+ *   sink[workgroup * 256 + thread] (workgroups * 256 floats). iters >= 0;
+ *   1 <= workgroups <= 2^20; sink 4-byte aligned. */
+int64_t moe_calib_read_granule(void);
+int moe_calib_hbm_read(const void* buf, int64_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
+int moe_calib_mfma_f16(int64_t iters, int32_t workgroups, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

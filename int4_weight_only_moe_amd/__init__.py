@@ -20,7 +20,7 @@ from ._binding import (  # noqa: F401
     moe_w4a16_abi_version, moe_w4a16_fc1, moe_w4a16_fc2, moe_w4a16_forward, moe_w4a16_layer, moe_w4a16_layer_noalloc, moe_w4a16_packed_bytes,
     moe_w4a16_preferred_block_m, moe_w4a16_repack, moe_w4a16_unpack, moe_w4a16_workspace_bytes,
     moe_mxfp4_fc1, moe_mxfp4_fc2, moe_mxfp4_forward, moe_mxfp4_layer, moe_mxfp4_packed_bytes, moe_mxfp4_repack,
-    moe_mxfp4_unpack, status_string,
+    moe_mxfp4_unpack, status_string, moe_calib_read_granule, moe_calib_hbm_read, moe_calib_mfma_f16,
 )
 
 FORMATS = ("int4", "mxfp4")  # weight formats: INT4 g32 + fp16 scales, MXFP4 (e2m1 + E8M0 per 32)

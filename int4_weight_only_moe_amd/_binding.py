@@ -54,6 +54,9 @@ _SIGNATURES = {
     "moe_mxfp4_repack": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "moe_mxfp4_unpack": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
 }
+_SIGNATURES["moe_calib_read_granule"] = (_i64, [])
+_SIGNATURES["moe_calib_hbm_read"] = (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp])
+_SIGNATURES["moe_calib_mfma_f16"] = (ctypes.c_int, [_i64, _i32, _vp, _vp])
 _SIGNATURES["moe_w4a16_layer_noalloc"] = (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                                           _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp])
 # the MXFP4 stages take the same arguments as the INT4 ones
@@ -322,3 +325,26 @@ def moe_mxfp4_fc2(*args, **kw) -> None:
 def moe_mxfp4_layer(*args, **kw) -> None:
     """moe_w4a16_layer with moe_mxfp4_repack weights."""
     moe_w4a16_layer(*args, _prefix="moe_mxfp4", **kw)
+
+
+# ------------------------------------------------------------------ measurement helpers
+def moe_calib_read_granule() -> int:
+    return lib().moe_calib_read_granule()
+
+
+def moe_calib_hbm_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of `buf` once (attainable HBM read rate); sink: int32
+    [workgroups * 256], its XOR = the XOR of buf's 32-bit words."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().moe_calib_hbm_read(buf.data_ptr(), nbytes, sink.numel() // 256,
+                                  _ptr(sink, torch.int32, "sink"), _stream(stream))
+    _check("moe_calib_hbm_read", st)
+
+
+def moe_calib_mfma_f16(iters: int, sink: torch.Tensor, stream=None) -> None:
+    """iters * 8 fp16 MFMAs per wave, 4 waves per workgroup, sink.numel() // 256
+    workgroups (attainable matrix-core rate); sink: float32 [workgroups * 256]."""
+    st = lib().moe_calib_mfma_f16(iters, sink.numel() // 256, _ptr(sink, torch.float32, "sink"), _stream(stream))
+    _check("moe_calib_mfma_f16", st)

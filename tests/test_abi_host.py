@@ -218,3 +218,22 @@ def test_both_formats_validate_alike(prefix):
                  None) == moe.MOE_ERR_UNSUPPORTED
     assert fc1(p, 4, 384, 7168, 2048, 8, 16, p, p, p, cap, p, p, ws - 16, None) == moe.MOE_ERR_WORKSPACE
     assert fc2(4, 384, 7168, 2048, 8, 16, p, p, p, p, cap, p, p, ws, None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_calib_validation():
+    lib = moe.lib()
+    g = moe.moe_calib_read_granule()
+    assert g == 256 * 8 * 16
+    sink = FAKE
+    assert lib.moe_calib_hbm_read(None, g, 1, sink, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_hbm_read(FAKE, g, 1, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_hbm_read(FAKE, 0, 1, sink, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_hbm_read(FAKE, g + 16, 1, sink, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_hbm_read(FAKE, g, 0, sink, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_hbm_read(FAKE, g, (1 << 20) + 1, sink, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_hbm_read(FAKE + 8, g, 1, sink, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_hbm_read(FAKE, g, 1, sink + 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_mfma_f16(1, 1, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_mfma_f16(-1, 1, sink, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_mfma_f16(1, 0, sink, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_mfma_f16(1, 1, sink + 2, None) == moe.MOE_ERR_INVALID_ARG
