@@ -348,7 +348,7 @@ int moe_mxfp4_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
  * memory bandwidth).
  *
  * moe_calib_read_granule (host): the byte multiple moe_calib_hbm_read reads
- *   (131072).
+ *   (32768).
  * moe_calib_hbm_read: reads `bytes` of `buf` once (non-temporal 16-byte loads,
  *   `workgroups` workgroups of 256 threads; each thread writes the XOR of the
  *   32-bit words it read to sink[workgroup * 256 + thread], so the XOR of the

@@ -241,6 +241,26 @@ static void check_noalloc(void) {
            MOE_ERR_SCRATCH);
 }
 
+static void check_calib(void) {
+  const int64_t g = moe_calib_read_granule();
+  CHECK_EQ(g, 32768);
+  uint32_t* sink = (uint32_t*)PI;
+  CHECK_EQ(moe_calib_hbm_read(NULL, g, 1, sink, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_hbm_read(P, g, 1, NULL, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_hbm_read(P, 0, 1, sink, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_hbm_read(P, INT64_MIN, 1, sink, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_hbm_read(P, g - 16, 1, sink, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_hbm_read(P, INT64_MAX, 1, sink, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_hbm_read(P, g, 0, sink, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_hbm_read(P, g, INT32_MIN, sink, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_hbm_read(P, g, INT32_MAX, sink, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_hbm_read(PU8 + 8, g, 1, sink, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_mfma_f16(1, 1, NULL, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_mfma_f16(INT64_MIN, 1, (float*)PF, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_mfma_f16(1, 0, (float*)PF, NULL), MOE_ERR_INVALID_ARG);
+  CHECK_EQ(moe_calib_mfma_f16(1, INT32_MAX, (float*)PF, NULL), MOE_ERR_INVALID_ARG);
+}
+
 int main(void) {
   CHECK_EQ(moe_w4a16_abi_version(), 3);
   check_status_strings();
@@ -252,6 +272,7 @@ int main(void) {
   check_stages(moe_w4a16_fc1, moe_w4a16_fc2, moe_w4a16_forward, moe_w4a16_layer);
   check_stages(moe_mxfp4_fc1, moe_mxfp4_fc2, moe_mxfp4_forward, moe_mxfp4_layer);
   check_noalloc();
+  check_calib();
   if (g_fails) {
     fprintf(stderr, "%d of %d checks failed\n", g_fails, g_checks);
     return 1;

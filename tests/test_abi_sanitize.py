@@ -1,7 +1,7 @@
 """The C ABI's host code under AddressSanitizer and UndefinedBehaviorSanitizer.
 
-abi.hip (every exported entry point and its validation) is compiled with the
-sanitizers on its host side only; the device code and the other objects are
+abi.hip and calib.hip (every exported entry point and its validation) are
+compiled with the sanitizers on their host side only; the device code and the other objects are
 the ordinary build. tests/abi_checks.c calls every entry point with invalid
 and extreme arguments that the library rejects before any HIP call, so the
 run needs no GPU and launches nothing. Any sanitizer report, or a return code
@@ -18,6 +18,7 @@ import pytest
 from int4_weight_only_moe_amd import build as b
 
 SAN_DIR = os.path.join(b.BUILD, "san")
+SANITIZED = ("abi.hip", "calib.hip")  # the sources holding the exported entry points
 CLANG = "/opt/rocm/llvm/bin/clang"
 SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
                  "-Xarch_host", "-fno-sanitize-recover=all"]
@@ -29,10 +30,10 @@ def _run(cmd):
 
 
 def _objects():
-    """Ordinary objects of every source but abi.hip (compiled if missing or stale)."""
+    """Ordinary objects of every source but the sanitized ones (compiled if missing or stale)."""
     objs = []
     for src in b.sources():
-        if os.path.basename(src) == "abi.hip":
+        if os.path.basename(src) in SANITIZED:
             continue
         obj = os.path.join(b.BUILD, os.path.basename(src)[:-4] + ".o")
         if not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(src):
@@ -50,15 +51,18 @@ def checker():
     if not os.path.exists(CLANG):
         pytest.skip("ROCm clang not found")
     os.makedirs(SAN_DIR, exist_ok=True)
-    abi_o = os.path.join(SAN_DIR, "abi.o")
-    _run([b.hipcc(), *b.COMMON, "-O1", "-g", "-fno-omit-frame-pointer", *SANITIZE_HOST, "-c",
-          os.path.join(b.CSRC, "abi.hip"), "-o", abi_o])
+    san_objs = []
+    for src in SANITIZED:
+        obj = os.path.join(SAN_DIR, src[:-4] + ".o")
+        _run([b.hipcc(), *b.COMMON, "-O1", "-g", "-fno-omit-frame-pointer", *SANITIZE_HOST, "-c",
+              os.path.join(b.CSRC, src), "-o", obj])
+        san_objs.append(obj)
     drv_o = os.path.join(SAN_DIR, "abi_checks.o")
     _run([CLANG, "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
           "-fno-sanitize-recover=all", "-I", os.path.join(b.ROOT, "include"), "-c",
           os.path.join(os.path.dirname(__file__), "abi_checks.c"), "-o", drv_o])
     exe = os.path.join(SAN_DIR, "abi_checks")
-    _run([CLANG + "++", "-fsanitize=address,undefined", drv_o, abi_o, *_objects(), "-L/opt/rocm/lib",
+    _run([CLANG + "++", "-fsanitize=address,undefined", drv_o, *san_objs, *_objects(), "-L/opt/rocm/lib",
           "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", exe])
     yield exe
     shutil.rmtree(SAN_DIR, ignore_errors=True)
