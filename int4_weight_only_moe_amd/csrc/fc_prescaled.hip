@@ -580,19 +580,23 @@ void fc_prescaled_kernel(FcArgs a) {
   if (e < 0 || e >= a.E || nsub < 1 || nsub > a.tile_rows / kTileRows) return;
 
   // exactly the tile's sub-tiles are multiplied
+  // (bodies for more sub-tiles than a tile can hold are not instantiated)
+#define MOE_PRESCALED_CASE(S)                                                          \
+  case S:                                                                              \
+    if constexpr (S * kTileRows <= kBMaxRows)                                          \
+      prescaled_policy<S, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig);   \
+    break;
   switch (nsub) {
-    case 1: prescaled_policy<1, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
-    case 2: prescaled_policy<2, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
-    case 3: prescaled_policy<3, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
-    case 4: prescaled_policy<4, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
-    case 5: prescaled_policy<5, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
-    case 6: prescaled_policy<6, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig); break;
-    default:
-      if constexpr (kBMaxRows >= 128) {
-        if (nsub == 7) prescaled_policy<7, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig);
-        else prescaled_policy<8, kFc1>(a, e, pair, row0, nsub, reuse, xs, xoffs, tr, psig);
-      }
+    MOE_PRESCALED_CASE(1)
+    MOE_PRESCALED_CASE(2)
+    MOE_PRESCALED_CASE(3)
+    MOE_PRESCALED_CASE(4)
+    MOE_PRESCALED_CASE(5)
+    MOE_PRESCALED_CASE(6)
+    MOE_PRESCALED_CASE(7)
+    MOE_PRESCALED_CASE(8)
   }
+#undef MOE_PRESCALED_CASE
 }
 
 }  // namespace
