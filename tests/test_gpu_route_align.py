@@ -1,6 +1,8 @@
 """moe_route_align on the GPU against the oracle: integers bit-exact, weights
-to 2e-6, on every workload, every block_m, both launch shapes (fused for
-M <= 16, two kernels above), constructed ties and load extremes."""
+to 2e-6, on every workload, every block_m, every launch shape (fused for
+M <= 16; above, the top-k kernel and a one-workgroup grouping kernel, or from
+4096 assignments a grid of grouping workgroups), constructed ties and load
+extremes."""
 import numpy as np
 import pytest
 import torch
@@ -30,7 +32,11 @@ def test_workloads(name, block_m):
 
 
 @pytest.mark.parametrize("E,k,M", [(5, 5, 3), (64, 4, 17), (65, 16, 40), (130, 3, 16), (300, 8, 200),
-                                   (1000, 12, 33), (1024, 16, 1), (1024, 1, 700), (8, 2, 2000)])
+                                   (1000, 12, 33), (1024, 16, 1), (1024, 1, 700), (8, 2, 2000),
+                                   # the grid grouping kernel (from 4096 assignments): a last segment of
+                                   # two assignments, E = 1024, an odd E, segments longer than 2048
+                                   # (more than 256 * 2048 assignments)
+                                   (8, 2, 2049), (1024, 16, 700), (100, 5, 1000), (64, 8, 70000)])
 def test_shapes_cover_every_lane_width(E, k, M):
     rng = np.random.default_rng(E * 7 + M)
     logits = rng.standard_normal((M, E)).astype(np.float32)
@@ -85,8 +91,9 @@ def test_deterministic_integers():
         np.testing.assert_array_equal(again["topk_weights"], first["topk_weights"])
 
 
-def test_guard_bands_untouched():
-    w = wl.WORKLOADS["k26_m90"]
+@pytest.mark.parametrize("name", ["k26_m90", "k26_m2048"])  # one-workgroup and grid grouping
+def test_guard_bands_untouched(name):
+    w = wl.WORKLOADS[name]
     t = wl.workload_tokens(w)
     E, k, B, M = w.shape.E, w.shape.k, 16, w.M
     cap = moe.moe_route_align_capacity(M, E, k, B)
