@@ -27,11 +27,11 @@ def expected_sigma(scales_f16: np.ndarray) -> np.ndarray:
     return np.where(m == 0, 0, sig).astype(np.int8)
 
 
-def layer_with_scales(factor13: float, factor2: float, seed: int = 41):
-    w13, s13, w2, s2 = wl.layer_weights(SHAPE, seed)
+def layer_with_scales(factor13: float, factor2: float, seed: int = 41, shape=SHAPE):
+    w13, s13, w2, s2 = wl.layer_weights(shape, seed)
     s13 = (s13.astype(np.float64) * factor13).astype(np.float16)
     s2 = (s2.astype(np.float64) * factor2).astype(np.float16)
-    return (w13, s13, w2, s2), DeviceLayer(SHAPE, w13, s13, w2, s2)
+    return (w13, s13, w2, s2), DeviceLayer(shape, w13, s13, w2, s2)
 
 
 def experts_of(host):
@@ -72,19 +72,24 @@ def test_prescaled_extreme_scales(factor13, factor2):
         print(f"prescaled scales x{factor13:g}/x{factor2:g} B={block_m}: rel-L2 {rel:.2e}", flush=True)
 
 
-def test_prescaled_activation_rows_outside_fp16():
+# the fp16 row copies: hidden 256 and 7168 hold a row in registers (2 and 16
+# vectors per lane), 8448 takes the two-pass loop
+@pytest.mark.parametrize("H", [256, 7168, 8448])
+def test_prescaled_activation_rows_outside_fp16(H):
     """Rows scaled by 1e6 (beyond 65504) and 1e-6, and all-zero rows: each row
     keeps its own power-of-two scale; zero rows give exactly zero."""
-    host, layer = layer_with_scales(1.0, 1.0)
-    t = wl.tokens(SHAPE, M, 43)
+    shape = wl.LayerShape(E=SHAPE.E, H=H, I=SHAPE.I, k=SHAPE.k)
+    host, layer = layer_with_scales(1.0, 1.0, shape=shape)
+    t = wl.tokens(shape, M, 43)
     x = wl.f32_from_bf16_bits(t.x_bits)
     x[0::3] *= 1e6
     x[1::3] *= 1e-6
     x[5] = 0.0
     x[77] = 0.0
     x_bits = wl.bf16_bits_from_f32(x)
+    print(f"prescaled activation rows H={H}", flush=True)
     rb, out = run_layer(layer, t.logits, x_bits, 64)
-    ids, w = assert_route_matches(route_host(rb), t.logits, SHAPE.E, SHAPE.k, 64)
+    ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, 64)
     ref = oracle.moe_forward(wl.f32_from_bf16_bits(x_bits).astype(np.float64), ids, w, experts_of(host))
     assert np.all(out[5] == 0) and np.all(out[77] == 0)
     # each magnitude class against the oracle on its own rows
