@@ -767,6 +767,7 @@ hipError_t launch_rowscale(const uint16_t* in, int64_t rows, int64_t K, uint16_t
   if (vpl <= 2) rowscale_regs_kernel<2><<<(unsigned)blocks, 64 * kRsWaves, 0, stream>>>(in, rows, (int)K, out, exps);
   else if (vpl <= 4) rowscale_regs_kernel<4><<<(unsigned)blocks, 64 * kRsWaves, 0, stream>>>(in, rows, (int)K, out, exps);
   else if (vpl <= 8) rowscale_regs_kernel<8><<<(unsigned)blocks, 64 * kRsWaves, 0, stream>>>(in, rows, (int)K, out, exps);
+  else if (vpl <= 14) rowscale_regs_kernel<14><<<(unsigned)blocks, 64 * kRsWaves, 0, stream>>>(in, rows, (int)K, out, exps);
   else if (vpl <= 16) rowscale_regs_kernel<16><<<(unsigned)blocks, 64 * kRsWaves, 0, stream>>>(in, rows, (int)K, out, exps);
   else rowscale_kernel<<<(unsigned)blocks, 64 * kRsWaves, 0, stream>>>(in, rows, (int)K, out, exps);
   return hipGetLastError();

@@ -72,9 +72,9 @@ def test_prescaled_extreme_scales(factor13, factor2):
         print(f"prescaled scales x{factor13:g}/x{factor2:g} B={block_m}: rel-L2 {rel:.2e}", flush=True)
 
 
-# the fp16 row copies: hidden 256 and 7168 hold a row in registers (2 and 16
-# vectors per lane), 8448 takes the two-pass loop
-@pytest.mark.parametrize("H", [256, 7168, 8448])
+# the fp16 row copies: hidden 256, 7168 and 8192 hold a row in registers (2,
+# 14 and 16 vectors per lane), 8448 takes the two-pass loop
+@pytest.mark.parametrize("H", [256, 7168, 8192, 8448])
 def test_prescaled_activation_rows_outside_fp16(H):
     """Rows scaled by 1e6 (beyond 65504) and 1e-6, and all-zero rows: each row
     keeps its own power-of-two scale; zero rows give exactly zero."""
