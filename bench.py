@@ -465,8 +465,9 @@ def traffic_for(launch_bytes_alg):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported in this build "
-              "(the layer's multi-GPU sharding is described, not built)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
+              "(the library implements the one-GPU layer; sharding it over GPUs is not implemented)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"

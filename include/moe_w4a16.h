@@ -344,7 +344,7 @@ int moe_mxfp4_layer(const float* logits, const uint16_t* x_bf16, int32_t M, int3
 /* Measurement helpers (not part of the layer). They measure what this GPU
  * sustains, so that a layer kernel's rate can be stated as a fraction of the
  * attainable rate as well as of the published peaks ("The Throughput Lever",
- * section "The Result: Two Regimes", judges the layer by its fraction of the
+ * section "The Result: Two Regimes", measures the layer as a fraction of the
  * memory bandwidth).
  *
  * moe_calib_read_granule (host): the byte multiple moe_calib_hbm_read reads
