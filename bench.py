@@ -349,6 +349,14 @@ class Bench:
             fc1_us=round(fc1_us, 2), fc1_GBps=round(fc1_bytes(D, w.M, s, fmt) / (fc1_us * 1e-6) / 1e9, 1),
             fc1_us_p10_p50_p90=[round(float(v), 2) for v in np.percentile(fc1, [10, 50, 90])],
             replicas=min(replicas, len(self.layers)), wall_s=round(wall, 3))
+        # the batch's grouping as the library computed it, and the inputs' hashes
+        rb = c["rb"]
+        ids = rb.topk_ids.cpu().numpy().reshape(-1)
+        r["npp"] = int(rb.num_tokens_post_pad.item())
+        r["max_per_expert"] = int(np.bincount(ids, minlength=s.E).max())
+        t = c["t"]
+        r["inputs_sha256_16"] = {"logits": hashlib.sha256(t.logits.tobytes()).hexdigest()[:16],
+                                 "x_bf16": hashlib.sha256(t.x_bits.tobytes()).hexdigest()[:16]}
         if fmt != "int4":
             r["weights"] = fmt
         return r, c
@@ -450,6 +458,12 @@ class Bench:
                        f"{wgs} workgroups of 4 waves; torch matmul: 8192^3 bf16 (context)"}
 
 
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "hip": torch.version.hip}
+
+
 def traffic_for(launch_bytes_alg):
     """HBM bytes per FC1 launch from committed rocprofv3 counter runs, if they
     were taken on the current FC1 source; else None."""
@@ -524,6 +538,8 @@ def main():
         "config": {"workload": f"{a.workload}: E=384, H=7168, I=2048, top-8, "
                                f"{'INT4 g32' if fmt == 'int4' else 'MXFP4'}, M={M} tokens",
                    "global_batch": M, "block_m": head["block_m"], "experts_touched": D,
+                   "npp": head["npp"], "max_per_expert": head["max_per_expert"],
+                   "inputs_sha256_16": head["inputs_sha256_16"],
                    "weight_copies_cycled": head["replicas"],
                    "launch": "eager, queued ahead of the GPU"},
         "graph_us_per_call": None if a.no_graph else round(b.run_graph(a.workload, a.steps, a.replicas, fmt) * 1e3, 2),
@@ -536,6 +552,7 @@ def main():
         "layer": {k: head[k] for k in ("us_per_call", "hbm_TBps", "mfma_pct", "roofline_frac", "frac_attainable",
                                        "fc1_us_p10_p50_p90")},
         "attainable_peaks": att,
+        "device": device_info(torch),
         "repack_ms": round(b.repack_ms, 2),
         "sweep": sweep,
         "mxfp4_sweep": mxfp4,
