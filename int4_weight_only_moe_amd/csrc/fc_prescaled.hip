@@ -71,6 +71,7 @@ constexpr int kCopyRows = 4 * kBW;                      // A rows one copy round
 constexpr int kBSlotRows = (kBMaxRows + kCopyRows - 1) / kCopyRows * kCopyRows;  // whole rounds
 constexpr int kBSlotVecs = kBSlotRows * kBVecs;         // one LDS slot: up to 128 rows x 16 vectors
 constexpr int kBXcds = 8;
+constexpr int kPlanMaxExperts = 1024;
 constexpr int kBWLoads = 4;                  // vector loads per weight chunk (2 tiles' codes + scales)
 #ifndef MOE_PRESCALED_APRE
 #define MOE_PRESCALED_APRE 3
@@ -127,49 +128,89 @@ __device__ __forceinline__ f16x8_t dequant_int4_f16(uint32_t w, f16x2_t s2) {
 }
 
 // ---------------------------------------------------------------------------
-// Plan: one workgroup turns the block list into the tile list.
-// tile_rows: 64, 96 or 128 (whole blocks).
+// Plan: one workgroup turns the block list into the tile list. Each
+// expert's run of r blocks becomes n = ceil(r / bpt) tiles of as equal a
+// size as whole blocks allow (bpt = tile_rows / block_m, tile_rows 64, 96 or
+// 128), counted from the run's own first block: an expert of up to tile_rows
+// rows is one tile and its weights are read once, and the tiles of a longer
+// run are alike, so the XCDs they are dealt to get alike work. (Tiles cut at
+// multiples of tile_rows of the whole list split most experts in two, each
+// part reading the expert's weights; full tiles followed by one remainder
+// alternated large and small tiles over the XCDs.)
 __global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restrict__ block_expert,
                                                         const int32_t* __restrict__ sorted_ids,
-                                                        const int32_t* __restrict__ npp_p, int block_m, int MK,
+                                                        const int32_t* __restrict__ npp_p, int E, int block_m, int MK,
                                                         int tile_rows, int max_tiles, int2* __restrict__ tiles,
                                                         int32_t* __restrict__ ntiles_out) {
+  __shared__ int run_blocks[kPlanMaxExperts];  // blocks per expert (each expert's blocks are one run)
   __shared__ int wave_cnt[16];
-  __shared__ int base;
+  __shared__ int wave_run[16];
+  __shared__ int base, carry;  // tiles so far; the last run start of the blocks so far
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bpt = tile_rows / block_m;  // blocks per full tile
   const int nblk = *npp_p / block_m;
-  if (tid == 0) base = 0;
+  for (int e = tid; e < E; e += 1024) run_blocks[e] = 0;
+  if (tid == 0) {
+    base = 0;
+    carry = 0;
+  }
+  __syncthreads();
+  for (int b = tid; b < nblk; b += 1024) {
+    const int e = block_expert[b];
+    if (e >= 0 && e < E) atomicAdd(&run_blocks[e], 1);
+  }
   __syncthreads();
   for (int b0 = 0; b0 < nblk; b0 += 1024) {
     const int b = b0 + tid;
     int e = -1;
-    bool head = false;
+    bool run_head = false;
     if (b < nblk) {
       e = block_expert[b];
-      head = (b % bpt == 0) || block_expert[b - 1] != e;  // b % bpt != 0 implies b >= 1
+      run_head = b == 0 || block_expert[b - 1] != e;
     }
+    // the first block of b's run: an inclusive max-scan of the run heads
+    int rs = run_head ? b : -1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(rs, d, 64);
+      if (lane >= d) rs = max(rs, o);
+    }
+    if (lane == 63) wave_run[wave] = rs;
+    __syncthreads();
+    int first = carry;
+    for (int w = 0; w < wave; ++w) first = max(first, wave_run[w]);
+    first = max(first, rs);
+    // tile j of the run starts at block floor(j * r / n): b starts a tile if
+    // it is that start for j = ceil(pos * n / r)
+    const int64_t pos = b - first;
+    const int64_t r = (e >= 0 && e < E) ? run_blocks[e] : 0;
+    const int64_t n = r > 0 ? (r + bpt - 1) / bpt : 1;
+    const int64_t j = r > 0 ? (pos * n + r - 1) / r : 0;
+    const bool head = b < nblk && pos < r && j * r / n == pos;
     const unsigned long long m = __ballot(head);
     if (lane == 0) wave_cnt[wave] = __popcll(m);
     __syncthreads();
     int t = base + __popcll(m & ((1ull << lane) - 1ull));
     for (int w = 0; w < wave; ++w) t += wave_cnt[w];
     if (head && t < max_tiles) {
-      // the tile runs to the next full-tile boundary or the end of the expert
-      int nb = 1;
-      while (nb < bpt - b % bpt && b + nb < nblk && block_expert[b + nb] == e) ++nb;
+      int nb = (int)((j + 1) * r / n - pos);
+      nb = nb < nblk - b ? nb : nblk - b;
       // sub-tiles that hold a row: an expert's padding sits at the end of its
       // range, so they are a prefix of the tile's
       int nsub = nb * block_m / kTileRows;
       while (nsub > 1 && sorted_ids[b * block_m + (nsub - 1) * kTileRows] >= MK) --nsub;
-      const bool reuse = (b > 0 && block_expert[b - 1] == e) || (b + nb < nblk && block_expert[b + nb] == e);
+      const bool reuse = n > 1;
       tiles[t] = make_int2(b * block_m, nsub | (reuse ? kTileReuseBit : 0) | (e << kTileExpertShift));
     }
     __syncthreads();
     if (tid == 0) {
-      int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += wave_cnt[w];
+      int tot = 0, last = carry;
+      for (int w = 0; w < 16; ++w) {
+        tot += wave_cnt[w];
+        last = max(last, wave_run[w]);
+      }
       base += tot;
+      carry = last;
     }
     __syncthreads();
   }
@@ -610,7 +651,8 @@ int64_t tile_grid_tiles(int64_t M, int64_t E, int64_t k, int64_t block_m, int64_
 }
 
 hipError_t launch_tile_plan(const FcArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, stream, a.block_expert, a.sorted_ids, a.npp,
+  if (a.E > kPlanMaxExperts || a.block_m <= 0 || a.tile_rows % a.block_m != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, stream, a.block_expert, a.sorted_ids, a.npp, a.E,
                      a.block_m, a.M * a.k, a.tile_rows, a.max_tiles, a.tiles, a.ntiles);
   return hipGetLastError();
 }

@@ -78,8 +78,8 @@ constexpr int kTileNsubMask = 15;
 constexpr int kTileReuseBit = 16;
 constexpr int kTileExpertShift = 8;
 // Upper bound of the tile count for any block_m and tile size of at least 64
-// rows (a tile starts at every expert change and every tile_rows rows of the
-// block_m-padded list).
+// rows (a tile starts at every expert change and every tile_rows rows of an
+// expert's run of blocks).
 inline int64_t tile_table_entries(int64_t M, int64_t k) { return 2 * M * k + 16; }
 
 // The pre-scaled tiled kernel takes over from the block kernels once experts

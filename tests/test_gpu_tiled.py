@@ -99,3 +99,65 @@ def test_tiled_with_oversized_route_buffers():
         ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,
                                  oracle_experts(shape, wseed))
         assert_output_close(out, ref, f"oversized cap B={block_m}")
+
+
+def expected_tiles(block_expert, sorted_ids, npp, block_m, tile_rows, MK):
+    """The tile list the plan must write: each expert's run of r blocks cut
+    into n = ceil(r / bpt) tiles, tile j starting at block floor(j r / n) of
+    the run; a tile's sub-tile count covers its real rows; the reuse flag
+    marks experts of several tiles."""
+    nblk, bpt = npp // block_m, tile_rows // block_m
+    out = []
+    b = 0
+    while b < nblk:
+        e, end = block_expert[b], b
+        while end < nblk and block_expert[end] == e:
+            end += 1
+        r = end - b
+        n = -(-r // bpt)
+        for j in range(n):
+            h, nb = b + j * r // n, (j + 1) * r // n - j * r // n
+            assert 1 <= nb <= bpt
+            nsub = nb * block_m // 16
+            while nsub > 1 and sorted_ids[h * block_m + (nsub - 1) * 16] >= MK:
+                nsub -= 1
+            out.append((h * block_m, nsub | (16 if n > 1 else 0) | (int(e) << 8)))
+        b = end
+    return out
+
+
+@pytest.mark.parametrize("case", [2, 3, 4])
+@pytest.mark.parametrize("block_m", [16, 32, 64])
+def test_tile_plan_cuts_each_expert_into_equal_tiles(case, block_m):
+    """White-box check of the tile table the forward leaves in its workspace
+    (layout: fp32 accumulator, bf16 activations, tile count, tile table): one
+    tile per expert of up to 96 rows (64 with 64-row blocks), whatever the
+    expert's offset in the padded list, longer experts in tiles of equal
+    size, and every block in exactly one tile."""
+    import int4_weight_only_moe_amd as moe
+    import torch
+    from gpu_common import to_dev, x_device
+    shape, M, sigma, wseed, tseed = TILED[case]
+    layer = device_layer(shape, wseed)
+    t = wl.tokens(shape, M, tseed, sigma)
+    rb = moe.alloc_route_buffers(M, shape.E, shape.k, block_m)
+    moe.route_align(to_dev(t.logits), rb)
+    ws = torch.zeros(moe.moe_w4a16_workspace_bytes(M, shape.E, shape.H, shape.I, shape.k), dtype=torch.uint8,
+                     device="cuda")
+    moe.forward(x_device(t.x_bits), rb, shape.I, layer.w13, layer.w2, workspace=ws)
+    torch.cuda.synchronize()
+    h = route_host(rb)
+
+    def a256(v):
+        return (v + 255) // 256 * 256
+    ntiles_off = a256(M * shape.H * 4) + a256(M * shape.k * shape.I * 2)
+    raw = ws.cpu().numpy()
+    ntiles = int(raw[ntiles_off:ntiles_off + 4].view(np.int32)[0])
+    table = raw[ntiles_off + 256:].view(np.int32)[:2 * ntiles].reshape(ntiles, 2)
+    tile_rows = 96 if 96 % block_m == 0 else block_m
+    want = expected_tiles(h["block_expert_ids"], h["sorted_token_ids"], int(h["num_tokens_post_pad"]), block_m,
+                          tile_rows, M * shape.k)
+    assert [tuple(map(int, r)) for r in table] == want
+    counts = np.bincount(h["topk_ids"].reshape(-1), minlength=shape.E)
+    small = int(np.sum((counts > 0) & (counts <= tile_rows)))
+    assert sum(1 for _, meta in want if not meta & 16) == small  # every such expert is one tile
