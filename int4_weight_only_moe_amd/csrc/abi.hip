@@ -170,8 +170,7 @@ int32_t moe_w4a16_preferred_block_m(int32_t M, int32_t E, int32_t H, int32_t I, 
   // expert averages more than ~24 rows. Batches of a few assignments keep
   // 16-row blocks: the wide kernel would launch too few workgroups.
   // From MOE_PRESCALED_MIN_PER_EXPERT on the pre-scaled tiled kernel runs,
-  // whose INT4 tiles are 96 rows with 16- or 32-row blocks (64 with 64-row
-  // blocks).
+  // whose tiles are up to 128 rows of whole blocks.
   const double per_expert = (double)M * top_k / E;
   if ((int64_t)M * top_k <= 32) return 16;
   if (moe::prescaled_batch(M, E, top_k) && moe::fmt_int4::prescaled_supported(H, I)) return 32;

@@ -1,5 +1,5 @@
 // Grouped GEMM (FC1 and FC2) with the group scales applied before the
-// product, on tiles of up to 96 or 128 rows: the large-batch regime.
+// product, on tiles of up to 128 rows: the large-batch regime.
 //
 // "The Throughput Lever: Quantifying the MoE GEMM and Mapping the Road to
 // B300", section "The Result: Two Regimes": once every expert holds tens to
@@ -22,26 +22,27 @@
 //     the bf16 activations themselves.
 // Work decomposition:
 //   * a plan kernel cuts each expert's row range (block_m-padded, from
-//     moe_route_align) into tiles: a tile starts at every expert change and
-//     at every tile_rows boundary of the padded list, so an expert holding
-//     hundreds of rows gets several tiles; a tile counts only the 16-row
-//     sub-tiles that hold a row (padding is not multiplied), and carries a
-//     reuse flag when its expert has other tiles (then the weights are read
-//     with the default cache policy, else non-temporally);
-//   * tiles of up to 96 rows of one expert for INT4 (64 with 64-row blocks),
-//     128 for MXFP4: one tile pair per
-//     wave, 8 waves per workgroup, two workgroups per CU (four waves per
-//     SIMD, <= 128 VGPRs, 56 or 74 KB of LDS each): while one workgroup waits
-//     at a barrier or runs its epilogue, the other keeps the matrix core busy
-//     (INT4's widened fp16 codes leave registers for 6 sub-tiles, MXFP4's for 8);
+//     moe_route_align) into tiles of equal size counted from the expert's
+//     first row, so an expert of up to 128 rows is one tile (its weights
+//     are read once) and one holding hundreds of rows gets several; a tile
+//     counts only the 16-row sub-tiles that hold a row (padding is not
+//     multiplied), and carries a reuse flag when its expert has other tiles
+//     (then the weights are read with the default cache policy, else
+//     non-temporally);
+//   * tiles of up to 128 rows of one expert: one tile pair per wave, 8
+//     waves per workgroup, two workgroups per CU (four waves per SIMD,
+//     <= 128 VGPRs, 74 KB of LDS each): while one workgroup waits at a
+//     barrier or runs its epilogue, the other keeps the matrix core busy
+//     (INT4's widened fp16 codes take registers: its bodies for 7 or 8
+//     sub-tiles keep two A fragments in flight instead of three);
 //   * the tile's activation chunk (up to 128 rows x 128 channels) is copied
 //     from memory straight into LDS by gfx950's buffer loads to LDS (no
 //     staging registers or stores), double-buffered; a row's sixteen 16-byte
 //     vectors are stored XOR-swizzled with the row index, so the A reads of a
 //     wave (16 rows, one vector each) hit 16 different bank groups;
 //   * per 32-channel group a wave widens both tiles' codes once and runs
-//     2 x S MFMAs (S = the tile's sub-tiles of 16 rows, at most 6, or 8 for
-//     MXFP4: padding sub-tiles are not multiplied);
+//     2 x S MFMAs (S = the tile's sub-tiles of 16 rows, at most 8: padding
+//     sub-tiles are not multiplied);
 //   * a workgroup's start costs one memory round trip: the first weight
 //     chunks go out before the tile's row ids (they do not depend on them),
 //     the row ids in one batch, and what the epilogue needs of each row
@@ -66,7 +67,7 @@ namespace {
 #endif
 constexpr int kBW = MOE_PRESCALED_WAVES;     // waves (= tile pairs) per workgroup
 constexpr int kBVecs = kChunkK / 8;          // 16-byte vectors of a row's chunk slice
-constexpr int kBMaxRows = prescaled_max_rows(kFmt);   // 96 (INT4) or 128 (MXFP4)
+constexpr int kBMaxRows = prescaled_max_rows(kFmt);   // 128
 constexpr int kCopyRows = 4 * kBW;                      // A rows one copy round of the workgroup covers
 constexpr int kBSlotRows = (kBMaxRows + kCopyRows - 1) / kCopyRows * kCopyRows;  // whole rounds
 constexpr int kBSlotVecs = kBSlotRows * kBVecs;         // one LDS slot: up to 128 rows x 16 vectors
@@ -478,22 +479,24 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
         const f16x2_t t0 = g < 2 ? s0lo : s0hi, t1 = g < 2 ? s1lo : s1hi;
         const f16x2_t g0 = (g & 1) ? __builtin_shufflevector(t0, t0, 1, 1) : __builtin_shufflevector(t0, t0, 0, 0);
         const f16x2_t g1 = (g & 1) ? __builtin_shufflevector(t1, t1, 1, 1) : __builtin_shufflevector(t1, t1, 0, 0);
-        // A fragments in a ring of kAPre registers: the first kAPre - 1
+        // A fragments in a ring of kAP registers: the first kAP - 1
         // sub-tiles' rows are read before the widening, and sub-tile
-        // s + kAPre - 1's while sub-tile s's MFMAs are issued
+        // s + kAP - 1's while sub-tile s's MFMAs are issued (two for seven
+        // or eight sub-tiles: their accumulators take the registers)
+        constexpr int kAP = S > 6 ? 2 : kAPre;
         const uint4* ap = xs.x[slot] + aoff(g);
-        f16x8_t ar[kAPre];
+        f16x8_t ar[kAP];
 #pragma unroll
-        for (int p = 0; p + 1 < kAPre; ++p)
+        for (int p = 0; p + 1 < kAP; ++p)
           if (p < S) ar[p] = __builtin_bit_cast(f16x8_t, ap[p * kTileRows * kBVecs]);
         __builtin_amdgcn_sched_barrier(0);
         const f16x8_t b0 = dequant_int4_f16(q0[g], g0);
         const f16x8_t b1 = dequant_int4_f16(q1[g], g1);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          if (s + kAPre - 1 < S)
-            ar[(s + kAPre - 1) % kAPre] = __builtin_bit_cast(f16x8_t, ap[(s + kAPre - 1) * kTileRows * kBVecs]);
-          const f16x8_t xv = ar[s % kAPre];
+          if (s + kAP - 1 < S)
+            ar[(s + kAP - 1) % kAP] = __builtin_bit_cast(f16x8_t, ap[(s + kAP - 1) * kTileRows * kBVecs]);
+          const f16x8_t xv = ar[s % kAP];
           if constexpr (kFc1) {  // D transposed (see the FC1 epilogue)
             acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b0, xv, acc0[s], 0, 0, 0);
             acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1, xv, acc1[s], 0, 0, 0);

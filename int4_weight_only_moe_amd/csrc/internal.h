@@ -60,11 +60,12 @@ static __host__ __device__ inline int64_t packed_bytes_per_expert(int64_t N, int
 // Tiles of the tiled grouped GEMM (fc_prescaled.hip): up to 128 rows of one
 // expert, in 16-row sub-tiles. Table entry: (first row in the sorted list,
 // meta = sub-tiles | reuse flag | expert << 8). A sub-tile has kTileRows rows.
-// Largest tile of the pre-scaled tiled kernel (fc_prescaled.hip): 96 rows
-// for INT4 (the widened fp16 codes take the registers of two more
-// sub-tiles), 128 for MXFP4.
+// Largest tile of the pre-scaled tiled kernel (fc_prescaled.hip): 128 rows
+// for both formats (measured on the 384-expert layer against 96-row INT4
+// tiles: M = 4096 -3.4 %, skewed routing -1.3 %, M <= 2048 and 8192 within
+// +-0.5 %).
 #ifndef MOE_PRESCALED_INT4_ROWS
-#define MOE_PRESCALED_INT4_ROWS 96
+#define MOE_PRESCALED_INT4_ROWS 128
 #endif
 __host__ __device__ constexpr int prescaled_max_rows(int fmt) {
   return fmt == kFmtMxfp4 ? 128 : MOE_PRESCALED_INT4_ROWS;

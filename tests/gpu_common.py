@@ -145,17 +145,18 @@ def covering_rows(ids: np.ndarray, must=()) -> list:
     return sorted(rows)
 
 
-def tile_rows_of_hot_experts(ids: np.ndarray, tile_rows: int) -> list:
-    """One token per tile of every expert holding more than one tile: the
-    expert's assignments in ascending f, cut every tile_rows entries (the
-    tiles of the tiled kernels start at each expert and every tile_rows rows)."""
+def tile_rows_of_hot_experts(ids: np.ndarray, tile_rows: int, stride: int = 64) -> list:
+    """Tokens in every tile of each expert holding more than one tile: the
+    expert's assignments in ascending f, one every `stride` entries. The
+    tiled kernel cuts such an expert into tiles of equal whole-block size,
+    at least two 32-row blocks each, so a stride of 64 lands in every tile."""
     k = ids.shape[1]
     flat = ids.reshape(-1)
     rows = []
     for e in np.unique(flat):
         fs = np.nonzero(flat == e)[0]
         if fs.size > tile_rows:
-            rows += [int(fs[i] // k) for i in range(0, fs.size, tile_rows)]
+            rows += [int(fs[i] // k) for i in range(0, fs.size, stride)]
     return rows
 
 

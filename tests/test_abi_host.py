@@ -95,7 +95,7 @@ def test_preferred_block_m():
     assert moe.moe_w4a16_preferred_block_m(4, 384, 7168, 2048, 8) == 16
     assert moe.moe_w4a16_preferred_block_m(9, 384, 7168, 2048, 8) == 32
     assert moe.moe_w4a16_preferred_block_m(90, 384, 7168, 2048, 8) == 32
-    # 16 per expert and up: the pre-scaled tiled kernel, 96-row tiles of 32-row blocks
+    # 16 per expert and up: the pre-scaled tiled kernel, 128-row tiles of 32-row blocks
     assert moe.moe_w4a16_preferred_block_m(768, 384, 7168, 2048, 8) == 32
     assert moe.moe_w4a16_preferred_block_m(1024, 384, 7168, 2048, 8) == 32
     assert moe.moe_w4a16_preferred_block_m(4096, 384, 7168, 2048, 8) == 32

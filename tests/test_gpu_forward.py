@@ -139,7 +139,7 @@ def test_output_guard_bands_and_reuse():
 # Token rows compared with the oracle at the 384-expert sizes: a few fixed
 # rows, and for the workloads named in COVER a greedy set of rows that
 # together hold every expert the batch routes to (for the skewed batch also
-# one row in every 96-row tile of each expert holding more than one tile).
+# a row in every tile of each expert holding more than one 128-row tile).
 K26_SAMPLES = {
     "k26_m1": [0],
     "k26_m9": [0, 4, 8],
@@ -169,7 +169,7 @@ def test_k26_sampled_parity(name):
     assert np.all(np.isfinite(out))
     rows = list(K26_SAMPLES[name])
     if name in COVER:
-        rows = covering_rows(ids, rows + (tile_rows_of_hot_experts(ids, 96) if name.endswith("skew") else []))
+        rows = covering_rows(ids, rows + (tile_rows_of_hot_experts(ids, 128) if name.endswith("skew") else []))
     touched = np.unique(ids)
     covered = np.unique(ids[rows])
     x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)

@@ -1,4 +1,4 @@
-"""The pre-scaled tiled GEMM (96-row INT4 tiles; INT4 weights enter the matrix
+"""The pre-scaled tiled GEMM (128-row tiles; INT4 weights enter the matrix
 core as fp16(q * s * 2^-sigma), the activation rows as fp16 copies scaled by a
 power of two): the per-row exponent shifts the repack stores after the INT4
 tiles, and every element against the oracle where fp16 alone would overflow

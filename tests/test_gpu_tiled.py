@@ -1,7 +1,7 @@
 """The tiled grouped GEMM, which the forward takes once experts average at
 least 16 assignments (and every pair group and K-chunk count divides
-evenly): the pre-scaled kernel (INT4: 96-row tiles with 16- or 32-row
-blocks, 64-row tiles with 64-row blocks). Every element against the oracle on shapes
+evenly): the pre-scaled kernel (tiles of up to 128 rows of whole blocks,
+cut per expert). Every element against the oracle on shapes
 whose experts hold from one small tile up to several full tiles, with
 partial tiles of every sub-tile count, all block sizes, and skewed routing
 (a per-expert logit bias) that piles hundreds of rows onto a few experts."""
@@ -21,7 +21,7 @@ TILED = [
     # (shape, M, bias sigma, weight seed, token seed)
     (SMALL, 64, 0.0, 11, 12),    # 16 assignments per expert: tiles of 1-2 sub-tiles
     (SMALL, 128, 0.0, 11, 17),   # 32 per expert: tiles of 2-3 sub-tiles
-    (SMALL, 300, 0.0, 11, 13),   # ~75 per expert: 5- and 6-sub-tile tiles, two tiles with 64-row blocks
+    (SMALL, 300, 0.0, 11, 13),   # ~75 per expert: one tile each, 4 to 6 sub-tiles
     (SMALL, 700, 2.0, 11, 14),   # skewed: several full tiles on the hot experts
     (WIDER, 320, 1.0, 15, 16),   # 40 per expert, mildly skewed
 ]
@@ -66,14 +66,14 @@ def test_tiled_at_the_size_limits(block_m):
 
 
 def test_tiled_skew_has_multi_tile_experts():
-    """The skewed case really exercises experts with several full 96-row tiles
-    and partial last tiles with an odd sub-tile count."""
+    """The skewed case really exercises experts of several 128-row tiles, and
+    tiles whose last sub-tile is partial."""
     shape, M, sigma, _, tseed = TILED[3]
     t = wl.tokens(shape, M, tseed, sigma)
     ids, _ = oracle.route(t.logits, shape.k)
     counts = np.bincount(ids.reshape(-1), minlength=shape.E)
-    assert counts.max() > 2 * 96
-    assert any(c % 96 and ((c % 96) + 15) // 16 in (3, 5) for c in counts)
+    assert counts.max() > 2 * 128
+    assert any(c > 128 and c % 16 for c in counts)
 
 
 def test_tiled_with_oversized_route_buffers():
@@ -131,7 +131,7 @@ def expected_tiles(block_expert, sorted_ids, npp, block_m, tile_rows, MK):
 def test_tile_plan_cuts_each_expert_into_equal_tiles(case, block_m):
     """White-box check of the tile table the forward leaves in its workspace
     (layout: fp32 accumulator, bf16 activations, tile count, tile table): one
-    tile per expert of up to 96 rows (64 with 64-row blocks), whatever the
+    tile per expert of up to 128 rows, whatever the
     expert's offset in the padded list, longer experts in tiles of equal
     size, and every block in exactly one tile."""
     import int4_weight_only_moe_amd as moe
@@ -154,7 +154,7 @@ def test_tile_plan_cuts_each_expert_into_equal_tiles(case, block_m):
     raw = ws.cpu().numpy()
     ntiles = int(raw[ntiles_off:ntiles_off + 4].view(np.int32)[0])
     table = raw[ntiles_off + 256:].view(np.int32)[:2 * ntiles].reshape(ntiles, 2)
-    tile_rows = 96 if 96 % block_m == 0 else block_m
+    tile_rows = 128  # a multiple of every block size
     want = expected_tiles(h["block_expert_ids"], h["sorted_token_ids"], int(h["num_tokens_post_pad"]), block_m,
                           tile_rows, M * shape.k)
     assert [tuple(map(int, r)) for r in table] == want
