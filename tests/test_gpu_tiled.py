@@ -161,3 +161,63 @@ def test_tile_plan_cuts_each_expert_into_equal_tiles(case, block_m):
     counts = np.bincount(h["topk_ids"].reshape(-1), minlength=shape.E)
     small = int(np.sum((counts > 0) & (counts <= tile_rows)))
     assert sum(1 for _, meta in want if not meta & 16) == small  # every such expert is one tile
+
+
+def logits_with_counts(E: int, counts, seed: int) -> np.ndarray:
+    """Top-2 logits that give expert e exactly counts[e] assignments (no count
+    above half the total): the sorted multiset of experts, entry i paired with
+    entry i + total / 2 (always a different expert), large logits for the pair,
+    small noise elsewhere; tokens in random order."""
+    rng = np.random.default_rng(seed)
+    pool = np.repeat(np.arange(E), counts)
+    half = pool.size // 2
+    assert pool.size == 2 * half and max(counts) <= half
+    pairs = np.stack([pool[:half], pool[half:]], axis=1)
+    assert np.all(pairs[:, 0] != pairs[:, 1])
+    pairs = pairs[rng.permutation(half)]
+    logits = rng.uniform(-1.0, 0.0, (half, E)).astype(np.float32)
+    top = (10.0 + rng.uniform(0.0, 1.0, (half, 2))).astype(np.float32)
+    logits[np.arange(half)[:, None], pairs] = top
+    return logits
+
+
+# per-expert row counts at the tile-size edges: 128 (one tile), 129 (two),
+# 256 and 257 (two and three), 16 (one full sub-tile), 1, 81, 0
+EDGE_COUNTS = [129, 128, 257, 256, 16, 1, 81, 0]
+
+
+@pytest.mark.parametrize("block_m", [16, 32, 64])
+def test_tile_edges_full_parity(block_m):
+    """Experts of exactly one and just over one, two and three tiles: the
+    tile table and every output element against the oracle."""
+    import int4_weight_only_moe_amd as moe
+    import torch
+    from gpu_common import to_dev, x_device
+    shape = SMALL
+    logits = logits_with_counts(shape.E, EDGE_COUNTS, 31)
+    M = logits.shape[0]
+    x_bits = wl.tokens(shape, M, 32).x_bits
+    layer = device_layer(shape, 11)
+    rb = moe.alloc_route_buffers(M, shape.E, shape.k, block_m)
+    moe.route_align(to_dev(logits), rb)
+    ws = torch.zeros(moe.moe_w4a16_workspace_bytes(M, shape.E, shape.H, shape.I, shape.k), dtype=torch.uint8,
+                     device="cuda")
+    out = moe.forward(x_device(x_bits), rb, shape.I, layer.w13, layer.w2, workspace=ws).float().cpu().numpy()
+    torch.cuda.synchronize()
+    h = route_host(rb)
+    ids, w = assert_route_matches(h, logits, shape.E, shape.k, block_m)
+    np.testing.assert_array_equal(np.bincount(ids.reshape(-1), minlength=shape.E), EDGE_COUNTS)
+
+    def a256(v):
+        return (v + 255) // 256 * 256
+    ntiles_off = a256(M * shape.H * 4) + a256(M * shape.k * shape.I * 2)
+    raw = ws.cpu().numpy()
+    ntiles = int(raw[ntiles_off:ntiles_off + 4].view(np.int32)[0])
+    table = [tuple(map(int, r)) for r in raw[ntiles_off + 256:].view(np.int32)[:2 * ntiles].reshape(ntiles, 2)]
+    assert table == expected_tiles(h["block_expert_ids"], h["sorted_token_ids"], int(h["num_tokens_post_pad"]),
+                                   block_m, 128, M * shape.k)
+    tiles_per_expert = np.bincount([meta >> 8 for _, meta in table], minlength=shape.E)
+    np.testing.assert_array_equal(tiles_per_expert, [2, 1, 3, 2, 1, 1, 1, 0])
+    ref = oracle.moe_forward(wl.f32_from_bf16_bits(x_bits).astype(np.float64), ids, w, oracle_experts(shape, 11))
+    assert np.all(np.isfinite(out))
+    assert_output_close(out, ref, f"tile edges B={block_m}")
