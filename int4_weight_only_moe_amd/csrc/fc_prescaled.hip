@@ -131,8 +131,8 @@ __device__ __forceinline__ f16x8_t dequant_int4_f16(uint32_t w, f16x2_t s2) {
 // ---------------------------------------------------------------------------
 // Plan: one workgroup turns the block list into the tile list. Each
 // expert's run of r blocks becomes n = ceil(r / bpt) tiles of as equal a
-// size as whole blocks allow (bpt = tile_rows / block_m, tile_rows 64, 96 or
-// 128), counted from the run's own first block: an expert of up to tile_rows
+// size as whole blocks allow (bpt = tile_rows / block_m; tile_rows is 128
+// rows by default), counted from the run's own first block: an expert of up to tile_rows
 // rows is one tile and its weights are read once, and the tiles of a longer
 // run are alike, so the XCDs they are dealt to get alike work. (Tiles cut at
 // multiples of tile_rows of the whole list split most experts in two, each
