@@ -41,7 +41,7 @@
  *   W2  (kind 1): N = H,   K = I.
  *
  * Limits (MOE_ERR_UNSUPPORTED otherwise): 1 <= E <= 1024, 1 <= top_k <= min(E, 16),
- * H and I multiples of 128, block_m in {16, 32, 64}, M*top_k*max(H, I) < 2^31,
+ * H and I multiples of 128, block_m in {16, 32, 64, 128}, M*top_k*max(H, I) < 2^31,
  * and one expert's repacked W13 or W2 (moe_w4a16_packed_bytes with E = 1,
  * less its trailer) below 2^31 bytes (H*I below about 1.9e9; the repack and size
  * calls apply the same per-tensor limit, and -1 / MOE_ERR_UNSUPPORTED past it).
@@ -164,6 +164,9 @@ int64_t moe_w4a16_workspace_bytes(int32_t M, int32_t E, int32_t H, int32_t I, in
 /*
  * moe_w4a16_preferred_block_m (host): the block_m the forward runs best with
  * for this batch (a function of the expected tokens per expert, M*top_k/E).
+ * It never returns 128: the kernels that take blocks take at most 64 rows,
+ * so with block_m = 128 they run each block as its two 64-row halves (and
+ * the tiled kernel as one tile), which only adds padding rows.
  */
 int32_t moe_w4a16_preferred_block_m(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k);
 

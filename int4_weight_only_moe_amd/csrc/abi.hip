@@ -19,7 +19,7 @@ using moe::kMaxTopK;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-bool block_m_ok(int32_t b) { return b == 16 || b == 32 || b == 64; }
+bool block_m_ok(int32_t b) { return b == 16 || b == 32 || b == 64 || b == 128; }
 
 // One expert's repacked tensor (N rows of K channels, either format) stays
 // below 2^31 bytes, so in-expert offsets fit 32 bits and E times it fits int64.
@@ -230,6 +230,13 @@ static moe::FcArgs fc_args(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, 
     // the workspace has the fp16 row copies (prescaled_batch)
     a.a16 = (uint16_t*)(ws + L.a16_off);
     a.a16_exp = (int32_t*)(ws + L.a16exp_off);
+  } else if (block_m == 128) {
+    // The block kernels run each block as two 64-row halves, with a map of
+    // the halves' experts where the tile table would be. It is sized for
+    // the padded total this batch can reach (capacity / 64 <= 2 M k + 2
+    // entries), so the grid is too.
+    a.half_expert = (int32_t*)(ws + L.tiles_off);
+    a.cap = capacity(M, E, top_k, block_m);
   }
   return a;
 }

@@ -546,6 +546,22 @@ hipError_t launch_routed_vpl(const DecodeArgs& d, hipStream_t stream, hipEvent_t
   return launch_routed<VPL, 0>(d, grid, stream, e0, e1);
 }
 
+// block_m = 128 on the block kernels, which take blocks of up to 64 rows:
+// each block is run as its two 64-row halves. half[h] = the expert of half
+// h, or -1 where it holds no row (an expert's padding is at the end of its
+// range, so a half whose first row is padding is all padding) or lies past
+// the padded total.
+__global__ __launch_bounds__(256) void half_block_kernel(const int32_t* __restrict__ block_expert,
+                                                         const int32_t* __restrict__ sorted_ids,
+                                                         const int32_t* __restrict__ npp_p, int MK, int64_t nhalf,
+                                                         int32_t* __restrict__ half) {
+  const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (h >= nhalf) return;
+  int e = -1;
+  if (h * 64 < *npp_p && sorted_ids[h * 64] < MK) e = block_expert[h >> 1];
+  half[h] = e;
+}
+
 // out = bf16(acc), 8 values per thread.
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ acc, uint16_t* __restrict__ out,
                                                        int64_t n8) {
@@ -597,6 +613,18 @@ hipError_t launch_fc(const FcArgs& a, hipStream_t stream, hipEvent_t e0, hipEven
     const int64_t n8 = (int64_t)a.M * a.H / 8;
     finalize_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, stream>>>(a.acc, a.out, n8);
     return hipGetLastError();
+  }
+  if (a.block_m == 128) {  // the 64-row kernels on each half of a block
+    if (a.half_expert == nullptr || a.cap % 128 != 0) return hipErrorInvalidValue;
+    const int64_t nhalf = a.cap / 64;
+    half_block_kernel<<<(unsigned)((nhalf + 255) / 256), 256, 0, stream>>>(a.block_expert, a.sorted_ids, a.npp,
+                                                                         a.M * a.k, nhalf, a.half_expert);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    FcArgs b = a;
+    b.block_expert = a.half_expert;
+    b.block_m = 64;
+    return launch_fc<kFc1>(b, stream, e0, e1);
   }
   const int N = kFc1 ? 2 * a.I : a.H;
   const int64_t nblk = a.cap / a.block_m;

@@ -157,6 +157,10 @@ struct FcArgs {
   int32_t* a16_exp;             // their row exponents
   const int32_t* row_exp;       // the A rows' exponents as the kernel reads them
   const int8_t* wsigma;         // per-weight-row shifts of the blob (E x N)
+  // block_m = 128 on the block kernels (workspace, where the tile table
+  // would be): the expert of each 64-row half of a block, -1 for a half
+  // that holds no row
+  int32_t* half_expert;
 };
 
 // Decode path (tiny batches): routing fused into FC1, output-stationary FC2.

@@ -73,15 +73,18 @@ static void check_capacity(void) {
   CHECK_EQ(moe_route_align_capacity(4, 384, 17, 16), -1);
   CHECK_EQ(moe_route_align_capacity(4, 8, 9, 16), -1);
   CHECK_EQ(moe_route_align_capacity(4, 384, 8, 8), -1);
-  CHECK_EQ(moe_route_align_capacity(4, 384, 8, 128), -1);
+  CHECK_EQ(moe_route_align_capacity(4, 384, 8, 256), -1);
+  CHECK_EQ(moe_route_align_capacity(4, 384, 8, 96), -1);
   CHECK_EQ(moe_route_align_capacity(INT32_MIN, 384, 8, 16), -1);
   CHECK_EQ(moe_route_align_capacity(4, INT32_MAX, 8, 16), -1);
   CHECK_EQ(moe_route_align_capacity(4, 384, INT32_MAX, 16), -1);
   CHECK_EQ(moe_route_align_capacity(4, 384, 8, INT32_MIN), -1);
   CHECK_EQ(moe_route_align_capacity(4096, 384, 8, 16), capacity_formula(4096, 384, 8, 16));
   CHECK_EQ(moe_route_align_capacity(1, 384, 8, 64), capacity_formula(1, 384, 8, 64));
+  CHECK_EQ(moe_route_align_capacity(90, 384, 8, 128), capacity_formula(90, 384, 8, 128));
   /* the largest batch the capacity call accepts: int64 arithmetic throughout */
   CHECK_EQ(moe_route_align_capacity(INT32_MAX, 1024, 16, 64), capacity_formula(INT32_MAX, 1024, 16, 64));
+  CHECK_EQ(moe_route_align_capacity(INT32_MAX, 1024, 16, 128), capacity_formula(INT32_MAX, 1024, 16, 128));
 }
 
 static void check_packed_bytes(void) {
@@ -187,7 +190,9 @@ static void check_stages(fc1_fn fc1, fc2_fn fc2, fwd_fn fwd, layer_fn layer) {
   CHECK_EQ(fc1(PU16, M, E, H, I, k, B, PI, PI, PI, cap - 16, P, P, ws, NULL), MOE_ERR_CAPACITY);
   CHECK_EQ(fc1(NULL, M, E, H, I, k, B, PI, PI, PI, cap, P, P, ws, NULL), MOE_ERR_INVALID_ARG);
   CHECK_EQ(fc1((uint16_t*)P_ODD16, M, E, H, I, k, B, PI, PI, PI, cap, P, P, ws, NULL), MOE_ERR_INVALID_ARG);
-  CHECK_EQ(fc1(PU16, M, E, H, I, k, 128, PI, PI, PI, cap, P, P, ws, NULL), MOE_ERR_UNSUPPORTED);
+  CHECK_EQ(fc1(PU16, M, E, H, I, k, 256, PI, PI, PI, cap, P, P, ws, NULL), MOE_ERR_UNSUPPORTED);
+  /* 128 passes the block_m check; the cap for 16-row blocks is too small for it */
+  CHECK_EQ(fc1(PU16, M, E, H, I, k, 128, PI, PI, PI, cap, P, P, ws, NULL), MOE_ERR_CAPACITY);
   CHECK_EQ(fc1(NULL, 0, E, H, I, k, B, NULL, NULL, NULL, 0, NULL, NULL, 0, NULL), MOE_OK);
   CHECK_EQ(fc2(M, E, H, I, k, B, PF, PI, PI, PI, cap, P, P, ws, NULL, NULL), MOE_ERR_INVALID_ARG);
   CHECK_EQ(fc2(M, E, H, I, k, B, PF, PI, PI, PI, cap, P, P, ws, (uint16_t*)P_ODD16, NULL), MOE_ERR_INVALID_ARG);

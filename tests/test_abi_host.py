@@ -40,7 +40,7 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("M,E,k,B", [(1, 384, 8, 16), (1024, 384, 8, 32), (1024, 384, 8, 64), (16, 8, 2, 16),
-                                     (0, 8, 2, 16), (3, 4, 4, 64)])
+                                     (0, 8, 2, 16), (3, 4, 4, 64), (90, 384, 8, 128), (3, 4, 4, 128)])
 def test_capacity_formula(M, E, k, B):
     raw = M * k + min(E, M * k) * (B - 1)
     assert moe.moe_route_align_capacity(M, E, k, B) == -(-raw // B) * B
@@ -48,6 +48,8 @@ def test_capacity_formula(M, E, k, B):
 
 def test_capacity_rejects():
     assert moe.moe_route_align_capacity(1, 384, 8, 8) == -1
+    assert moe.moe_route_align_capacity(1, 384, 8, 256) == -1
+    assert moe.moe_route_align_capacity(1, 384, 8, 48) == -1
     assert moe.moe_route_align_capacity(1, 2000, 8, 16) == -1
     assert moe.moe_route_align_capacity(1, 4, 5, 16) == -1
     assert moe.moe_route_align_capacity(-1, 4, 2, 16) == -1
@@ -119,6 +121,9 @@ def test_route_align_validation():
     assert _route(lib, k=17, E=64) == moe.MOE_ERR_UNSUPPORTED
     assert _route(lib, k=9, E=8) == moe.MOE_ERR_UNSUPPORTED
     assert _route(lib, B=8, cap=1024) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(lib, B=256, cap=4096) == moe.MOE_ERR_UNSUPPORTED
+    cap128 = moe.moe_route_align_capacity(4, 384, 8, 128)
+    assert _route(lib, B=128, cap=cap128 - 128) == moe.MOE_ERR_CAPACITY  # 128 passes the block_m check
     assert _route(lib, logits=None) == moe.MOE_ERR_INVALID_ARG
     assert _route(lib, logits=FAKE + 2) == moe.MOE_ERR_INVALID_ARG
     cap = moe.moe_route_align_capacity(4, 384, 8, 16)
@@ -159,7 +164,10 @@ def test_forward_validation():
                                  None, 0, None, None) == moe.MOE_OK
     assert _fwd(lib, H=7000) == moe.MOE_ERR_UNSUPPORTED
     assert _fwd(lib, I=2000) == moe.MOE_ERR_UNSUPPORTED
-    assert _fwd(lib, B=128) == moe.MOE_ERR_UNSUPPORTED
+    assert _fwd(lib, B=256) == moe.MOE_ERR_UNSUPPORTED
+    assert _fwd(lib, B=48) == moe.MOE_ERR_UNSUPPORTED
+    cap128 = moe.moe_route_align_capacity(4, 384, 8, 128)
+    assert _fwd(lib, B=128, cap=cap128 - 128) == moe.MOE_ERR_CAPACITY  # 128 passes the block_m check
     assert _fwd(lib, k=0) == moe.MOE_ERR_INVALID_ARG
     cap = moe.moe_route_align_capacity(4, 384, 8, 16)
     assert _fwd(lib, cap=cap - 16) == moe.MOE_ERR_CAPACITY

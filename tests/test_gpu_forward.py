@@ -29,7 +29,7 @@ MID_SHAPES = [
 
 
 @pytest.mark.parametrize("case", range(len(MID_SHAPES)))
-@pytest.mark.parametrize("block_m", [16, 32, 64])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
 def test_full_parity_mid_shapes(case, block_m):
     shape, M, wseed, tseed = MID_SHAPES[case]
     print(f"forward {shape} M={M} block_m={block_m}", flush=True)
@@ -56,6 +56,44 @@ def const_layer(shape, byte=0x99, scale_bits=0x2000):
     layer.w2 = moe.repack(q2, s2, moe.KIND_W2)
     torch.cuda.synchronize()
     return layer
+
+
+@pytest.mark.parametrize("case", [1, 3, 5])
+def test_block_m_128_half_map(case):
+    """block_m = 128 outside the tiled kernel: the block kernels take at most
+    64 rows, so the forward runs each block as its two 64-row halves through
+    a map of the halves' experts left where the tile table would be (after
+    the tile count's 256 bytes): the expert for a half that holds a row, -1
+    for an all-padding half (skipped, its weights not read) and for halves
+    past the padded total. Checked against the routing outputs, and the
+    output against the oracle."""
+    shape, M, wseed, tseed = MID_SHAPES[case]
+    assert M * shape.k / shape.E < 16  # the block kernels, not the tiled one
+    layer = device_layer(shape, wseed)
+    t = wl.tokens(shape, M, tseed)
+    rb = moe.alloc_route_buffers(M, shape.E, shape.k, 128)
+    moe.route_align(to_dev(t.logits), rb)
+    ws = torch.full((moe.moe_w4a16_workspace_bytes(M, shape.E, shape.H, shape.I, shape.k),), 0x5A, dtype=torch.uint8,
+                    device="cuda")
+    out = moe.forward(x_device(t.x_bits), rb, shape.I, layer.w13, layer.w2, workspace=ws)
+    torch.cuda.synchronize()
+    h = route_host(rb)
+    MK = M * shape.k
+    cap = moe.moe_route_align_capacity(M, shape.E, shape.k, 128)
+    npp = h["num_tokens_post_pad"]
+    srt, blk = h["sorted_token_ids"], h["block_expert_ids"]
+    want = [int(blk[i // 2]) if i * 64 < npp and srt[i * 64] < MK else -1 for i in range(cap // 64)]
+    assert any(v == -1 for v in want[: npp // 64])  # some all-padding halves inside the list
+
+    def a256(v):
+        return (v + 255) // 256 * 256
+    off = a256(M * shape.H * 4) + a256(MK * shape.I * 2) + 256
+    got = ws.cpu().numpy()[off:off + 4 * len(want)].view(np.int32)
+    assert got.tolist() == want
+    ids, w = assert_route_matches(h, t.logits, shape.E, shape.k, 128)
+    ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,
+                             oracle_experts(shape, wseed))
+    assert_output_close(out.float().cpu().numpy(), ref, f"{shape} M={M} B=128 halves")
 
 
 @pytest.mark.parametrize("shape,M,expect", [
@@ -181,7 +219,7 @@ def test_k26_sampled_parity(name):
         assert covered.size == touched.size
 
 
-@pytest.mark.parametrize("block_m", [16, 32, 64])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
 def test_k26_m90_every_block_m(block_m):
     w = wl.WORKLOADS["k26_m90"]
     s = w.shape

@@ -49,7 +49,7 @@ def run_layer_call(layer, logits, x_bits, block_m, reps=1):
 
 @pytest.mark.parametrize("shape_name", list(SHAPES))
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9, 16, 17])
-@pytest.mark.parametrize("block_m", [16, 32, 64])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
 def test_layer_matches_oracle(shape_name, M, block_m):
     shape, seed = SHAPES[shape_name]
     if M * shape.k > 64 and M <= 4:
@@ -192,7 +192,7 @@ def test_layer_routed_sizes_with_tiled_grouped_gemm():
     assert M * shape.k > 1.2 * shape.E          # not the per-token FC2: the grouped FC2 follows
     layer = device_layer(shape, 31)
     t = wl.tokens(shape, M, 32)
-    for block_m in (16, 32, 64):
+    for block_m in (16, 32, 64, 128):
         rb, outs = run_layer_call(layer, t.logits, t.x_bits, block_m)
         ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, block_m)
         ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,

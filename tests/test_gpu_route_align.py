@@ -22,7 +22,7 @@ def run_route(logits: np.ndarray, k: int, block_m: int):
 
 
 @pytest.mark.parametrize("name", list(wl.WORKLOADS))
-@pytest.mark.parametrize("block_m", [16, 32, 64])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
 def test_workloads(name, block_m):
     w = wl.WORKLOADS[name]
     t = wl.workload_tokens(w)
@@ -40,7 +40,7 @@ def test_workloads(name, block_m):
 def test_shapes_cover_every_lane_width(E, k, M):
     rng = np.random.default_rng(E * 7 + M)
     logits = rng.standard_normal((M, E)).astype(np.float32)
-    for block_m in (16, 64):
+    for block_m in (16, 64, 128):
         print(f"route_align E={E} k={k} M={M} block_m={block_m}", flush=True)
         _, got = run_route(logits, k, block_m)
         assert_route_matches(got, logits, E, k, block_m)

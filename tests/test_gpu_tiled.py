@@ -28,7 +28,7 @@ TILED = [
 
 
 @pytest.mark.parametrize("case", range(len(TILED)))
-@pytest.mark.parametrize("block_m", [16, 32, 64])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
 def test_tiled_full_parity(case, block_m):
     shape, M, sigma, wseed, tseed = TILED[case]
     assert M * shape.k / shape.E >= 16
@@ -45,7 +45,7 @@ def test_tiled_full_parity(case, block_m):
     assert_output_close(out, ref, f"tiled {shape} M={M} B={block_m}")
 
 
-@pytest.mark.parametrize("block_m", [16, 32, 64])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
 def test_tiled_at_the_size_limits(block_m):
     """1024 experts (the largest E) with top-16 (the largest k) at 16
     assignments per expert: the pre-scaled kernel with 1024 experts' tiles;
@@ -127,7 +127,7 @@ def expected_tiles(block_expert, sorted_ids, npp, block_m, tile_rows, MK):
 
 
 @pytest.mark.parametrize("case", [2, 3, 4])
-@pytest.mark.parametrize("block_m", [16, 32, 64])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
 def test_tile_plan_cuts_each_expert_into_equal_tiles(case, block_m):
     """White-box check of the tile table the forward leaves in its workspace
     (layout: fp32 accumulator, bf16 activations, tile count, tile table): one
@@ -186,7 +186,7 @@ def logits_with_counts(E: int, counts, seed: int) -> np.ndarray:
 EDGE_COUNTS = [129, 128, 257, 256, 16, 1, 81, 0]
 
 
-@pytest.mark.parametrize("block_m", [16, 32, 64])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
 def test_tile_edges_full_parity(block_m):
     """Experts of exactly one and just over one, two and three tiles: the
     tile table and every output element against the oracle."""
