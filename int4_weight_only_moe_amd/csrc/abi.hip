@@ -216,7 +216,11 @@ static moe::FcArgs fc_args(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, 
   a.acc = (float*)(ws + L.acc_off);
   a.act_out = (uint16_t*)(ws + L.act_off);
   a.M = M; a.E = E; a.H = H; a.I = I; a.k = top_k; a.block_m = block_m;
-  a.cap = cap;
+  // The block kernels' grid is sized from the padded total this batch can
+  // reach, not from the caller's cap (route buffers may be allocated for a
+  // larger batch): the rows past it are never part of the batch.
+  const int64_t reach = capacity(M, E, top_k, block_m);
+  a.cap = cap < reach ? cap : reach;
   a.zero_words16 = (int64_t)M * H * 4 / 16;
   if (use_tiled(fmt, M, E, H, I, top_k)) {
     a.tiles = (int2*)(ws + L.tiles_off);
@@ -232,11 +236,9 @@ static moe::FcArgs fc_args(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, 
     a.a16_exp = (int32_t*)(ws + L.a16exp_off);
   } else if (block_m == 128) {
     // The block kernels run each block as two 64-row halves, with a map of
-    // the halves' experts where the tile table would be. It is sized for
-    // the padded total this batch can reach (capacity / 64 <= 2 M k + 2
-    // entries), so the grid is too.
+    // the halves' experts where the tile table would be: cap / 64 <= 2 M k + 2
+    // entries (cap being at most the batch's capacity, above).
     a.half_expert = (int32_t*)(ws + L.tiles_off);
-    a.cap = capacity(M, E, top_k, block_m);
   }
   return a;
 }

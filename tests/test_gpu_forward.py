@@ -58,6 +58,29 @@ def const_layer(shape, byte=0x99, scale_bits=0x2000):
     return layer
 
 
+@pytest.mark.parametrize("case", [1, 3])
+def test_block_kernels_with_oversized_route_buffers(case):
+    """Route buffers allocated for a batch 400 times larger (cap far above
+    this batch's capacity) through the block kernels (wide and narrow): their
+    grid is sized from the batch, so the result is unchanged."""
+    shape, M, wseed, tseed = MID_SHAPES[case]
+    layer = device_layer(shape, wseed)
+    t = wl.tokens(shape, M, tseed)
+    for block_m in (16, 32, 64, 128):
+        big = moe.alloc_route_buffers(400 * M, shape.E, shape.k, block_m)
+        assert big.cap >= 5 * moe.moe_route_align_capacity(M, shape.E, shape.k, block_m)
+        rb = moe.RouteBuffers(M, shape.E, shape.k, block_m, big.cap, big.topk_ids[:M], big.topk_weights[:M],
+                              big.sorted_token_ids, big.block_expert_ids, big.expert_offsets,
+                              big.num_tokens_post_pad)
+        moe.route_align(to_dev(t.logits), rb)
+        out = moe.forward(x_device(t.x_bits), rb, shape.I, layer.w13, layer.w2).float().cpu().numpy()
+        torch.cuda.synchronize()
+        ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, block_m)
+        ref = oracle.moe_forward(wl.f32_from_bf16_bits(t.x_bits).astype(np.float64), ids, w,
+                                 oracle_experts(shape, wseed))
+        assert_output_close(out, ref, f"{shape} M={M} oversized cap B={block_m}")
+
+
 @pytest.mark.parametrize("case", [1, 3, 5])
 def test_block_m_128_half_map(case):
     """block_m = 128 outside the tiled kernel: the block kernels take at most
