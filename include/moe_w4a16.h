@@ -166,7 +166,9 @@ int64_t moe_w4a16_workspace_bytes(int32_t M, int32_t E, int32_t H, int32_t I, in
  * for this batch (a function of the expected tokens per expert, M*top_k/E).
  * It never returns 128: the kernels that take blocks take at most 64 rows,
  * so with block_m = 128 they run each block as its two 64-row halves (and
- * the tiled kernel as one tile), which only adds padding rows.
+ * the tiled kernel as one tile). Measured on the 384-expert layer: as fast
+ * as the preferred size from 16 assignments per expert (the tiled kernel),
+ * 1.5-1.8x slower below (64-row blocks of mostly padding rows).
  */
 int32_t moe_w4a16_preferred_block_m(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k);
 

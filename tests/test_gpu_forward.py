@@ -254,3 +254,24 @@ def test_k26_m90_every_block_m(block_m):
     rows = [13]
     ref = oracle.moe_forward(x, ids, wts, oracle_experts(s, 2026, keep=0), tokens_subset=rows)
     assert_output_close(out[rows], ref[rows], f"k26_m90 B={block_m}")
+
+
+@pytest.mark.parametrize("name", ["k26_m1024", "k26_m1024_skew"])
+def test_k26_block_m_128_tiled(name):
+    """The 384-expert layer with 128-row blocks on the tiled path (each block
+    one tile; the skewed batch's hot experts several): every element of a
+    set of token rows that together touch every routed expert."""
+    w = wl.WORKLOADS[name]
+    s = w.shape
+    layer = k26_layer()
+    t = wl.workload_tokens(w)
+    rb, out = run_layer(layer, t.logits, t.x_bits, 128)
+    ids, wts = assert_route_matches(route_host(rb), t.logits, s.E, s.k, 128)
+    assert np.all(np.isfinite(out))
+    rows = covering_rows(ids, [0] + (tile_rows_of_hot_experts(ids, 128) if name.endswith("skew") else []))
+    covered, touched = np.unique(ids[rows]), np.unique(ids)
+    x = wl.f32_from_bf16_bits(t.x_bits).astype(np.float64)
+    ref = oracle_rows_parallel(s, 2026, x, ids, wts, rows)
+    assert_output_close(out[rows], ref[rows], f"{name} B=128")
+    print(f"forward {name} B=128: {len(rows)} rows, experts covered {covered.size}/{touched.size}", flush=True)
+    assert covered.size == touched.size
