@@ -191,9 +191,12 @@ static int check_fc(int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, i
 
 // The pre-scaled tiled grouped GEMM (fc_prescaled.hip) takes the batch from
 // MOE_PRESCALED_MIN_PER_EXPERT assignments per expert on, where the shape
-// divides into its pair groups; the block kernels of fc.hip take the rest.
-static bool use_tiled(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k) {
-  return moe::prescaled_batch(M, E, top_k) && FMT_CALL(fmt, prescaled_supported, H, I);
+// divides into its pair groups and a block fits in its largest tile (a build
+// with smaller INT4 tiles leaves 128-row blocks to the block kernels); the
+// block kernels of fc.hip take the rest.
+static bool use_tiled(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, int32_t top_k, int32_t block_m) {
+  return moe::prescaled_batch(M, E, top_k) && FMT_CALL(fmt, prescaled_supported, H, I) &&
+         block_m <= moe::prescaled_max_rows(fmt);
 }
 
 // The weights a stage reads: the blob and, for INT4, its per-row shifts.
@@ -222,7 +225,7 @@ static moe::FcArgs fc_args(int fmt, int32_t M, int32_t E, int32_t H, int32_t I, 
   const int64_t reach = capacity(M, E, top_k, block_m);
   a.cap = cap < reach ? cap : reach;
   a.zero_words16 = (int64_t)M * H * 4 / 16;
-  if (use_tiled(fmt, M, E, H, I, top_k)) {
+  if (use_tiled(fmt, M, E, H, I, top_k, block_m)) {
     a.tiles = (int2*)(ws + L.tiles_off);
     a.ntiles = (int32_t*)(ws + L.ntiles_off);
     a.tile_rows = moe::prescaled_tile_rows(fmt, block_m);
@@ -331,7 +334,7 @@ static int layer_impl(int fmt, const float* logits, const uint16_t* x_bf16, int3
   // the decode path fits (the routed kernel always fits there); else the
   // grouped kernels. The routed FC1 writes no tile table, so it is not
   // combined with the tiled grouped FC2.
-  const bool tiled = use_tiled(fmt, M, E, H, I, top_k);
+  const bool tiled = use_tiled(fmt, M, E, H, I, top_k, block_m);
   const bool decode_fits = moe::decode_path_fits(M, H, I, top_k);
   const bool routed_pref = FMT_CALL(fmt, routed_fc1_preferred, M, E, H, I, top_k);
   const bool decode = decode_fits && (M == 1 || (M == moe::kDecodeMaxTokens && !routed_pref));
