@@ -43,7 +43,8 @@ def test_mxfp4_repack_round_trip():
 
 
 @pytest.mark.parametrize("case", range(len(SHAPES)))
-@pytest.mark.parametrize("M,block_m", [(1, 16), (5, 16), (33, 32), (33, 64), (300, 32), (300, 64)])
+@pytest.mark.parametrize("M,block_m", [(1, 16), (5, 16), (33, 32), (33, 64), (300, 32), (300, 64), (33, 128),
+                                       (300, 128)])
 def test_mxfp4_forward_matches_oracle(case, M, block_m):
     shape, seed = SHAPES[case]
     print(f"mxfp4 forward {shape} M={M} block_m={block_m}", flush=True)
@@ -83,7 +84,7 @@ def test_mxfp4_wide_scale_spread():
     s2 = (127 + rng.integers(0, 11, (shape.E, shape.H, shape.I // 32))).astype(np.uint8)
     layer = DeviceLayer(shape, w13, s13, w2, s2, fmt="mxfp4")
     experts = oracle.DequantCache(lambda e: (w13[e], s13[e], w2[e], s2[e]), fmt="mxfp4")
-    for M, block_m in ((3, 16), (40, 32), (200, 64)):
+    for M, block_m in ((3, 16), (40, 32), (200, 64), (200, 128)):
         t = wl.tokens(shape, M, 300 + M)
         rb, out = run_layer(layer, t.logits, t.x_bits, block_m)
         ids, w = assert_route_matches(route_host(rb), t.logits, shape.E, shape.k, block_m)
