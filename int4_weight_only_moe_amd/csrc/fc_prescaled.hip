@@ -387,16 +387,17 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
   const int rows_total = kFc1 ? a.M : MK;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.act_in, (uint32_t)rows_total * (uint32_t)K * 2u);
   const uint32_t rid0 = a_row<kFc1>(rows[0], a.k);
-  // The per-lane source offsets are kept in LDS (this thread's kD words),
-  // not in registers: they are needed only while the copies are issued.
-  uint32_t* myoff = xoffs + tid * (kBSlotRows / kCopyRows);
+  // The per-lane source offsets are kept in LDS (this thread's kD words,
+  // copy-major so that a wave's accesses are consecutive words), not in
+  // registers: they are needed only while the copies are issued.
+  uint32_t* myoff = xoffs + tid;
 #pragma unroll
   for (int i = 0; i < kD; ++i) {
     const int r = 4 * (wave + kBW * i) + (lane >> 4);
     const int f = r <= last ? fr[i] : MK;
     const uint32_t rid = (f >= 0 && f < MK) ? a_row<kFc1>(f, a.k) : rid0;
     const uint32_t v = (uint32_t)((lane & 15) ^ (r & 15));
-    myoff[i] = (rid * (uint32_t)K + 8u * v) * 2u;
+    myoff[i * 64 * kBW] = (rid * (uint32_t)K + 8u * v) * 2u;
   }
   // The epilogue's row data (two more loads for thread t < 16 S), stored to
   // LDS before the prologue's barrier.
@@ -412,7 +413,7 @@ __device__ __forceinline__ void prescaled_body(const FcArgs& a, const int e, con
   auto copy_rows = [&](int c, int slot) {
     uint32_t xoff[kD];
 #pragma unroll
-    for (int i = 0; i < kD; ++i) xoff[i] = myoff[i];
+    for (int i = 0; i < kD; ++i) xoff[i] = myoff[i * 64 * kBW];
 #pragma unroll
     for (int i = 0; i < kD; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xs.x[slot] + (wave + kBW * i) * 64), 16,
