@@ -102,7 +102,10 @@ void fc_kernel(FcArgs a) {
 constexpr int kWideNP = 16;                 // waves = tile pairs per workgroup
 constexpr int kWideP = 2;                   // chunks in flight per wave (even: LDS slot parity is static)
 constexpr int kRowVecs = kChunkK / 8;       // 16-byte vectors of a row's chunk slice
-constexpr int kRowPad = kRowVecs + 1;       // +16 B per row: conflict-free A reads
+// A row's 16 vectors are stored XOR-swizzled with the row index (vector v of
+// row r at v ^ (r % 16)): the A reads of a lane group (16 rows, the same
+// vector) and the staging writes (one row's 16 vectors) hit distinct banks.
+__device__ __forceinline__ int xswz(int row, int v) { return v ^ (row & 15); }
 
 constexpr int kXcds = 8;
 
@@ -111,7 +114,7 @@ constexpr int kXcds = 8;
 template <int S, bool kFc1, int kPolicy>
 __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const int pair, const int (&frow)[S],
                                              const int sf, const bool stager, const int srow, const int svec,
-                                             uint4 (&xt)[2][16 * S][kRowPad], f32x4_t (&xs4)[2][4][4 * S]) {
+                                             uint4 (&xt)[2][16 * S][kRowVecs], f32x4_t (&xs4)[2][4][4 * S]) {
   // A deeper ring does not fit: at 4 chunks the compiler spills, and a
   // scratch reload inside the loop waits for every weight load in flight.
   constexpr int P = kWideP;
@@ -165,7 +168,7 @@ __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const
   // store one staged vector and its share of the group sum (4 vectors = 1 group)
   auto store_x = [&](uint4 v, int slot) {
     if (!stager) return;
-    xt[slot][srow][svec] = v;
+    xt[slot][srow][xswz(srow, svec)] = v;
     const float corr = group_corr_quad(v);
     if ((svec & 3) == 0) reinterpret_cast<float*>(&xs4[slot][svec >> 2][0])[srow] = corr;
   };
@@ -202,7 +205,7 @@ __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const
 #pragma unroll
           for (int s = 0; s < S; ++s) {
             if (s > 0 && !sact[s]) continue;
-            const bf16x8_t xv = as_bf16x8(xt[slot][16 * s + mrow][4 * g + kv]);
+            const bf16x8_t xv = as_bf16x8(xt[slot][16 * s + mrow][xswz(mrow, 4 * g + kv)]);
             if constexpr (kFmt == kFmtMxfp4) {  // scaled operand: accumulate in the MFMA
               acc0[s] = mfma16x16x32(xv, b0, acc0[s]);
               acc1[s] = mfma16x16x32(xv, b1, acc1[s]);
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
   constexpr int BM = 16 * S;
   constexpr int kThreads = 64 * kWideNP;
   constexpr int kItems = BM * kRowVecs;  // multiple of 64: whole waves stage or idle
-  __shared__ uint4 xt[2][BM][kRowPad];   // the block's activation chunk, double-buffered
+  __shared__ uint4 xt[2][BM][kRowVecs];  // the block's activation chunk, double-buffered (swizzled)
   __shared__ f32x4_t xs4[2][4][BM / 4];  // -136 * group sums: [slot][group][4-row quad]
 
   const int tid = threadIdx.x, lane = tid & 63;
