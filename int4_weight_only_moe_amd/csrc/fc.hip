@@ -114,7 +114,7 @@ constexpr int kXcds = 8;
 template <int S, bool kFc1, int kPolicy>
 __device__ __forceinline__ void fc_wide_body(const FcArgs& a, const int e, const int pair, const int (&frow)[S],
                                              const int sf, const bool stager, const int srow, const int svec,
-                                             uint4 (&xt)[2][16 * S][kRowVecs], f32x4_t (&xs4)[2][4][4 * S]) {
+                                             uint4 (&xt)[2][16 * S][kRowVecs], f32x4_t (&xs4)[2][4][4 * S + 1]) {
   // A deeper ring does not fit: at 4 chunks the compiler spills, and a
   // scratch reload inside the loop waits for every weight load in flight.
   constexpr int P = kWideP;
@@ -239,7 +239,9 @@ __global__ __launch_bounds__(64 * kWideNP) void fc_wide_kernel(FcArgs a) {
   constexpr int kThreads = 64 * kWideNP;
   constexpr int kItems = BM * kRowVecs;  // multiple of 64: whole waves stage or idle
   __shared__ uint4 xt[2][BM][kRowVecs];  // the block's activation chunk, double-buffered (swizzled)
-  __shared__ f32x4_t xs4[2][4][BM / 4];  // -136 * group sums: [slot][group][4-row quad]
+  // -136 * group sums: [slot][group][4-row quad], one quad of padding per
+  // group so that the four groups' stores of a row land in distinct banks
+  __shared__ f32x4_t xs4[2][4][BM / 4 + 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
